@@ -1,0 +1,199 @@
+"""Throughput of the fused filter+sample path on one MI355X.
+
+One step = one qs_sample call over a whole batch: sigma-truncation pass,
+pivot searches, tie quota, renormalisation, mask/candidate outputs and the
+token draw, for every row. Inputs are resident in HBM before timing starts;
+the calls rotate over several input sets whose total size exceeds the 256 MB
+Infinity Cache, so the logits are read from HBM.
+
+Prints one JSON line (rank 0, one GPU):
+  value       rows per second over the whole timed region
+  roofline    algorithmic bytes read per launch / mean launch duration (HIP
+              events around every launch on the stream the kernel runs on),
+              against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle on a bounded sample of the same rows
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_NAMES = {
+    1: "B=4 V=32000 fp32 N(0,1)+6 on 16 ids, T=1 k=50 p=0.9",
+    2: "B=64 V=128256 fp32 N(0,4)+20 ids N(8,2), per-row k/p/T, 10% greedy",
+    3: "B=256 V=151936 bf16 N(0,9), thirds top-k/top-p/both, 30% legal bitmask",
+    4: "B=1024 V=262144 fp32 near-flat/bimodal/heavy-tail, k=4096 p=0.99",
+    5: "B=512 V=151936 bf16 as 3 + per-row T and degenerate rows, candidate lists",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=4,
+                    help="distinct input sets rotated through (default 4 > 256 MB MALL)")
+    ap.add_argument("--cand-cap", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows for the oracle baseline (0 = sized to ~15 s)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--flags", type=int, default=0)
+    return ap.parse_args()
+
+
+class Prepared:
+    """One input set on the device with preallocated outputs and the ctypes
+    argument tuple for qs_sample (no Python-side allocation in the loop)."""
+
+    def __init__(self, lib, w, cand_cap, flags, stream):
+        import torch
+        dev = "cuda"
+        self.w = w
+        if w.dtype == "bf16":
+            self.logits = torch.from_numpy(w.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            self.logits = torch.from_numpy(w.logits).to(dev)
+        self.T = torch.from_numpy(w.T).to(dev)
+        self.k = torch.from_numpy(w.k).to(dev)
+        self.p = torch.from_numpy(w.p).to(dev)
+        self.bm = None if w.bitmask is None else \
+            torch.from_numpy(w.bitmask.view(np.int32)).to(dev)
+        self.seed = torch.from_numpy(w.seeds.view(np.int64)).to(dev)
+        self.offset = torch.zeros(w.B, dtype=torch.int64, device=dev)
+        W = (w.V + 31) // 32
+        self.tokens = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.status = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.keep = torch.empty((w.B, W), dtype=torch.int32, device=dev)
+        self.cids = torch.empty((w.B, cand_cap), dtype=torch.int32, device=dev)
+        self.cprobs = torch.empty((w.B, cand_cap), dtype=torch.float32, device=dev)
+        self.ccount = torch.empty(w.B, dtype=torch.int32, device=dev)
+        P = ctypes.c_void_p
+        self.args = (
+            P(self.logits.data_ptr()), 1 if w.dtype == "bf16" else 0, w.B, w.V, w.V,
+            P(self.T.data_ptr()), P(self.k.data_ptr()), P(self.p.data_ptr()),
+            None if self.bm is None else P(self.bm.data_ptr()),
+            0 if self.bm is None else self.bm.stride(0),
+            P(self.seed.data_ptr()), P(self.offset.data_ptr()), None,
+            P(self.tokens.data_ptr()), P(self.keep.data_ptr()), P(self.cids.data_ptr()),
+            P(self.cprobs.data_ptr()), P(self.ccount.data_ptr()), cand_cap, None,
+            P(self.status.data_ptr()), None, flags, stream)
+        self.lib = lib
+
+    def call(self):
+        rc = self.lib.qs_sample(*self.args)
+        if rc != 0:
+            raise RuntimeError(f"qs_sample returned {rc}")
+
+
+def cpu_baseline(w, rows):
+    import oracle
+    t0 = time.perf_counter()
+    res = oracle.filter_batch(w.logits, w.dtype, w.T, w.k, w.p, w.bitmask, rows=rows)
+    oracle.sample_batch(res, w.seeds, w.offsets)
+    dt = time.perf_counter() - t0
+    return len(rows) / dt, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(rows are independent: a batch shards across GPUs with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import top_sampling_vocabs_amd as qs
+    lib = qs.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = args.workload
+    base = workloads.make(cfg)
+    sets = [base] + [workloads.make(cfg, seed=workloads.BASE_SEED + cfg + 1000 * i)
+                     for i in range(1, args.sets)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    preps = [Prepared(lib, w, args.cand_cap, args.flags, stream) for w in sets]
+    torch.cuda.synchronize()
+    bytes_read = workloads.bytes_read(base)
+    B = base.B
+
+    for i in range(args.warmup):
+        preps[i % len(preps)].call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start_all = torch.cuda.Event(enable_timing=True)
+    end_all = torch.cuda.Event(enable_timing=True)
+    start_all.record()
+    for i in range(K):
+        ev[i][0].record()
+        preps[i % len(preps)].call()
+        ev[i][1].record()
+    end_all.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start_all.elapsed_time(end_all)
+    per = np.array([a.elapsed_time(b) for a, b in ev])  # ms per launch
+    ms_step = total_ms / K
+    rows_per_s = B * K / (total_ms / 1e3)
+    mean_launch = float(per.mean())
+    achieved = bytes_read / (mean_launch / 1e3) / 1e9
+
+    # sanity: every row OK or an expected degenerate status
+    st = preps[0].status.cpu().numpy()
+    assert ((st == 0) | (st == 1) | (st == 2) | (st == 3) | (st == 5)).all(), np.unique(st)
+
+    cpu = None
+    if not args.no_cpu:
+        n = args.cpu_rows or {1: 4, 2: 64, 3: 128, 4: 48, 5: 128}[cfg]
+        rows = list(range(min(n, B)))
+        v, dt = cpu_baseline(base, rows)
+        cpu = {"value": round(v, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {len(rows)} rows of the same workload, filter + sample, "
+                         f"single process ({dt:.1f} s)"}
+
+    line = {
+        "metric": "rows/sec and effective HBM GB/s (fraction of peak), B=256 V=151936",
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": base.dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[cfg], "batch_rows": B, "vocab": base.V,
+                   "input_sets": len(sets), "bytes_read_per_step": bytes_read,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel_ms_mean": round(mean_launch, 5),
+                     "kernel_ms_p50": round(float(np.median(per)), 5),
+                     "kernel_ms_p99": round(float(np.percentile(per, 99)), 5)},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/* qs.h — C ABI of the exact top-k / top-p filter-and-sample library for MI355X.
+ *
+ * One call processes a batch of B rows of vocabulary logits z[B][V] on the
+ * caller's HIP stream. Per row r it applies, in this order (page
+ * "Attention算完，还没有选出下一个token", section 02, reference convention):
+ *   temperature T[r]  ->  legal-token bitmask (illegal -> -inf)  ->  top-k with
+ *   renormalisation  ->  top-p (shortest descending-mass prefix whose
+ *   cumulative mass reaches p)  ->  renormalisation  ->  (qs_sample) one draw
+ *   by inverse CDF in token-id order.
+ * The kept set is exactly the one a full stable sort by (-z, token id) gives;
+ * boundary duplicates keep the earliest token ids (page "Qrita", key design 3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer owned by the caller. The library
+ *   allocates nothing, keeps no state between calls and never synchronises:
+ *   work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *   default stream). Row outputs are valid once the caller has synchronised
+ *   with that stream. Concurrent calls on different streams are safe.
+ * - Logits are row-major, `row_stride` elements apart (row_stride >= V).
+ *   `logits` must be 16-byte aligned and row_stride * element size must be a
+ *   multiple of 16 bytes.
+ * - The legal-token bitmask is packed LSB-first: token i is bit (i & 31) of
+ *   32-bit word (i >> 5); W = ceil(V/32) words per row, rows `bitmask_stride`
+ *   words apart (>= W). Bits at positions >= V are ignored. NULL = all legal.
+ * - Return value: QS_OK, or QS_ERR_INVALID_ARG when a pointer, size, stride or
+ *   alignment check fails (reported before any HIP call, nothing is
+ *   enqueued), or QS_ERR_HIP when the launch fails. Row errors are reported
+ *   per row in `row_status` (qs_row_status), never by the return value.
+ * - Parameter semantics (page "Sampling 系统设计", temperature section: T = 0 is
+ *   greedy, and T < 0, p > 1, k < 0 must be rejected): T finite and >= 0,
+ *   T == 0 selects the greedy argmax path; k == 0 disables top-k and k >= the
+ *   number of finite legal tokens keeps them all; p == 1 disables top-p;
+ *   any other value (T < 0 or not finite, k < 0, p <= 0, p > 1, NaN) makes the
+ *   row QS_ROW_BAD_PARAM.
+ * - Row errors (page "Attention算完，还没有选出下一个token", sections 03 and 07: an
+ *   empty candidate set, NaN and all -inf rows are explicit errors, never a
+ *   substituted token) are checked in this order: EMPTY, NONFINITE, ALL_NEG_INF.
+ *   An error row gets token -1, an all-zero keep-mask row, cand_count 0,
+ *   all-zero dense probabilities and an unchanged RNG offset.
+ */
+#ifndef QS_H
+#define QS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define QS_API __attribute__((visibility("default")))
+#else
+#define QS_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QS_OK = 0,
+  QS_ERR_INVALID_ARG = 1,
+  QS_ERR_HIP = 3
+} qs_status;
+
+typedef enum {
+  QS_ROW_OK = 0,
+  QS_ROW_EMPTY = 1,          /* no legal token (all masked)                         */
+  QS_ROW_ALL_NEG_INF = 2,    /* legal tokens exist, every legal logit is -inf       */
+  QS_ROW_NONFINITE = 3,      /* NaN or +inf at a legal position                     */
+  QS_ROW_BAD_PARAM = 4,      /* invalid T, k or p                                   */
+  QS_ROW_CAND_OVERFLOW = 5,  /* |P| > cand_cap: candidate lists truncated to
+                                cand_cap entries; mask, probs and token complete    */
+  QS_ROW_INTERNAL = 6        /* pivot search did not converge (never expected)      */
+} qs_row_status;
+
+typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
+
+/* Path switches for ablations and path-invariance tests; outputs are identical
+ * with or without them (page "Qrita", ablation table: forced fallback and no
+ * truncation). 0 is the normal path. */
+#define QS_FLAG_FORCE_MISS     1u  /* run every search over the full row        */
+#define QS_FLAG_NO_TRUNCATION  2u  /* skip the sigma-truncation compaction      */
+
+/* Filter a batch: kept-candidate mask and renormalised probabilities.
+ *
+ * Defines the candidate set O of page "Qrita" (overall framework: strict
+ * top-k / top-p mask and candidate set) under the contract order above.
+ *
+ * logits       [B][row_stride] float32 or bfloat16 (dtype)
+ * temperature  [B] float32; top_k [B] int32; top_p [B] float32
+ * bitmask      [B][bitmask_stride] uint32, or NULL
+ * keep_mask    [B][ceil(V/32)] uint32 out, required: bit i set iff token i is
+ *              in the final set P (packed like the bitmask; every word written)
+ * cand_ids     [B][cand_cap] int32 out, optional: ids of P in ascending order
+ * cand_probs   [B][cand_cap] float32 out, optional: their probabilities
+ * cand_count   [B] int32 out, required if cand_ids or cand_probs is given:
+ *              |P| (the true size, also when it exceeds cand_cap)
+ * dense_probs  [B][V] float32 out, optional: probability of every token
+ *              (0 outside P)
+ * row_status   [B] int32 out, required (qs_row_status)
+ * debug_stats  [B][4] int32 out, optional: {path (0 candidate pool, 1 full
+ *              row), search rounds, |Z_t| (candidates above the truncation
+ *              threshold), |P|}
+ * flags        QS_FLAG_* bits, 0 normally
+ */
+QS_API int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V,
+                   int64_t row_stride, const float* temperature,
+                   const int32_t* top_k, const float* top_p,
+                   const uint32_t* bitmask, int64_t bitmask_stride,
+                   uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
+                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
+                   int32_t* row_status, int32_t* debug_stats, uint32_t flags,
+                   void* stream);
+
+/* Filter and draw one token per row.
+ *
+ * Same inputs and optional outputs as qs_filter_mask (keep_mask is optional
+ * here). The draw walks P in ascending token id and returns the first id whose
+ * cumulative probability exceeds u (page "Attention算完，还没有选出下一个token",
+ * section 02 widget: CDF by token id; right-open intervals).
+ *
+ * seed, offset [B] uint64: per-row RNG state (page above, section 06: explicit
+ *              seed/offset advanced by actual consumption). A sampled row
+ *              draws u from Philox4x32-10 (Salmon et al., SC'11) with
+ *              counter (offset lo, offset hi, 0, 0) and key (seed lo, seed hi),
+ *              u = (x0 >> 8) * 2^-24, and then offset += 1. Greedy rows and
+ *              error rows consume nothing and leave offset unchanged.
+ *              Required unless `uniforms` is given.
+ * uniforms     [B] float64 in [0,1), optional: when given, row r uses
+ *              u = uniforms[r] and offsets are neither read nor written.
+ * tokens       [B] int32 out, required: the token, -1 on an error row.
+ */
+QS_API int qs_sample(const void* logits, int dtype, int64_t B, int64_t V,
+              int64_t row_stride, const float* temperature,
+              const int32_t* top_k, const float* top_p,
+              const uint32_t* bitmask, int64_t bitmask_stride,
+              const uint64_t* seed, uint64_t* offset, const double* uniforms,
+              int32_t* tokens, uint32_t* keep_mask, int32_t* cand_ids,
+              float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+              uint32_t flags, void* stream);
+
+/* Greedy selection: tokens[r] = lowest token id holding the largest finite
+ * legal logit. No softmax and no random number (page "第 9 讲 · 生成与推测解码",
+ * section 1: argmax needs no normalisation; exercise 1: ties by vocabulary
+ * order). tokens and row_status are required; row statuses as above
+ * (QS_ROW_EMPTY, QS_ROW_NONFINITE, QS_ROW_ALL_NEG_INF, else QS_ROW_OK). */
+QS_API int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V,
+              int64_t row_stride, const uint32_t* bitmask,
+              int64_t bitmask_stride, int32_t* tokens, int32_t* row_status,
+              void* stream);
+
+/* Library version string (static storage). */
+QS_API const char* qs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QS_H */

@@ -1,0 +1,115 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments before making any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from top_sampling_vocabs_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qs.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:QS_API\s+)?(?:int|const char\*|size_t)\s+(qs_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libqs.so is not built: run python -m top_sampling_vocabs_amd.build")
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.qs_version().decode().startswith("qs ")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        _lib.load(str(tmp_path / "nope.so"))
+
+
+# Fake but aligned device addresses: validation must reject the call before it
+# dereferences or launches anything, so no GPU is needed.
+A16 = ctypes.c_void_p(0x100000)
+A8 = ctypes.c_void_p(0x200000)
+
+
+def filt(lib, **kw):
+    args = dict(logits=A16, dtype=0, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
+                bitmask=None, bms=0, keep=A16, cids=None, cprobs=None, ccount=None,
+                cap=0, dense=None, status=A16, dbg=None, flags=0, stream=None)
+    args.update(kw)
+    return lib.qs_filter_mask(args["logits"], args["dtype"], args["B"], args["V"],
+                              args["stride"], args["T"], args["k"], args["p"],
+                              args["bitmask"], args["bms"], args["keep"], args["cids"],
+                              args["cprobs"], args["ccount"], args["cap"], args["dense"],
+                              args["status"], args["dbg"], args["flags"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(logits=None), dict(dtype=2), dict(dtype=-1), dict(B=-1), dict(V=0),
+    dict(stride=63), dict(stride=65), dict(logits=ctypes.c_void_p(0x100004)),
+    dict(T=None), dict(k=None), dict(p=None), dict(status=None), dict(keep=None),
+    dict(cids=A16, ccount=None, cap=8), dict(cids=A16, ccount=A16, cap=0),
+    dict(bitmask=A16, bms=1), dict(bitmask=ctypes.c_void_p(0x100002), bms=2),
+    dict(flags=4), dict(T=ctypes.c_void_p(0x100001)),
+    dict(dtype=1, stride=68),
+])
+def test_filter_rejects_bad_arguments(lib, kw):
+    assert filt(lib, **kw) == _lib.QS_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert filt(lib, B=0) == _lib.QS_OK
+    assert filt(lib, B=0, logits=None, T=None) == _lib.QS_OK
+
+
+def smp(lib, **kw):
+    args = dict(logits=A16, dtype=1, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
+                bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16,
+                keep=None, cids=None, cprobs=None, ccount=None, cap=0, dense=None,
+                status=A16, dbg=None, flags=0, stream=None)
+    args.update(kw)
+    return lib.qs_sample(args["logits"], args["dtype"], args["B"], args["V"], args["stride"],
+                         args["T"], args["k"], args["p"], args["bitmask"], args["bms"],
+                         args["seed"], args["offset"], args["uni"], args["tokens"],
+                         args["keep"], args["cids"], args["cprobs"], args["ccount"],
+                         args["cap"], args["dense"], args["status"], args["dbg"],
+                         args["flags"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tokens=None), dict(seed=None), dict(offset=None), dict(seed=None, offset=None),
+    dict(offset=ctypes.c_void_p(0x200004)), dict(uni=ctypes.c_void_p(0x200004)),
+    dict(stride=60), dict(V=-5),
+])
+def test_sample_rejects_bad_arguments(lib, kw):
+    assert smp(lib, **kw) == _lib.QS_ERR_INVALID_ARG
+
+
+def test_argmax_rejects_bad_arguments(lib):
+    def am(**kw):
+        a = dict(logits=A16, dtype=0, B=2, V=10, stride=12, bitmask=None, bms=0,
+                 tokens=A16, status=A16, stream=None)
+        a.update(kw)
+        return lib.qs_argmax(a["logits"], a["dtype"], a["B"], a["V"], a["stride"],
+                             a["bitmask"], a["bms"], a["tokens"], a["status"], a["stream"])
+    assert am(tokens=None) == _lib.QS_ERR_INVALID_ARG
+    assert am(status=None) == _lib.QS_ERR_INVALID_ARG
+    assert am(stride=10) == _lib.QS_ERR_INVALID_ARG  # 40 bytes is not a multiple of 16
+    assert am(V=0) == _lib.QS_ERR_INVALID_ARG
+    assert am(B=0) == _lib.QS_OK

@@ -1,0 +1,343 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Masks and candidate ids are compared bit-exactly; probabilities within 1e-6
+relative (floor 2^-126); tokens exactly for the same u unless u lies within
+1e-6 of a CDF step; statuses and RNG offsets exactly. Rows whose top-p cut sits
+within 1e-9 * W_K of the threshold may keep the adjacent prefix (counted).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _harness import Report, compare_filter, compare_tokens, to_device, words_u32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qs():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import top_sampling_vocabs_amd as qs
+    qs.load()
+    return qs
+
+
+def run_all(qs, d, uniforms=None, flags=0, cand_cap=None, V=None):
+    import torch
+    cap = cand_cap if cand_cap is not None else V
+    out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                    seed=d["seed"], offset=d["offset"], uniforms=uniforms,
+                    keep_mask=True, cand_cap=cap, dense=True, debug=True, flags=flags)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_workload(qs, w, rows=None, seed=0, flags=0, cand_cap=None, dense=True):
+    import torch
+    rows = list(range(w.B)) if rows is None else rows
+    d = to_device(w)
+    uni = np.random.default_rng(seed).random(w.B)
+    uni_t = torch.from_numpy(uni).cuda()
+    out = run_all(qs, d, uniforms=uni_t, flags=flags, cand_cap=cand_cap, V=w.V)
+    res = oracle.filter_batch(w.logits, w.dtype, w.T, w.k, w.p, w.bitmask, rows=rows)
+    rep = Report()
+    compare_filter(w, res, out, rows, rep, check_dense=dense)
+    compare_tokens(res, out["tokens"], rows, rep, uniforms=uni)
+    # filter_mask gives the same mask and lists
+    fm = qs.filter_mask(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                        cand_cap=cand_cap or w.V, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(words_u32(fm["keep_mask"]), words_u32(out["keep_mask"]))
+    assert np.array_equal(fm["cand_count"].cpu().numpy(), out["cand_count"].cpu().numpy())
+    rep.check()
+    return rep, out
+
+
+SMALL = {1: dict(B=4, V=32000), 2: dict(B=24, V=20000), 3: dict(B=48, V=9000),
+         4: dict(B=24, V=16384), 5: dict(B=100, V=9000)}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_parity_small(qs, cfg):
+    w = workloads.make(cfg, **SMALL[cfg])
+    print(f"workload {cfg} B={w.B} V={w.V}", flush=True)
+    rep, out = check_workload(qs, w, seed=cfg)
+    assert rep.band_rows <= max(1, w.B // 50)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 5, 31, 33, 100, 511, 513, 1000, 5003, 8193, 40000])
+def test_parity_ragged(qs, dtype, V):
+    """Odd vocabulary sizes (ragged final step, partial mask word, V < one wave
+    step), many exact ties (rounded logits), -inf, and every parameter mode."""
+    import torch
+    rng = np.random.default_rng(V * 7 + (dtype == "bf16"))
+    B = 36
+    z = np.round(rng.normal(size=(B, V)) * 2, 1).astype(np.float32)
+    z[rng.random((B, V)) < 0.02] = -np.inf
+    bits = rng.random((B, V)) < rng.uniform(0.2, 1.0, size=(B, 1))
+    bits[np.arange(B), rng.integers(0, V, size=B)] = True
+    k = rng.integers(0, max(2, V + 3), size=B).astype(np.int32)
+    k[::4] = 0
+    p = rng.uniform(0.05, 1.0, size=B).astype(np.float32)
+    p[1::5] = 1.0
+    T = rng.uniform(0.3, 2.0, size=B).astype(np.float32)
+    T[2::9] = 0.0
+    es = 2 if dtype == "bf16" else 4
+    stride = -(-V // (16 // es)) * (16 // es)
+    if dtype == "bf16":
+        logits = np.zeros((B, stride), np.uint16)
+        logits[:, :V] = workloads.f32_to_bf16_bits(z)
+    else:
+        logits = np.zeros((B, stride), np.float32)
+        logits[:, :V] = z
+    w = workloads.Workload(cfg=0, dtype=dtype, logits=logits, T=T, k=k, p=p,
+                           bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    d = to_device(w)
+    d["logits"] = d["logits"][:, :V]  # row stride stays padded
+    w.logits = logits[:, :V]
+    uni = rng.random(B)
+    out = run_all(qs, d, uniforms=torch.from_numpy(uni).cuda(), V=V)
+    res = oracle.filter_batch(w.logits, dtype, T, k, p, w.bitmask)
+    rep = Report()
+    compare_filter(w, res, out, range(B), rep)
+    compare_tokens(res, out["tokens"], range(B), rep, uniforms=uni)
+    rep.check()
+
+
+def test_path_invariance(qs):
+    """Forced fallback and no truncation run every search over the full row; the
+    outputs are bitwise identical to the truncated path (page "Qrita" ablation
+    runs D and E compute the same result as run A)."""
+    import torch
+    for cfg in (2, 3, 5):
+        w = workloads.make(cfg, **SMALL[cfg])
+        d = to_device(w)
+        uni = torch.from_numpy(np.random.default_rng(9).random(w.B)).cuda()
+        base = run_all(qs, d, uniforms=uni, V=w.V)
+        for flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION):
+            alt = run_all(qs, d, uniforms=uni, flags=flags, V=w.V)
+            for key in ("keep_mask", "cand_count", "dense", "tokens", "status"):
+                assert torch.equal(base[key], alt[key]), (cfg, flags, key)
+            assert lists_equal(base, alt), (cfg, flags)
+            dbg = alt["debug"].cpu().numpy()
+            ok = base["status"].cpu().numpy() == 0
+            assert (dbg[ok, 0] == 1).all()  # every OK row took the full-row path
+
+
+def lists_equal(a, b):
+    """Candidate lists agree on their first cand_count entries (the rest of each
+    row is not written)."""
+    cnt = a["cand_count"].cpu().numpy()
+    cap = a["cand_ids"].shape[1]
+    ia, ib = a["cand_ids"].cpu().numpy(), b["cand_ids"].cpu().numpy()
+    pa = a["cand_probs"].cpu().numpy().view(np.uint32)
+    pb = b["cand_probs"].cpu().numpy().view(np.uint32)
+    for r in range(len(cnt)):
+        n = min(int(cnt[r]), cap)
+        if not (np.array_equal(ia[r, :n], ib[r, :n]) and np.array_equal(pa[r, :n], pb[r, :n])):
+            return False
+    return True
+
+
+def test_determinism(qs):
+    import torch
+    w = workloads.make(5, **SMALL[5])
+    d = to_device(w)
+    a = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"], seed=d["seed"],
+                  offset=d["offset"].clone(), keep_mask=True, cand_cap=4096, dense=True)
+    b = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"], seed=d["seed"],
+                  offset=d["offset"].clone(), keep_mask=True, cand_cap=4096, dense=True)
+    torch.cuda.synchronize()
+    for key in ("tokens", "status", "keep_mask", "cand_count", "dense"):
+        assert torch.equal(a[key], b[key]), key
+    assert lists_equal(a, b)
+
+
+def test_philox_stream_and_offsets(qs):
+    """Tokens drawn from the library's own Philox match the oracle's Philox walk;
+    sampled rows advance their offset by exactly one, greedy and error rows not
+    at all; a second call continues the stream from the advanced offsets."""
+    import torch
+    w = workloads.make(5, **SMALL[5])
+    w.T[3] = 0.0
+    w.offsets[:] = np.random.default_rng(3).integers(0, 1 << 40, size=w.B).astype(np.uint64)
+    d = to_device(w)
+    res = oracle.filter_batch(w.logits, w.dtype, w.T, w.k, w.p, w.bitmask)
+    off0 = w.offsets.copy()
+    for call in range(2):
+        before = d["offset"].cpu().numpy().view(np.uint64).copy()
+        out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                        seed=d["seed"], offset=d["offset"])
+        torch.cuda.synchronize()
+        after = d["offset"].cpu().numpy().view(np.uint64).copy()
+        rep = Report()
+        compare_tokens(res, out["tokens"], range(w.B), rep, offsets_in=before,
+                       offsets_out=after, seeds=w.seeds)
+        rep.check()
+    sampled = np.array([res[r].status == 0 and not res[r].greedy for r in range(w.B)])
+    assert np.array_equal(after - off0, np.where(sampled, 2, 0).astype(np.uint64))
+
+
+def test_sampling_statistics(qs):
+    """One filtered row replicated with distinct seeds: token frequencies match
+    the oracle's q (chi-square with bins pooled to expectation >= 5, and total
+    variation within the finite-sample scale)."""
+    import torch
+    from scipy import stats
+    rng = np.random.default_rng(11)
+    V = 3000
+    z = (rng.normal(size=V) * 1.5).astype(np.float32)
+    n = 20000
+    logits = torch.from_numpy(np.tile(z, (n, 1))).cuda()
+    T = torch.full((n,), 0.8, dtype=torch.float32, device="cuda")
+    k = torch.full((n,), 200, dtype=torch.int32, device="cuda")
+    p = torch.full((n,), 0.9, dtype=torch.float32, device="cuda")
+    seed = torch.arange(n, dtype=torch.int64, device="cuda") * 7919 + 5
+    offset = torch.zeros(n, dtype=torch.int64, device="cuda")
+    out = qs.sample(logits, T, k, p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    toks = out["tokens"].cpu().numpy()
+    rr = oracle.filter_row(z.astype(np.float64), 0.8, 200, 0.9)
+    assert set(np.unique(toks)) <= set(rr.kept.tolist())
+    counts = np.array([(toks == i).sum() for i in rr.kept], dtype=np.float64)
+    expect = rr.q * n
+    order = np.argsort(expect)
+    obs_b, exp_b, acc_o, acc_e = [], [], 0.0, 0.0
+    for i in order:
+        acc_o += counts[i]
+        acc_e += expect[i]
+        if acc_e >= 5:
+            obs_b.append(acc_o)
+            exp_b.append(acc_e)
+            acc_o = acc_e = 0.0
+    if acc_e > 0:
+        obs_b[-1] += acc_o
+        exp_b[-1] += acc_e
+    pval = stats.chisquare(obs_b, exp_b).pvalue
+    assert pval > 1e-4, pval
+    tv = 0.5 * np.abs(counts / n - rr.q).sum()
+    # finite-sample TV scale ~ sum_i sqrt(q_i (1-q_i) / n) * sqrt(2/pi) / 2
+    scale = 0.5 * np.sqrt(2 / np.pi) * np.sqrt(rr.q * (1 - rr.q) / n).sum()
+    assert tv < 1.5 * scale + 0.005, (tv, scale)
+
+
+def test_argmax_parity(qs):
+    import torch
+    for cfg in (1, 2, 3, 5):
+        w = workloads.make(cfg, **SMALL[cfg])
+        d = to_device(w)
+        tok, st = qs.argmax(d["logits"], d["bitmask"])
+        torch.cuda.synchronize()
+        want = oracle.argmax_batch(w.logits, w.dtype, w.bitmask)
+        for r in range(w.B):
+            assert (st[r].item(), tok[r].item()) == want[r], (cfg, r)
+
+
+def test_argmax_ties_and_specials(qs):
+    import torch
+    z = np.array([[1.0, 3.0, 3.0, 2.0],
+                  [np.nan, 0.0, 1.0, 1.0],
+                  [-np.inf, -np.inf, -np.inf, -np.inf],
+                  [0.0, np.inf, 1.0, 2.0],
+                  [5.0, 5.0, 5.0, 5.0],
+                  [-1.0, -1.0, -3.0, -0.5]], np.float32)
+    zz = np.zeros((6, 8), np.float32)
+    zz[:, :4] = z
+    bits = np.ones((6, 4), bool)
+    bits[1, 0] = False      # NaN at an illegal position is fine
+    bits[3, 1] = False      # so is +inf
+    bits[5, 3] = False
+    t = torch.from_numpy(zz).cuda()[:, :4]
+    bm = torch.from_numpy(workloads.pack_bits(bits).view(np.int32)).cuda()
+    tok, st = qs.argmax(t, bm)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0, 0, 2, 0, 0, 0]
+    assert tok.cpu().tolist() == [1, 2, -1, 3, 0, 0]
+
+
+def test_error_rows_and_bad_params(qs):
+    import torch
+    V = 700
+    B = 10
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=(B, V)).astype(np.float32)
+    bits = np.ones((B, V), bool)
+    bits[0] = False                    # EMPTY
+    z[1, 17] = np.nan                  # NONFINITE
+    z[2] = -np.inf                     # ALL_NEG_INF
+    z[3, 5] = np.inf                   # NONFINITE (+inf)
+    z[4, 9] = np.nan
+    bits[4, 9] = False                 # NaN at an illegal position: OK
+    T = np.ones(B, np.float32)
+    k = np.full(B, 20, np.int32)
+    p = np.full(B, 0.9, np.float32)
+    T[5] = -1.0                        # BAD_PARAM
+    k[6] = -2                          # BAD_PARAM
+    p[7] = 1.5                         # BAD_PARAM
+    p[8] = 0.0                         # BAD_PARAM
+    T[9] = np.nan                      # BAD_PARAM
+    w = workloads.Workload(cfg=0, dtype="f32", logits=z, T=T, k=k, p=p,
+                           bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64), offsets=np.zeros(B, np.uint64))
+    d = to_device(w)
+    out = run_all(qs, d, V=V)
+    st = out["status"].cpu().tolist()
+    assert st == [1, 3, 2, 3, 0, 4, 4, 4, 4, 4]
+    off = d["offset"].cpu().numpy()
+    assert off.tolist() == [0, 0, 0, 0, 1, 0, 0, 0, 0, 0]
+    tok = out["tokens"].cpu().numpy()
+    assert (tok[[0, 1, 2, 3, 5, 6, 7, 8, 9]] == -1).all()
+    res = oracle.filter_batch(z, "f32", T, k, p, w.bitmask)
+    rep = Report()
+    compare_filter(w, res, out, range(B), rep)
+    rep.check()
+
+
+def test_candidate_overflow(qs):
+    import torch
+    w = workloads.make(3, B=12, V=9000)
+    d = to_device(w)
+    out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                    uniforms=torch.full((w.B,), 0.5, dtype=torch.float64, device="cuda"),
+                    keep_mask=True, cand_cap=8)
+    torch.cuda.synchronize()
+    res = oracle.filter_batch(w.logits, w.dtype, w.T, w.k, w.p, w.bitmask)
+    rep = Report()
+    compare_filter(w, res, out, range(w.B), rep)
+    rep.check()
+    st = out["status"].cpu().numpy()
+    assert (st == 5).sum() == sum(len(res[r].kept) > 8 for r in range(w.B))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg,rows", [(1, None), (2, None), (3, 24), (4, 12), (5, 24)])
+def test_parity_full_size(qs, cfg, rows):
+    """Full-size workloads in the launch configuration the bench times; the
+    oracle checks a seeded sample of rows (all rows for the small workloads)."""
+    w = workloads.make(cfg)
+    print(f"full workload {cfg} B={w.B} V={w.V}", flush=True)
+    if rows is None:
+        pick = list(range(w.B))
+    else:
+        pick = sorted(np.random.default_rng(cfg).choice(w.B, size=rows, replace=False).tolist())
+        if cfg == 4:  # every row kind
+            pick = sorted(set(pick) | {0, 1, 2})
+        if cfg == 5:  # include every degenerate row
+            empty = np.nonzero(~w.bitmask.any(axis=1))[0]
+            ninf = np.nonzero((w.logits == 0xFF80).all(axis=1))[0]
+            nan = np.nonzero(((w.logits & 0x7FFF) > 0x7F80).any(axis=1))[0]
+            pick = sorted(set(pick) | set(empty[:4].tolist()) | set(ninf.tolist())
+                          | set(nan.tolist()))
+    rep, out = check_workload(qs, w, rows=pick, seed=100 + cfg, cand_cap=8192, dense=False)
+    dbg = out["debug"].cpu().numpy()
+    if cfg == 4:
+        # near-flat rows hit the truncated pool; bimodal and heavy-tail rows fall back
+        kinds = np.arange(w.B) % 3
+        assert (dbg[kinds == 0, 0] == 0).mean() > 0.9
+        assert dbg[:, 1].max() <= 2 * 17

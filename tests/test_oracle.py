@@ -406,3 +406,11 @@ def test_cdf_walk_right_open_on_exact_boundary():
     assert sample_from(kept, q, 0.5)[0] == 5
     assert sample_from(kept, q, 0.75)[0] == 9
     assert sample_from(kept, q, 0.0)[0] == 2
+
+
+def test_signed_zeros_tie():
+    """-0.0 and +0.0 compare equal, so they are a tie broken by token id."""
+    z = np.array([-1.0, -0.0, 0.0, -0.0, -2.0])
+    assert list(filter_row(z, 1.0, 1, 1.0).kept) == [1]
+    assert list(filter_row(z, 1.0, 2, 1.0).kept) == [1, 2]
+    assert oracle.argmax_row(z) == (oracle.ROW_OK, 1)

@@ -1,0 +1,218 @@
+"""ctypes binding of libqs.so (the C ABI in include/qs.h).
+
+This layer only marshals arguments: tensors become device pointers, the
+current torch stream becomes the hipStream_t. Every step of the filtering and
+sampling runs in the HIP kernels; there is no CPU or torch fallback. If the
+library is missing the first call raises.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqs.so")
+
+QS_OK = 0
+QS_ERR_INVALID_ARG = 1
+QS_ERR_HIP = 3
+
+ROW_OK = 0
+ROW_EMPTY = 1
+ROW_ALL_NEG_INF = 2
+ROW_NONFINITE = 3
+ROW_BAD_PARAM = 4
+ROW_CAND_OVERFLOW = 5
+ROW_INTERNAL = 6
+
+QS_F32 = 0
+QS_BF16 = 1
+
+FLAG_FORCE_MISS = 1
+FLAG_NO_TRUNCATION = 2
+
+EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_version")
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_u32 = ctypes.c_uint32
+
+
+def load(path=LIB_PATH):
+    """Load libqs.so and declare the C signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m top_sampling_vocabs_amd.build`")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    lib.qs_filter_mask.restype = _i32
+    lib.qs_filter_mask.argtypes = [
+        _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
+        _p, _p, _p,                          # temperature, top_k, top_p
+        _p, _i64,                            # bitmask, bitmask_stride
+        _p, _p, _p, _p, _i64,                # keep_mask, cand_ids, cand_probs, cand_count, cand_cap
+        _p, _p, _p, _u32, _p]                # dense, row_status, debug, flags, stream
+    lib.qs_sample.restype = _i32
+    lib.qs_sample.argtypes = [
+        _p, _i32, _i64, _i64, _i64,
+        _p, _p, _p,
+        _p, _i64,
+        _p, _p, _p, _p,                      # seed, offset, uniforms, tokens
+        _p, _p, _p, _p, _i64,
+        _p, _p, _p, _u32, _p]
+    lib.qs_argmax.restype = _i32
+    lib.qs_argmax.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
+    lib.qs_version.restype = ctypes.c_char_p
+    lib.qs_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(logits):
+    import torch
+    if logits.dtype == torch.float32:
+        return QS_F32
+    if logits.dtype == torch.bfloat16:
+        return QS_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+
+
+def _check_rowvec(t, B, dtype, name):
+    if t is None or t.dim() != 1 or t.shape[0] != B or t.dtype != dtype or not t.is_cuda \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor of shape [{B}] and {dtype}")
+
+
+def _check_logits(logits, bitmask):
+    if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a CUDA tensor [B, V] with unit column stride")
+    B, V = logits.shape
+    if bitmask is not None:
+        import torch
+        if bitmask.dim() != 2 or bitmask.shape[0] != B or bitmask.dtype != torch.int32 \
+                or bitmask.stride(1) != 1 or not bitmask.is_cuda:
+            raise ValueError("bitmask must be an int32 CUDA tensor [B, >= ceil(V/32)] "
+                             "holding the uint32 words")
+    return B, V
+
+
+def _status(rc, what):
+    if rc != QS_OK:
+        name = {QS_ERR_INVALID_ARG: "QS_ERR_INVALID_ARG", QS_ERR_HIP: "QS_ERR_HIP"}.get(rc, rc)
+        raise RuntimeError(f"{what} returned {name}")
+
+
+def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
+                dense=False, debug=False, flags=0):
+    """Kept-candidate mask and renormalised probabilities for every row.
+
+    logits [B, V] float32 / bfloat16 (CUDA); temperature, top_p float32 [B];
+    top_k int32 [B]; bitmask int32 [B, >= ceil(V/32)] holding uint32 words, or
+    None. Returns a dict of device tensors: keep_mask (int32 words [B, W]),
+    status [B], and if requested cand_ids / cand_probs [B, cand_cap],
+    cand_count [B], dense [B, V], debug [B, 4]. Enqueued on the current stream;
+    synchronise before reading.
+    """
+    import torch
+    lib = load()
+    B, V = _check_logits(logits, bitmask)
+    dev = logits.device
+    _check_rowvec(temperature, B, torch.float32, "temperature")
+    _check_rowvec(top_k, B, torch.int32, "top_k")
+    _check_rowvec(top_p, B, torch.float32, "top_p")
+    W = (V + 31) // 32
+    out = {"keep_mask": torch.empty((B, W), dtype=torch.int32, device=dev),
+           "status": torch.empty(B, dtype=torch.int32, device=dev)}
+    if cand_cap:
+        out["cand_ids"] = torch.empty((B, cand_cap), dtype=torch.int32, device=dev)
+        out["cand_probs"] = torch.empty((B, cand_cap), dtype=torch.float32, device=dev)
+        out["cand_count"] = torch.empty(B, dtype=torch.int32, device=dev)
+    if dense:
+        out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
+    if debug:
+        out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    rc = lib.qs_filter_mask(
+        _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+        _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
+        _ptr(out["keep_mask"]), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
+        _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
+        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), _stream(dev))
+    _status(rc, "qs_filter_mask")
+    return out
+
+
+def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset=None,
+           uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False, flags=0):
+    """Filter and draw one token per row.
+
+    seed, offset: int64 [B] CUDA tensors holding the uint64 RNG state; offset is
+    advanced in place by the randomness actually consumed. uniforms: float64
+    [B] to use fixed u values instead (offsets untouched). Returns a dict with
+    tokens [B], status [B] and the optional outputs of filter_mask.
+    """
+    import torch
+    lib = load()
+    B, V = _check_logits(logits, bitmask)
+    dev = logits.device
+    _check_rowvec(temperature, B, torch.float32, "temperature")
+    _check_rowvec(top_k, B, torch.int32, "top_k")
+    _check_rowvec(top_p, B, torch.float32, "top_p")
+    if uniforms is None:
+        _check_rowvec(seed, B, torch.int64, "seed")
+        _check_rowvec(offset, B, torch.int64, "offset")
+    else:
+        _check_rowvec(uniforms, B, torch.float64, "uniforms")
+    W = (V + 31) // 32
+    out = {"tokens": torch.empty(B, dtype=torch.int32, device=dev),
+           "status": torch.empty(B, dtype=torch.int32, device=dev)}
+    if keep_mask:
+        out["keep_mask"] = torch.empty((B, W), dtype=torch.int32, device=dev)
+    if cand_cap:
+        out["cand_ids"] = torch.empty((B, cand_cap), dtype=torch.int32, device=dev)
+        out["cand_probs"] = torch.empty((B, cand_cap), dtype=torch.float32, device=dev)
+        out["cand_count"] = torch.empty(B, dtype=torch.int32, device=dev)
+    if dense:
+        out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
+    if debug:
+        out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    rc = lib.qs_sample(
+        _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+        _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
+        _ptr(seed) if uniforms is None else None,
+        _ptr(offset) if uniforms is None else None, _ptr(uniforms), _ptr(out["tokens"]),
+        _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
+        _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
+        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), _stream(dev))
+    _status(rc, "qs_sample")
+    return out
+
+
+def argmax(logits, bitmask=None):
+    """Greedy token per row: (tokens [B] int32, status [B] int32)."""
+    import torch
+    lib = load()
+    B, V = _check_logits(logits, bitmask)
+    dev = logits.device
+    tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = lib.qs_argmax(_ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+                       _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
+                       _ptr(tokens), _ptr(status), _stream(dev))
+    _status(rc, "qs_argmax")
+    return tokens, status

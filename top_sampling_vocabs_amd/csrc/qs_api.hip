@@ -1,0 +1,141 @@
+// C-ABI entry points: argument validation (before any HIP call), launch
+// geometry, and error mapping. Every entry point enqueues exactly one kernel
+// launch on the caller's stream and returns without synchronising.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qs.h"
+
+#include "qs_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxV = (int64_t)1 << 30;
+constexpr int64_t kMaxB = ((int64_t)1 << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared checks of the logits / bitmask description.
+int check_input(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                const uint32_t* bitmask, int64_t bitmask_stride) {
+  if (dtype != QS_F32 && dtype != QS_BF16) return QS_ERR_INVALID_ARG;
+  if (B < 0 || B > kMaxB || V < 1 || V > kMaxV) return QS_ERR_INVALID_ARG;
+  if (B == 0) return QS_OK;
+  if (!logits || !aligned(logits, 16)) return QS_ERR_INVALID_ARG;
+  const int64_t es = dtype == QS_F32 ? 4 : 2;
+  if (row_stride < V || (row_stride * es) % 16 != 0) return QS_ERR_INVALID_ARG;
+  if (bitmask) {
+    if (!aligned(bitmask, 4)) return QS_ERR_INVALID_ARG;
+    if (bitmask_stride < (V + 31) / 32) return QS_ERR_INVALID_ARG;
+  }
+  return QS_OK;
+}
+
+int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t V,
+                  int64_t row_stride, const float* temperature, const int32_t* top_k,
+                  const float* top_p, const uint32_t* bitmask, int64_t bitmask_stride,
+                  const uint64_t* seed, uint64_t* offset, const double* uniforms,
+                  int32_t* tokens, uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
+                  int32_t* cand_count, int64_t cand_cap, float* dense_probs,
+                  int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* stream) {
+  int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
+  if (rc != QS_OK) return rc;
+  if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION)) return QS_ERR_INVALID_ARG;
+  if (B == 0) return QS_OK;
+  if (!temperature || !top_k || !top_p || !row_status) return QS_ERR_INVALID_ARG;
+  if (!sample && !keep_mask) return QS_ERR_INVALID_ARG;
+  if (sample) {
+    if (!tokens) return QS_ERR_INVALID_ARG;
+    if (!uniforms && (!seed || !offset)) return QS_ERR_INVALID_ARG;
+  }
+  if (cand_ids || cand_probs) {
+    if (!cand_count || cand_cap < 1 || cand_cap > kMaxV) return QS_ERR_INVALID_ARG;
+  }
+  if (!aligned(temperature, 4) || !aligned(top_k, 4) || !aligned(top_p, 4) ||
+      !aligned(row_status, 4) || !aligned(keep_mask, 4) || !aligned(cand_ids, 4) ||
+      !aligned(cand_probs, 4) || !aligned(cand_count, 4) || !aligned(dense_probs, 4) ||
+      !aligned(debug_stats, 4) || !aligned(tokens, 4) || !aligned(seed, 8) ||
+      !aligned(offset, 8) || !aligned(uniforms, 8))
+    return QS_ERR_INVALID_ARG;
+
+  qs::FilterArgs a;
+  a.logits = static_cast<const uint8_t*>(logits);
+  a.row_bytes = row_stride * (dtype == QS_F32 ? 4 : 2);
+  a.V = (int)V;
+  a.seg = qs::seg_for((int)V);
+  a.T = temperature;
+  a.k = top_k;
+  a.p = top_p;
+  a.bitmask = bitmask;
+  a.bm_stride = bitmask_stride;
+  a.seed = seed;
+  a.offset = offset;
+  a.uniforms = uniforms;
+  a.tokens = tokens;
+  a.keep_mask = keep_mask;
+  a.cand_ids = cand_ids;
+  a.cand_probs = cand_probs;
+  a.cand_count = cand_count;
+  a.cand_cap = (cand_ids || cand_probs) ? cand_cap : 0;
+  a.dense = dense_probs;
+  a.status = row_status;
+  a.dbg = debug_stats;
+  a.flags = flags;
+  hipError_t e = qs::launch_filter(a, dtype, sample, (int)B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                   const float* temperature, const int32_t* top_k, const float* top_p,
+                   const uint32_t* bitmask, int64_t bitmask_stride, uint32_t* keep_mask,
+                   int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+                   float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+                   uint32_t flags, void* stream) {
+  return filter_common(false, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, nullptr, nullptr, nullptr, nullptr, keep_mask,
+                       cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
+                       debug_stats, flags, stream);
+}
+
+int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+              const float* temperature, const int32_t* top_k, const float* top_p,
+              const uint32_t* bitmask, int64_t bitmask_stride, const uint64_t* seed,
+              uint64_t* offset, const double* uniforms, int32_t* tokens, uint32_t* keep_mask,
+              int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              float* dense_probs, int32_t* row_status, int32_t* debug_stats, uint32_t flags,
+              void* stream) {
+  return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, keep_mask,
+                       cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
+                       debug_stats, flags, stream);
+}
+
+int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+              const uint32_t* bitmask, int64_t bitmask_stride, int32_t* tokens,
+              int32_t* row_status, void* stream) {
+  int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
+  if (rc != QS_OK) return rc;
+  if (B == 0) return QS_OK;
+  if (!tokens || !row_status || !aligned(tokens, 4) || !aligned(row_status, 4))
+    return QS_ERR_INVALID_ARG;
+  qs::ArgmaxArgs a;
+  a.logits = static_cast<const uint8_t*>(logits);
+  a.row_bytes = row_stride * (dtype == QS_F32 ? 4 : 2);
+  a.V = (int)V;
+  a.seg = qs::seg_for((int)V);
+  a.bitmask = bitmask;
+  a.bm_stride = bitmask_stride;
+  a.tokens = tokens;
+  a.status = row_status;
+  hipError_t e = qs::launch_argmax(a, dtype, (int)B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
+const char* qs_version(void) { return "qs 0.1.0 gfx950"; }
+
+}  // extern "C"

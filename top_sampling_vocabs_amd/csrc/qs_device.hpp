@@ -1,0 +1,218 @@
+// Device building blocks for the gfx950 filter/sample kernels: order-preserving
+// keys, wave64 DPP reductions, ballot-based scans, block reductions through LDS,
+// Philox4x32-10 and the row layout every kernel shares.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qs {
+
+constexpr int kThreads = 1024;            // one workgroup per row
+constexpr int kWaves = kThreads / 64;     // 16 wave64s
+constexpr int kChunk = 8;                 // elements a lane handles per step
+constexpr int kStep = 64 * kChunk;        // 512 elements per wave step
+constexpr int kPoolPerWave = 1024;        // LDS candidate entries per wave
+
+// ---------------------------------------------------------------------------
+// Order-preserving unsigned keys. key(a) < key(b) iff a < b and key(a) == key(b)
+// iff a == b for non-NaN values (so -0 and +0 share one key, as IEEE compares
+// them equal); -inf maps to kNegInf, +inf to kPosInf, positive NaNs above
+// kPosInf and negative NaNs below kNegInf. bf16 keys use 16 bits.
+template <int DT> struct Keys;
+
+template <> struct Keys<0> {  // float32
+  static constexpr uint32_t kNegInf = 0x007FFFFFu;
+  static constexpr uint32_t kPosInf = 0xFF800000u;
+  static constexpr uint32_t kMax = 0xFFFFFFFFu;
+  __device__ __forceinline__ static uint32_t of(uint32_t bits) {
+    bits = (bits == 0x80000000u) ? 0u : bits;  // -0 -> +0
+    uint32_t s = (uint32_t)((int32_t)bits >> 31);
+    return bits ^ (s | 0x80000000u);
+  }
+  __device__ __forceinline__ static float value(uint32_t key) {
+    uint32_t b = (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
+    return __uint_as_float(b);
+  }
+};
+
+template <> struct Keys<1> {  // bfloat16
+  static constexpr uint32_t kNegInf = 0x007Fu;
+  static constexpr uint32_t kPosInf = 0xFF80u;
+  static constexpr uint32_t kMax = 0xFFFFu;
+  __device__ __forceinline__ static uint32_t of(uint32_t bits16) {
+    bits16 = (bits16 == 0x8000u) ? 0u : bits16;  // -0 -> +0
+    return bits16 ^ ((bits16 & 0x8000u) ? 0xFFFFu : 0x8000u);
+  }
+  __device__ __forceinline__ static float value(uint32_t key) {
+    uint32_t b = (key & 0x8000u) ? (key ^ 0x8000u) : (~key & 0xFFFFu);
+    return __uint_as_float(b << 16);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Lane helpers.
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// number of set bits of `mask` in lanes strictly below this lane
+__device__ __forceinline__ uint32_t count_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Wave-uniform values made explicit (scalar registers).
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ double uni(double v) {
+  uint64_t b = __double_as_longlong(v);
+  uint32_t lo = uni((uint32_t)b), hi = uni((uint32_t)(b >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ bool uni(bool v) { return uni((uint32_t)v) != 0u; }
+
+// Exclusive prefix over lanes of a value in [0, 15], and the wave total, from
+// four bit-sliced ballots.
+__device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t& total) {
+  uint64_t b0 = ballot(c & 1u), b1 = ballot(c & 2u), b2 = ballot(c & 4u),
+           b3 = ballot(c & 8u);
+  total = (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) +
+                     8 * __popcll(b3));
+  return count_below(b0) + 2u * count_below(b1) + 4u * count_below(b2) +
+         8u * count_below(b3);
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 all-reductions. Inside each 16-lane row: DPP quad_perm xor-1,
+// quad_perm xor-2, row_half_mirror, row_mirror (every lane of the row ends
+// with the row total); across the four rows: readlane of lanes 0/16/32/48.
+// The combination order is fixed, so fp64 sums are deterministic.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  uint64_t b = __double_as_longlong(v);
+  uint32_t lo = dpp_u32<CTRL>((uint32_t)b);
+  uint32_t hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  uint64_t b = __double_as_longlong(v);
+  uint32_t lo = readlane_u32((uint32_t)b, l), hi = readlane_u32((uint32_t)(b >> 32), l);
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+struct OpSum { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a + b; } };
+struct OpMax { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a > b ? a : b; } };
+struct OpMin { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a < b ? a : b; } };
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
+  v = Op::f(v, dpp_u32<kDppXor1>(v));
+  v = Op::f(v, dpp_u32<kDppXor2>(v));
+  v = Op::f(v, dpp_u32<kDppHalfMirror>(v));
+  v = Op::f(v, dpp_u32<kDppMirror>(v));
+  uint32_t a = readlane_u32(v, 0), b = readlane_u32(v, 16);
+  uint32_t c = readlane_u32(v, 32), d = readlane_u32(v, 48);
+  return Op::f(Op::f(a, b), Op::f(c, d));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  double a = readlane_f64(v, 0), b = readlane_f64(v, 16);
+  double c = readlane_f64(v, 32), d = readlane_f64(v, 48);
+  return (a + b) + (c + d);
+}
+
+// (minimum key, number of occurrences of that minimum) pairs.
+struct MinCnt {
+  uint32_t key;
+  uint32_t cnt;
+};
+__device__ __forceinline__ MinCnt mc_merge(MinCnt a, MinCnt b) {
+  MinCnt r;
+  r.key = a.key < b.key ? a.key : b.key;
+  r.cnt = (a.key == r.key ? a.cnt : 0u) + (b.key == r.key ? b.cnt : 0u);
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ MinCnt dpp_mc(MinCnt v) {
+  return MinCnt{dpp_u32<CTRL>(v.key), dpp_u32<CTRL>(v.cnt)};
+}
+__device__ __forceinline__ MinCnt wave_reduce_mc(MinCnt v) {
+  v = mc_merge(v, dpp_mc<kDppXor1>(v));
+  v = mc_merge(v, dpp_mc<kDppXor2>(v));
+  v = mc_merge(v, dpp_mc<kDppHalfMirror>(v));
+  v = mc_merge(v, dpp_mc<kDppMirror>(v));
+  MinCnt a{readlane_u32(v.key, 0), readlane_u32(v.cnt, 0)};
+  MinCnt b{readlane_u32(v.key, 16), readlane_u32(v.cnt, 16)};
+  MinCnt c{readlane_u32(v.key, 32), readlane_u32(v.cnt, 32)};
+  MinCnt d{readlane_u32(v.key, 48), readlane_u32(v.cnt, 48)};
+  return mc_merge(mc_merge(a, b), mc_merge(c, d));
+}
+
+// Inclusive scan of doubles over the lanes of a wave (shuffle-up ladder; used
+// once per sampled row).
+__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    double o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Block reduction scratch: each wave deposits wave-uniform values in its slot,
+// one barrier, then every thread combines the 16 slots in wave order. Two
+// parities alternate so one barrier per reduction suffices.
+constexpr int kSlots = 40;
+struct RedScratch {
+  uint32_t v[2][kWaves][kSlots];
+};
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// two-multiplier S-box on a 4x32 counter, key advanced by the Weyl constants
+// between rounds.
+__device__ __forceinline__ uint32_t philox_u24(uint64_t seed, uint64_t offset) {
+  uint32_t c0 = (uint32_t)offset, c1 = (uint32_t)(offset >> 32), c2 = 0u, c3 = 0u;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0 >> 8;
+}
+
+}  // namespace qs

@@ -1,0 +1,50 @@
+// Kernel argument blocks and launchers shared by the C-ABI layer and the
+// kernels' translation unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qs {
+
+struct FilterArgs {
+  const uint8_t* logits;
+  int64_t row_bytes;      // distance between rows in bytes
+  int V;
+  int seg;                // tokens per wave slice (multiple of 32)
+  const float* T;
+  const int32_t* k;
+  const float* p;
+  const uint32_t* bitmask;
+  int64_t bm_stride;      // words
+  const uint64_t* seed;
+  uint64_t* offset;
+  const double* uniforms;
+  int32_t* tokens;
+  uint32_t* keep_mask;
+  int32_t* cand_ids;
+  float* cand_probs;
+  int32_t* cand_count;
+  int64_t cand_cap;
+  float* dense;
+  int32_t* status;
+  int32_t* dbg;
+  uint32_t flags;
+};
+
+struct ArgmaxArgs {
+  const uint8_t* logits;
+  int64_t row_bytes;
+  int V;
+  int seg;
+  const uint32_t* bitmask;
+  int64_t bm_stride;
+  int32_t* tokens;
+  int32_t* status;
+};
+
+int seg_for(int V);
+hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st);
+hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st);
+
+}  // namespace qs
