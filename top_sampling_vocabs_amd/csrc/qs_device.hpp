@@ -12,41 +12,59 @@ constexpr int kThreads = 1024;            // one workgroup per row
 constexpr int kWaves = kThreads / 64;     // 16 wave64s
 constexpr int kChunk = 8;                 // elements a lane handles per step
 constexpr int kStep = 64 * kChunk;        // 512 elements per wave step
-constexpr int kPoolPerWave = 1024;        // LDS candidate entries per wave
+constexpr int kPoolBytes = 131072;        // LDS candidate pool per workgroup
+
+// Candidate pool entry layout per dtype: key plus the token id relative to the
+// wave's slice start (16 bits, so slices of at most 65536 tokens).
+template <int DT> struct PoolLayout;
+template <> struct PoolLayout<0> {   // fp32: 4-byte key + 2-byte id
+  using KeyT = uint32_t;
+  static constexpr int kPerWave = 1344;
+};
+template <> struct PoolLayout<1> {   // bf16: 2-byte key + 2-byte id
+  using KeyT = uint16_t;
+  static constexpr int kPerWave = 2048;
+};
+static_assert(kWaves * PoolLayout<0>::kPerWave * 6 <= kPoolBytes, "fp32 pool size");
+static_assert(kWaves * PoolLayout<1>::kPerWave * 4 <= kPoolBytes, "bf16 pool size");
+static_assert((PoolLayout<0>::kPerWave * 2) % 16 == 0, "pool rows stay 16-byte aligned");
 
 // ---------------------------------------------------------------------------
-// Order-preserving unsigned keys. key(a) < key(b) iff a < b and key(a) == key(b)
-// iff a == b for non-NaN values (so -0 and +0 share one key, as IEEE compares
-// them equal); -inf maps to kNegInf, +inf to kPosInf, positive NaNs above
-// kPosInf and negative NaNs below kNegInf. bf16 keys use 16 bits.
+// Order-preserving unsigned keys: the sign-magnitude bit pattern mapped to
+// offset binary. key(a) < key(b) iff a < b and key(a) == key(b) iff a == b for
+// non-NaN values (-0 and +0 share one key, as IEEE compares them equal); -inf
+// maps to kNegInf, +inf to kPosInf, positive NaNs above kPosInf and negative
+// NaNs below kNegInf. bf16 keys use 16 bits.
 template <int DT> struct Keys;
 
 template <> struct Keys<0> {  // float32
-  static constexpr uint32_t kNegInf = 0x007FFFFFu;
+  static constexpr uint32_t kNegInf = 0x00800000u;
   static constexpr uint32_t kPosInf = 0xFF800000u;
   static constexpr uint32_t kMax = 0xFFFFFFFFu;
+  // sign-magnitude -> offset binary: 0x80000000 +/- magnitude (both zeros 0x80000000)
   __device__ __forceinline__ static uint32_t of(uint32_t bits) {
-    bits = (bits == 0x80000000u) ? 0u : bits;  // -0 -> +0
-    uint32_t s = (uint32_t)((int32_t)bits >> 31);
-    return bits ^ (s | 0x80000000u);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    return (bits & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
   }
-  __device__ __forceinline__ static float value(uint32_t key) {
-    uint32_t b = (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
-    return __uint_as_float(b);
+  __device__ __forceinline__ static uint32_t raw(uint32_t key) {
+    return key >= 0x80000000u ? key - 0x80000000u : 0x80000000u | (0x80000000u - key);
   }
+  __device__ __forceinline__ static float value(uint32_t key) { return __uint_as_float(raw(key)); }
 };
 
 template <> struct Keys<1> {  // bfloat16
-  static constexpr uint32_t kNegInf = 0x007Fu;
+  static constexpr uint32_t kNegInf = 0x0080u;
   static constexpr uint32_t kPosInf = 0xFF80u;
   static constexpr uint32_t kMax = 0xFFFFu;
   __device__ __forceinline__ static uint32_t of(uint32_t bits16) {
-    bits16 = (bits16 == 0x8000u) ? 0u : bits16;  // -0 -> +0
-    return bits16 ^ ((bits16 & 0x8000u) ? 0xFFFFu : 0x8000u);
+    const uint32_t mag = bits16 & 0x7FFFu;
+    return (bits16 & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+  }
+  __device__ __forceinline__ static uint32_t raw(uint32_t key) {
+    return key >= 0x8000u ? key - 0x8000u : 0x8000u | (0x8000u - key);
   }
   __device__ __forceinline__ static float value(uint32_t key) {
-    uint32_t b = (key & 0x8000u) ? (key ^ 0x8000u) : (~key & 0xFFFFu);
-    return __uint_as_float(b << 16);
+    return __uint_as_float(raw(key) << 16);
   }
 };
 
@@ -190,6 +208,29 @@ constexpr int kSlots = 40;
 struct RedScratch {
   uint32_t v[2][kWaves][kSlots];
 };
+
+// ---------------------------------------------------------------------------
+// exp(x) in fp64 for the weights exp((z - m) / T), x <= ~0: x = n ln2 + r with
+// n = rint(x / ln2) and a two-part ln2, |r| <= ln2/2, then the degree-11 Taylor
+// polynomial of e^r (truncation < 7e-15 relative) and a power-of-two scale.
+__device__ __forceinline__ double exp64(double x) {
+  if (!(x > -745.0)) return 0.0;
+  const double n = rint(x * 1.4426950408889634);
+  const double r = fma(-n, 2.3190468138462996e-17, fma(-n, 0.6931471805599453, x));
+  double q = 2.5052108385441720e-08;             // 1/11!
+  q = fma(q, r, 2.7557319223985893e-07);         // 1/10!
+  q = fma(q, r, 2.7557319223985888e-06);         // 1/9!
+  q = fma(q, r, 2.4801587301587302e-05);         // 1/8!
+  q = fma(q, r, 1.9841269841269841e-04);         // 1/7!
+  q = fma(q, r, 1.3888888888888889e-03);         // 1/6!
+  q = fma(q, r, 8.3333333333333333e-03);         // 1/5!
+  q = fma(q, r, 4.1666666666666667e-02);         // 1/4!
+  q = fma(q, r, 1.6666666666666667e-01);         // 1/3!
+  q = fma(q, r, 0.5);
+  q = fma(q, r, 1.0);
+  q = fma(q, r, 1.0);
+  return ldexp(q, (int)n);
+}
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
