@@ -51,6 +51,9 @@ def parse():
                     help="rows for the oracle baseline (0 = sized to ~15 s)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, also run plain device copies of the "
+                         "logits (known bytes) so counter runs can scale FETCH/WRITE sizes")
     return ap.parse_args()
 
 
@@ -96,6 +99,59 @@ class Prepared:
         rc = self.lib.qs_sample(*self.args)
         if rc != 0:
             raise RuntimeError(f"qs_sample returned {rc}")
+
+
+def source_digest():
+    """sha256 over the HIP sources the library is built from: a stored counter
+    reading applies only to the kernel it was taken on."""
+    import hashlib
+    csrc = os.path.join(ROOT, "top_sampling_vocabs_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(cfg):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
+    (scaled by a plain copy of known size), from profiles/, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_workload{cfg}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, v = line.partition(":")
+                vals[key.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(preps, reps=20):
+    """Plain device-to-device copies of each input set's logits: a kernel of
+    known bytes (read = write = logits size) for scaling counter readings."""
+    import torch
+    srcs = [p.logits for p in preps]
+    dsts = [torch.empty_like(s) for s in srcs]
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        dsts[i % len(dsts)].copy_(srcs[i % len(srcs)])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = srcs[0].numel() * srcs[0].element_size()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 5),
+            "gbs_rw": round(2 * nbytes / (ms / 1e3) / 1e9, 1)}
 
 
 def cpu_baseline(w, rows):
@@ -158,6 +214,8 @@ def main():
     st = preps[0].status.cpu().numpy()
     assert ((st == 0) | (st == 1) | (st == 2) | (st == 3) | (st == 5)).all(), np.unique(st)
 
+    copy = copy_calibration(preps) if args.copy_calibration else None
+
     cpu = None
     if not args.no_cpu:
         n = args.cpu_rows or {1: 4, 2: 64, 3: 128, 4: 48, 5: 128}[cfg]
@@ -185,13 +243,15 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": stored_traffic(cfg),
                      "kernel_ms_mean": round(mean_launch, 5),
                      "kernel_ms_p50": round(float(np.median(per)), 5),
                      "kernel_ms_p99": round(float(np.percentile(per, 99)), 5)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
+    if copy is not None:
+        line["copy_calibration"] = copy
     print(json.dumps(line), flush=True)
 
 
