@@ -79,6 +79,10 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
  * truncation). 0 is the normal path. */
 #define QS_FLAG_FORCE_MISS     1u  /* run every search over the full row        */
 #define QS_FLAG_NO_TRUNCATION  2u  /* skip the sigma-truncation compaction      */
+#define QS_FLAG_PIVOT_SEARCH   4u  /* quaternary pivot search also on bf16 pools
+                                      (instead of the histogram scan)           */
+#define QS_FLAG_STREAM         8u  /* stream the row even when it fits in
+                                      registers                                 */
 
 /* Filter a batch: kept-candidate mask and renormalised probabilities.
  *

@@ -68,11 +68,13 @@ def test_parity_small(qs, cfg):
     assert rep.band_rows <= max(1, w.B // 50)
 
 
+@pytest.mark.parametrize("stream", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 5, 31, 33, 100, 511, 513, 1000, 5003, 8193, 40000])
-def test_parity_ragged(qs, dtype, V):
+def test_parity_ragged(qs, dtype, V, stream):
     """Odd vocabulary sizes (ragged final step, partial mask word, V < one wave
-    step), many exact ties (rounded logits), -inf, and every parameter mode."""
+    step), many exact ties (rounded logits), -inf, and every parameter mode;
+    rows held in registers and rows streamed through the prefetch ring."""
     import torch
     rng = np.random.default_rng(V * 7 + (dtype == "bf16"))
     B = 36
@@ -102,7 +104,8 @@ def test_parity_ragged(qs, dtype, V):
     d["logits"] = d["logits"][:, :V]  # row stride stays padded
     w.logits = logits[:, :V]
     uni = rng.random(B)
-    out = run_all(qs, d, uniforms=torch.from_numpy(uni).cuda(), V=V)
+    out = run_all(qs, d, uniforms=torch.from_numpy(uni).cuda(), V=V,
+                  flags=qs.FLAG_STREAM if stream else 0)
     res = oracle.filter_batch(w.logits, dtype, T, k, p, w.bitmask)
     rep = Report()
     compare_filter(w, res, out, range(B), rep)
@@ -112,22 +115,28 @@ def test_parity_ragged(qs, dtype, V):
 
 def test_path_invariance(qs):
     """Forced fallback and no truncation run every search over the full row; the
-    outputs are bitwise identical to the truncated path (page "Qrita" ablation
-    runs D and E compute the same result as run A)."""
+    pivot-search switch replaces the histogram scan by the quaternary search;
+    the stream switch reads the row through the prefetch ring instead of the
+    register-resident pass. Every variant gives bitwise identical outputs (page
+    "Qrita" ablation runs D and E compute the same result as run A)."""
     import torch
-    for cfg in (2, 3, 5):
+    variants = (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION, qs.FLAG_PIVOT_SEARCH,
+                qs.FLAG_STREAM, qs.FLAG_STREAM | qs.FLAG_PIVOT_SEARCH)
+    for cfg in (1, 2, 3, 5):
         w = workloads.make(cfg, **SMALL[cfg])
         d = to_device(w)
         uni = torch.from_numpy(np.random.default_rng(9).random(w.B)).cuda()
         base = run_all(qs, d, uniforms=uni, V=w.V)
-        for flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION):
+        for flags in variants:
+            print(f"workload {cfg} flags {flags}", flush=True)
             alt = run_all(qs, d, uniforms=uni, flags=flags, V=w.V)
             for key in ("keep_mask", "cand_count", "dense", "tokens", "status"):
                 assert torch.equal(base[key], alt[key]), (cfg, flags, key)
             assert lists_equal(base, alt), (cfg, flags)
             dbg = alt["debug"].cpu().numpy()
             ok = base["status"].cpu().numpy() == 0
-            assert (dbg[ok, 0] == 1).all()  # every OK row took the full-row path
+            if flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION):
+                assert (dbg[ok, 0] == 1).all()  # every OK row took the full-row path
 
 
 def lists_equal(a, b):

@@ -29,6 +29,8 @@ QS_BF16 = 1
 
 FLAG_FORCE_MISS = 1
 FLAG_NO_TRUNCATION = 2
+FLAG_PIVOT_SEARCH = 4
+FLAG_STREAM = 8
 
 EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_version")
 

@@ -41,7 +41,9 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
                   int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* stream) {
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
   if (rc != QS_OK) return rc;
-  if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION)) return QS_ERR_INVALID_ARG;
+  if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION | QS_FLAG_PIVOT_SEARCH |
+                QS_FLAG_STREAM))
+    return QS_ERR_INVALID_ARG;
   if (B == 0) return QS_OK;
   if (!temperature || !top_k || !top_p || !row_status) return QS_ERR_INVALID_ARG;
   if (!sample && !keep_mask) return QS_ERR_INVALID_ARG;
@@ -63,7 +65,7 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.logits = static_cast<const uint8_t*>(logits);
   a.row_bytes = row_stride * (dtype == QS_F32 ? 4 : 2);
   a.V = (int)V;
-  a.seg = qs::seg_for((int)V);
+  a.seg = qs::seg_for((int)V);  // the launcher sets the slice length of its tier
   a.T = temperature;
   a.k = top_k;
   a.p = top_p;

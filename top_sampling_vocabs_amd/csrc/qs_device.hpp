@@ -6,24 +6,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace qs {
 
 constexpr int kThreads = 1024;            // one workgroup per row
 constexpr int kWaves = kThreads / 64;     // 16 wave64s
 constexpr int kChunk = 8;                 // elements a lane handles per step
 constexpr int kStep = 64 * kChunk;        // 512 elements per wave step
-constexpr int kPoolBytes = 131072;        // LDS candidate pool per workgroup
+constexpr int kPoolBytes = 98304;         // LDS candidate pool per workgroup
+constexpr int kResidentMaxSteps = 20;     // longest slice held in registers (steps)
 
 // Candidate pool entry layout per dtype: key plus the token id relative to the
 // wave's slice start (16 bits, so slices of at most 65536 tokens).
 template <int DT> struct PoolLayout;
 template <> struct PoolLayout<0> {   // fp32: 4-byte key + 2-byte id
   using KeyT = uint32_t;
-  static constexpr int kPerWave = 1344;
+  static constexpr int kPerWave = 1024;
 };
 template <> struct PoolLayout<1> {   // bf16: 2-byte key + 2-byte id
   using KeyT = uint16_t;
-  static constexpr int kPerWave = 2048;
+  static constexpr int kPerWave = 1536;
 };
 static_assert(kWaves * PoolLayout<0>::kPerWave * 6 <= kPoolBytes, "fp32 pool size");
 static_assert(kWaves * PoolLayout<1>::kPerWave * 4 <= kPoolBytes, "bf16 pool size");
@@ -67,6 +70,17 @@ template <> struct Keys<1> {  // bfloat16
     return __uint_as_float(raw(key) << 16);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so that
+// register arrays are only ever indexed by constants.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Lane helpers.

@@ -1,33 +1,37 @@
 // Exact top-k / top-p filter-and-sample kernels for gfx950 (MI355X).
 //
 // One 1024-thread workgroup owns one row. Its 16 wave64s each own a
-// contiguous slice of the vocabulary (a multiple of 32 tokens, so every
-// packed-mask word belongs to one wave), which keeps every per-wave walk in
-// token-id order and makes the outputs deterministic.
+// contiguous slice of the vocabulary (a multiple of 512 tokens for rows held
+// in registers, of 32 tokens otherwise), so every packed-mask word belongs to
+// one wave and every per-wave walk runs in token-id order; the outputs are
+// deterministic.
 //
 // Per row (page "Qrita", overall framework and key designs 1-3):
-//  1. sigma-truncation (key design 1): the first 512-token step of each
-//     slice is a sample (8192 tokens) for mean, sigma and the sample maximum;
-//     the threshold t = t0 - 0.2|t0| uses the Gaussian quantile of k/V
-//     (top-k) or of p under the mass-weighted Gaussian (top-p). One pipelined
-//     pass over the row then compacts the legal tokens with z >= t into a
-//     per-wave LDS pool, in id order, counts legal tokens, checks for NaN,
-//     and for rows with top-k off accumulates the mass below t.
-//  2. hit test: |Z_t| >= k (top-k), or mass(Z_t) >= p * W (top-p only);
-//     otherwise every later step runs over the full row (the page's
-//     fallback Z_s = Z).
-//  3. quaternary three-pivot search (key design 2) for the k-th largest
-//     value: pivots at 1/4, 1/2, 3/4 of the current key interval; one fused
-//     pass counts N_tau, the minimum above tau and its multiplicity for all
-//     three pivots; it stops when N_tau >= k and N_tau - N_zm < k. Pivots are
-//     order-preserving integer keys, so a search ends within 8 (bf16) or 16
-//     (fp32) rounds even when values repeat. For bf16 pools the pass runs over
-//     a per-key histogram of the pool instead of its elements.
-//  4. the same search on fp64 mass for the top-p boundary inside the top-k set.
-//  5. duplicate handling (key design 3): at the boundary value only the
-//     earliest N_keep token ids are kept; the id cut comes from an ordered
-//     per-wave count.
-//  6. renormalise, write the packed mask, id-ordered candidate lists and
+//  1. sigma-truncation (key design 1). Rows of up to 20 loads of 16 bytes per
+//     lane are held in VGPRs: every load of the row is issued up front, so the
+//     whole row is in flight at once. The first 512-token step of each slice
+//     (8192 tokens) is the sample for mean, sigma and the sample maximum; the
+//     threshold t = t0 - 0.2|t0| uses the Gaussian quantile of k/V (top-k) or
+//     of p under the mass-weighted Gaussian (top-p). Each later step is
+//     compacted as soon as it arrives: legal tokens with z >= t go, in id
+//     order, to a per-wave LDS pool and (bf16) to a per-key histogram; the pass
+//     also counts legal tokens, flags NaN / -inf, and for rows with top-k off
+//     sums the mass below t. Longer rows stream through a prefetch ring with
+//     the same per-step work.
+//  2. hit test: |Z_t| > k (top-k), or mass(Z_t) >= p * W (top-p only);
+//     otherwise every later step runs over the full row, re-read from memory
+//     (the page's fallback Z_s = Z).
+//  3. the k-th largest value and the top-p boundary value. On a bf16 pool the
+//     keys above t span a short key range: a suffix scan of the per-key
+//     histogram (counts, then fp64 masses) evaluates the page's stop test
+//     N_tau >= k > N_tau - N_zm at every key at once. Element sources (fp32
+//     pools, the full row) run the quaternary three-pivot search (key design
+//     2): pivots at 1/4, 1/2, 3/4 of the key interval, one fused pass counting
+//     N_tau, the minimum above tau and its multiplicity for all three pivots.
+//  4. duplicate handling (key design 3): at the boundary value only the
+//     earliest N_keep token ids are kept; each wave keeps its share of that
+//     quota, in id order.
+//  5. renormalise, write the packed mask, id-ordered candidate lists and
 //     optional dense probabilities, and draw the token by an inverse CDF in
 //     id order with Philox4x32-10 (sampling-contract page, sections 02 and 06).
 
@@ -50,7 +54,14 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
   return (m & a) | (~m & b);
 }
 
-constexpr int kHistBins = 2048;   // bf16 pool histogram (keys tkey .. tkey+2047)
+constexpr int kHistBins = kThreads;   // bf16 pool histogram: one key per thread
+// Register-resident tiers (steps of 512 tokens per wave slice), per dtype:
+// fp32 rows take two 16-byte loads per step, bf16 rows one.
+constexpr int kResidentTier[2][2] = {{5, 10}, {5, 20}};
+// Register ring depth (steps in flight per wave) of those tiers.
+constexpr int kRingDepth[2] = {5, 10};
+constexpr int kStageWords = 320;      // packed-mask words of one slice held in LDS
+static_assert(kResidentMaxSteps * (kStep / 32) <= kStageWords, "stage holds a resident slice");
 
 // Relative error bound of one hardware exp2 (v_exp_f32), taken as 4 ulp.
 constexpr double kExp2Err = 2.384185791015625e-07;  // 2^-22
@@ -66,7 +77,9 @@ __device__ __forceinline__ double weight(uint32_t key, double m, double invT) {
 // k/V) for top-k; for top-p the mass-weighted Gaussian N(mu + sigma^2/T,
 // sigma^2), truncated at the sample maximum, gives the value above which a
 // fraction p of the mass lies. t = t0 - 0.2|t0|, never above the sample max.
-// Returns -inf when every finite legal token must be a candidate.
+// The quantiles are single precision: t only decides how many tokens are
+// compacted, never which tokens are kept. Returns -inf when every finite
+// legal token must be a candidate.
 __device__ __forceinline__ double truncation_value(double n_s, double sum, double sumsq,
                                                    double ms, double frac_legal, int V,
                                                    bool greedy, bool topk_on, int k,
@@ -81,14 +94,14 @@ __device__ __forceinline__ double truncation_value(double n_s, double sum, doubl
   if (topk_on) {
     const double q = (double)k / (frac_legal * (double)V);
     if (!(q < 1.0)) return ninf;
-    t0 = mu + sd * (1.4142135623730951 * erfcinv(2.0 * q));
+    t0 = mu + sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * q)));
   } else if (topp_on) {
     if (!(sd > 0.0)) return ninf;
     const double mp = mu + sd * sd * invT;
     const double a = (ms - mp) / sd;
-    const double c = (1.0 - p) * 0.5 * erfc(-a * 0.7071067811865476);
+    const double c = (1.0 - p) * 0.5 * (double)erfcf((float)(-a * 0.7071067811865476));
     if (!(c > 0.0)) return ninf;
-    t0 = mp - sd * (1.4142135623730951 * erfcinv(2.0 * c));
+    t0 = mp - sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * c)));
   } else {
     return ninf;
   }
@@ -108,22 +121,54 @@ __device__ __forceinline__ uint32_t raw_floor(double t) {
   return h;
 }
 
+// Inclusive prefix over the lanes of a wave (ascending lanes); excl gets the
+// inclusive value of the lane below (0 in lane 0), so that neighbouring
+// partial sums are the same floating-point values.
+__device__ __forceinline__ double wave_incl_f64(double x, int lane, double& excl) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  const double b = __shfl_up(x, 1, 64);
+  excl = lane > 0 ? b : 0.0;
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // ---------------------------------------------------------------------------
-template <int DT, bool SAMPLE>
+// NL > 0: the row is held in registers, NL steps of 512 tokens per wave slice.
+// NL == 0: the row streams through a prefetch ring.
+template <int DT, bool SAMPLE, int NL>
 __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   using K = Keys<DT>;
   using PL = PoolLayout<DT>;
   using PKey = typename PL::KeyT;
   constexpr uint32_t kCap = (uint32_t)PL::kPerWave;
+  constexpr bool kResident = NL > 0;
+  constexpr int kHB = DT == 1 ? kHistBins : 1;
+  static_assert(NL <= kResidentMaxSteps, "resident rows are at most 20 steps per slice");
   __shared__ __align__(16) uint8_t pool_raw[kPoolBytes];
+  __shared__ __align__(16) uint32_t stage[kWaves][kStageWords];
   __shared__ __align__(16) uint4 lut[DT == 1 ? 256 : 1];
-  __shared__ uint32_t hist[DT == 1 ? kHistBins : 1];
+  __shared__ uint32_t hist[kHB];
+  __shared__ double binw[kHB];
   __shared__ RedScratch red;
   __shared__ struct {
     uint32_t cnt[kWaves];
     uint32_t gt[kWaves];
     uint32_t ties[kWaves];
-    double q[kWaves];
+    double mass[kWaves];
+    int32_t bsel;
+    uint32_t sel_u[2];
+    double sel_d[2];
   } info;
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
@@ -144,13 +189,16 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   sl.wb = uni(min(V, w * a.seg));
   sl.we = uni(min(V, (w + 1) * a.seg));
   const int W = (V + 31) >> 5;
+  const uint32_t* const bmrow = a.bitmask ? a.bitmask + (size_t)r * a.bm_stride : nullptr;
 
   uint32_t* mask_row = a.keep_mask ? a.keep_mask + (size_t)r * W : nullptr;
   float* dense_row = a.dense ? a.dense + (size_t)r * V : nullptr;
+  // this slice's packed-mask words fit the LDS stage (always for resident rows)
+  const bool stage_ok = (sl.we - sl.wb + 31) / 32 <= kStageWords;
 
-  // Zero this wave's share of the mask and dense outputs and wait until the
-  // stores have completed, so that this wave's later scatter into the same
-  // slice lands after them.
+  // Zero this wave's share of the mask and dense outputs in memory and wait
+  // until the stores have completed, so that a later scatter into the same
+  // slice by this wave lands after them.
   auto zero_outputs = [&]() {
     if (mask_row && sl.we > sl.wb) {  // a non-empty slice starts on a word boundary
       int w0 = sl.wb >> 5, w1 = (sl.we + 31) >> 5;
@@ -193,6 +241,44 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const bool need_bg = topp_on && !topk_req;
   const bool no_trunc = (a.flags & QS_FLAG_NO_TRUNCATION) != 0u;
 
+  // -- the sample: step 0 of every slice ----------------------------------------
+  // The first 512 tokens of each of the 16 slices (8192 tokens) are the only
+  // request in flight until they have returned, so they come back at unloaded
+  // latency; the rest of the row is requested after them. Step 0 stays in the
+  // ring for the pass.
+  constexpr int kPiece = 16 / (DT == 0 ? 4 : 2);  // tokens per 16-byte piece
+  constexpr int kPieces = DT == 0 ? 2 : 1;        // 16-byte loads per lane per step
+  constexpr int RD = kResident ? (NL < kRingDepth[DT] ? NL : kRingDepth[DT]) : 1;
+  uint4 buf[RD][kPieces];
+  // A 16-byte piece that starts below V lies inside the row's stride; pieces
+  // past the slice read the slice's last piece instead (their tokens are
+  // clipped), so every lane issues the same loads.
+  const int last_piece = sl.we > sl.wb ? (sl.we - 1) & ~(kPiece - 1) : 0;
+  const int lane_e = sl.wb + lane * kChunk;
+  auto res_issue = [&](auto stc) {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (kResident && st < NL) {
+#pragma unroll
+      for (int pc = 0; pc < kPieces; ++pc) {
+        const int ep = min(lane_e + st * kStep + pc * kPiece, last_piece);
+        buf[st % RD][pc] = *reinterpret_cast<const uint4*>(chunk_ptr<DT>(sl.row, ep));
+      }
+    }
+  };
+  constexpr int D = DT == 1 ? 8 : 4;
+  using Reader = std::conditional_t<kResident, NoReader<DT>, RowReader<DT, D>>;
+  Reader rd(sl, lane);
+  const int nst = kResident ? NL : rd.n;
+  uint32_t s0mb = 0u;
+  if constexpr (kResident) {
+    res_issue(std::integral_constant<int, 0>{});
+    const int e0 = min(lane_e, last_piece);
+    s0mb = sl.mrow ? (uint32_t)sl.mrow[e0 >> 3] : 0xFFu;
+  } else {
+    if (nst > 0) rd.issue(0, 0);
+  }
+
+  // -- tables ----------------------------------------------------------------------
   if constexpr (DT == 1) {  // pair masks of every legal byte: 0xFFFF per legal token
     if (tid < 256) {
       uint32_t v[4];
@@ -202,25 +288,29 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
                ((((uint32_t)tid >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
       lut[tid] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+    hist[tid] = 0u;
   }
+  if (tid == 0) info.bsel = -1;
 
-  // -- one pass over the row, with the sample taken from its first step --------
-  constexpr int D = DT == 1 ? 8 : 4;
-  RowReader<DT, D> rd(sl, lane);
-  const int nst = rd.n;
-#pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (i < nst) rd.issue(i, i);
-
-  // sample statistics of step 0 (legal finite tokens)
+  // -- per-lane sample statistics (legal finite tokens of step 0) ------------------
   double s_n = 0.0, s_sum = 0.0, s_sq = 0.0, s_all = 0.0;
   uint32_t s_maxk = 0u;
-  if (nst > 0) {
+  if (sl.we > sl.wb) {
     Raw<DT> raw;
     uint32_t mb;
-    rd.fetch(0, 0, raw, mb);
-    const int e = rd.first(0);
-    s_all = (double)max(0, min(8, min(sl.we, sl.wb + kStep) - e));
+    if constexpr (kResident) {
+      raw.r[0] = buf[0][0].x; raw.r[1] = buf[0][0].y;
+      raw.r[2] = buf[0][0].z; raw.r[3] = buf[0][0].w;
+      if constexpr (DT == 0) {
+        raw.r[4] = buf[0][kPieces - 1].x; raw.r[5] = buf[0][kPieces - 1].y;
+        raw.r[6] = buf[0][kPieces - 1].z; raw.r[7] = buf[0][kPieces - 1].w;
+      }
+      const int rem = sl.we - lane_e;
+      mb = s0mb & (rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u));
+    } else {
+      rd.fetch(0, 0, raw, mb);
+    }
+    s_all = (double)max(0, min(8, sl.we - lane_e));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t key = K::of(raw.bits(j));
@@ -231,6 +321,30 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       }
     }
   }
+
+  // -- the rest of the row: packed-mask words of the slice and the ring -----------
+  constexpr int kMW = NL * (kStep / 32);  // packed-mask words of a resident slice
+  constexpr int kML = kResident ? (kMW + 63) / 64 : 1;
+  uint32_t mw[kML];
+  if constexpr (kResident) {
+    // without a bitmask the word loads read the row start (16 bytes at least)
+    // and are ignored, so that the load sequence has no branch
+    const uint32_t* const mwsrc = bmrow ? bmrow : reinterpret_cast<const uint32_t*>(sl.row);
+    const int w0 = sl.wb >> 5;
+    const int wlim = bmrow ? min(W, (sl.we + 31) >> 5) : 0;  // words of this slice
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+      const int wi = w0 + lane + 64 * i;
+      mw[i] = mwsrc[(lane + 64 * i < kMW && wi < wlim) ? wi : 0];
+    }
+    static_for<1, RD>(res_issue);
+  } else {
+#pragma unroll
+    for (int i = 1; i < D; ++i)
+      if (i < nst) rd.issue(i, i);
+  }
+
+  // -- the threshold, while the row's loads are in flight ------------------------
   {
     double st[4] = {s_n, s_sum, s_sq, s_all};
 #pragma unroll
@@ -246,22 +360,55 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       red.v[par][w][8] = mx;
     }
   }
-  __syncthreads();  // also publishes the pair-mask table
+  __syncthreads();  // sample partials, the pair-mask table, the zeroed histogram, bsel
   {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    uint32_t mx = 0u;
-    for (int ww = 0; ww < kWaves; ++ww) {
+    // lane i holds wave i's partials; the same combination order in every wave
+    const bool act = lane < kWaves;
+    double acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] += __longlong_as_double(((uint64_t)red.v[par][ww][2 * i + 1] << 32) |
-                                       red.v[par][ww][2 * i]);
-      const uint32_t m2 = red.v[par][ww][8];
-      mx = m2 > mx ? m2 : mx;
-    }
-    s_n = uni(acc[0]); s_sum = uni(acc[1]); s_sq = uni(acc[2]); s_all = uni(acc[3]);
-    s_maxk = uni(mx);
+    for (int i = 0; i < 4; ++i)
+      acc[i] = act ? __longlong_as_double(((uint64_t)red.v[par][lane][2 * i + 1] << 32) |
+                                          red.v[par][lane][2 * i])
+                   : 0.0;
+    const uint32_t mx = act ? red.v[par][lane][8] : 0u;
+    s_n = uni(wave_sum_f64(acc[0]));
+    s_sum = uni(wave_sum_f64(acc[1]));
+    s_sq = uni(wave_sum_f64(acc[2]));
+    s_all = uni(wave_sum_f64(acc[3]));
+    s_maxk = uni(wave_reduce<OpMax>(mx));
   }
   par ^= 1;
+  if constexpr (kResident) {  // stage this slice's packed-mask words
+    if (bmrow) {
+      const int w0 = sl.wb >> 5;
+      const int wlim = min(W, (sl.we + 31) >> 5);
+#pragma unroll
+      for (int i = 0; i < kML; ++i) {
+        const int wi = w0 + lane + 64 * i;
+        if (lane + 64 * i < kMW) stage[w][lane + 64 * i] = wi < wlim ? mw[i] : 0u;
+      }
+    }
+  }
+  const uint8_t* const stage_bytes = reinterpret_cast<const uint8_t*>(stage[w]) + lane;
+  // step ST of a resident slice: raw bits and legal bits (clipped to the slice)
+  auto res_fetch = [&](auto stc, Raw<DT>& raw, uint32_t& mb) {
+    if constexpr (kResident) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int sl_ = st % RD;
+      raw.r[0] = buf[sl_][0].x; raw.r[1] = buf[sl_][0].y;
+      raw.r[2] = buf[sl_][0].z; raw.r[3] = buf[sl_][0].w;
+      if constexpr (DT == 0) {
+        raw.r[4] = buf[sl_][kPieces - 1].x; raw.r[5] = buf[sl_][kPieces - 1].y;
+        raw.r[6] = buf[sl_][kPieces - 1].z; raw.r[7] = buf[sl_][kPieces - 1].w;
+      }
+      uint32_t m8 = bmrow ? (uint32_t)stage_bytes[st * 64] : 0xFFu;
+      if (sl.wb + (st + 1) * kStep > sl.we) {  // a step that ends past the slice
+        const int rem = sl.we - (lane_e + st * kStep);
+        m8 &= rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u);
+      }
+      mb = m8;
+    }
+  };
 
   const double ms = s_n >= 1.0 ? (double)K::value(s_maxk) : 0.0;
   const double tval = truncation_value(s_n, s_sum, s_sq, ms, s_all > 0.0 ? s_n / s_all : 0.0,
@@ -279,159 +426,206 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const float bg_c = (float)(1.4426950408889634 * invT);
 
   // -- the pass ------------------------------------------------------------------
-  uint32_t nlegal = 0u, pcnt = 0u;
-  int32_t nmin = DT == 1 ? 0x7FFF : 0x7FFFFFFF;  // smallest legal signed value
-  uint32_t nmin2 = 0x7FFF7FFFu;                  // bf16: packed per half
-  uint32_t nmax2 = 0u, nmax1 = 0u;               // largest legal raw bits (POS pass)
-  double bg_sum = 0.0;     // sum of exp2((z - bg_ref) c) over legal finite z < t
+  uint32_t anyl = 0u, pcnt = 0u, pmax = 0u, hover = 0u;
+  // Non-finite detectors over legal tokens (illegal tokens never trigger them):
+  // POS pass: the largest raw bits read as unsigned (> the -inf pattern: a
+  // negative NaN; equal: a -inf); NEG pass: the smallest signed value (below
+  // -inf: a negative NaN).
+  uint32_t ext2 = 0u;                        // bf16, packed per half
+  uint32_t ext1 = 0u;                        // fp32
+  double bg_sum = 0.0;     // sum of exp2((z - t) c) over legal finite z < t
   float bg_wx = 0.0f;      // sum of w |x| (error bound)
   float bg_w32 = 0.0f;     // sum of w in fp32 (error bound)
   PKey* const my_pk = pool_key + w * kCap;
   uint16_t* const my_pid = pool_id + w * kCap;
+  // background terms: x = z c - t c, excluded tokens read as a large negative
+  // finite value so that w = 0 and w x = 0
+  const float bg_off = -bg_ref * bg_c;
+  constexpr uint32_t kSent2 = 0xC47AC47Au;   // bf16 pair (-1000, -1000)
+  constexpr uint32_t kSent1 = 0xC47A0000u;   // fp32 -1000
 
-  auto pass = [&](auto bg_on, auto pos_t) {
-    constexpr bool BG = decltype(bg_on)::value;
-    // POS: the threshold is a positive value, so a legal token is a candidate
-    // iff its raw bits, read as a signed integer, are >= those of t (negative
-    // values have the sign bit set); no magnitude transform is needed.
-    constexpr bool POS = decltype(pos_t)::value;
-    auto step = [&](const Raw<DT>& raw, uint32_t mb, int e) {
-      nlegal += (uint32_t)__popc(mb);
-      uint32_t cb;
-      float sw = 0.0f, swx = 0.0f;
-      if constexpr (DT == 1) {
-        const uint4 pm4 = lut[mb];
-        const uint32_t pm[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
-        const uint32_t t2m1 = ((uint32_t)(tS - 1) & 0xFFFFu) * 0x10001u;
-        uint32_t dl[4];
+  // One step: 8 tokens per lane. A legal token is a candidate iff its signed
+  // value (+magnitude / -magnitude of the raw bits, so that -0 == +0) is >= tS;
+  // when t > 0 (POS) that is the raw bits read as a signed integer. Rows with
+  // top-k off also sum exp2((z - t) log2(e) / T) over the legal tokens below t
+  // (fp32 terms, fp64 accumulation per step).
+  auto step = [&](auto pos_c, const Raw<DT>& raw, uint32_t mb, int e) {
+    constexpr bool POS = decltype(pos_c)::value;
+    anyl |= mb;
+    uint32_t cb;
+    if constexpr (DT == 1) {
+      const uint4 pm4 = lut[mb];
+      const uint32_t pm[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
+      const uint32_t t2m1 = ((uint32_t)(tS - 1) & 0xFFFFu) * 0x10001u;
+      uint32_t dl[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t d = raw.r[q];
+        uint32_t rl;
+        if constexpr (POS) {
+          rl = bfi(pm[q], d, 0x80008000u);  // illegal -> the lowest signed value
+          ext2 = bits_of(__builtin_elementwise_max(as_u2(ext2), as_u2(rl)));
+        } else {
+          const uint32_t sg = bits_of(as_s2(d) >> 15);
+          const uint32_t sv = bits_of(as_s2((d & 0x7FFF7FFFu) ^ sg) - as_s2(sg));
+          rl = bfi(pm[q], sv, 0x80808080u);  // illegal -> -inf
+          ext2 = bits_of(__builtin_elementwise_min(as_s2(ext2), as_s2(rl)));
+        }
+        dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(rl)));  // <0 iff cand
+      }
+      // settle the detector here, before the candidate loop below, so that its
+      // operands do not stay live across that loop
+      __asm__ volatile("" : "+v"(ext2));
+      const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
+      const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
+      cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
+                                   __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
+      if (need_bg) {  // legal tokens below t; the others read as the sentinel
+        const uint4 nb4 = lut[mb & ~cb];
+        const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
+        float sw = 0.0f, swx = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t d = raw.r[q];
-          uint32_t rl;
-          if constexpr (POS) {
-            rl = bfi(pm[q], d, 0x80008000u);  // illegal -> 0x8000 (lowest as signed)
-            // a legal negative NaN has raw bits above 0xFF80
-            nmax2 = bits_of(__builtin_elementwise_max(as_u2(nmax2), as_u2(rl)));
-          } else {
-            // signed value of each half: +magnitude or -magnitude
-            const uint32_t mag = d & 0x7FFF7FFFu;
-            const uint32_t sg = bits_of(as_s2(d) >> 15);
-            const uint32_t sv = bits_of(as_s2(mag ^ sg) - as_s2(sg));
-            rl = bfi(pm[q], sv, 0x80008000u);   // illegal -> lowest
-            nmin2 = bits_of(__builtin_elementwise_min(as_s2(nmin2),
-                                                      as_s2(bfi(pm[q], sv, 0x7FFF7FFFu))));
-          }
-          dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(rl)));  // <0 iff cand
-          if constexpr (BG) {
-            const uint32_t cm = bits_of(as_s2(dl[q]) >> 15);        // 0xFFFF per candidate
-            const uint32_t zb = bfi(pm[q] & ~cm, d, 0xFF80FF80u);   // others -> -inf
-            const float zlo = __uint_as_float(zb << 16);
-            const float zhi = __uint_as_float(zb & 0xFFFF0000u);
-            const float xlo = fmaxf((zlo - bg_ref) * bg_c, -200.0f);
-            const float xhi = fmaxf((zhi - bg_ref) * bg_c, -200.0f);
-            const float wlo = __builtin_amdgcn_exp2f(xlo);
-            const float whi = __builtin_amdgcn_exp2f(xhi);
-            sw += wlo + whi;
-            swx = fmaf(wlo, -xlo, fmaf(whi, -xhi, swx));
-          }
+          const uint32_t zb = bfi(nb[q], raw.r[q], kSent2);
+          const float xlo = fmaf(__uint_as_float(zb << 16), bg_c, bg_off);
+          const float xhi = fmaf(__uint_as_float(zb & 0xFFFF0000u), bg_c, bg_off);
+          const float wlo = __builtin_amdgcn_exp2f(xlo);
+          const float whi = __builtin_amdgcn_exp2f(xhi);
+          sw += wlo + whi;
+          swx = fmaf(wlo, -xlo, fmaf(whi, -xhi, swx));
         }
-        const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
-        const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
-        cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
-                                     __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
-      } else {
-        cb = 0u;
-#pragma unroll
-        for (int j = 7; j >= 0; --j) {
-          const uint32_t d = raw.r[j];
-          const uint32_t mj = (uint32_t)__builtin_amdgcn_sbfe((int)mb, j, 1);
-          int32_t rl;
-          if constexpr (POS) {
-            rl = (int32_t)bfi(mj, d, 0x80000000u);  // illegal -> INT_MIN
-            nmax1 = max(nmax1, (uint32_t)rl);       // legal negative NaN > 0xFF800000
-          } else {
-            const uint32_t mag = d & 0x7FFFFFFFu;
-            const uint32_t sv = (d & 0x80000000u) ? 0u - mag : mag;
-            rl = (int32_t)bfi(mj, sv, 0x80000000u);
-            nmin = min(nmin, (int32_t)bfi(mj, sv, 0x7FFFFFFFu));
-          }
-          const bool cand = rl >= tS;
-          cb = cb * 2u + (cand ? 1u : 0u);
-          if constexpr (BG) {
-            const float z = (mj && !cand) ? __uint_as_float(d) : -__builtin_inff();
-            const float x = fmaxf((z - bg_ref) * bg_c, -200.0f);
-            const float wv = __builtin_amdgcn_exp2f(x);
-            sw += wv;
-            swx = fmaf(wv, -x, swx);
-          }
-        }
-      }
-      if constexpr (BG) {
         bg_sum += (double)sw;
         bg_w32 += sw;
         bg_wx += swx;
       }
-      pcnt = append_candidates<DT>(cb, raw, (uint32_t)(e - sl.wb), pcnt, my_pk, my_pid);
-    };
-    for (int s0 = 0; s0 < nst; s0 += D) {
+    } else {
+      const int32_t tm1 = tS - 1;
+      int32_t dl[8];
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
-        const int st = s0 + i;
-        if (st < nst) {
-          Raw<DT> raw;
-          uint32_t mb;
-          rd.fetch(st, i, raw, mb);
-          step(raw, mb, rd.first(st));
-          if (st + D < nst) rd.issue(st + D, i);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t d = raw.r[j];
+        const uint32_t mj = (uint32_t)__builtin_amdgcn_sbfe((int)mb, j, 1);
+        uint32_t rl;
+        if constexpr (POS) {
+          rl = bfi(mj, d, 0x80000000u);
+          ext1 = max(ext1, rl);
+        } else {
+          const uint32_t mag = d & 0x7FFFFFFFu;
+          const uint32_t sv = (d & 0x80000000u) ? 0u - mag : mag;
+          rl = bfi(mj, sv, 0x80800000u);  // illegal -> -inf
+          ext1 = (uint32_t)min((int32_t)ext1, (int32_t)rl);
+        }
+        dl[j] = (int32_t)rl > tm1 ? -1 : 0;
+      }
+      __asm__ volatile("" : "+v"(ext1));
+      cb = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cb |= (dl[j] & 1u) << j;
+      if (need_bg) {
+        const uint32_t nb = mb & ~cb;
+        float sw = 0.0f, swx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t zb = ((nb >> j) & 1u) ? raw.r[j] : kSent1;
+          const float x = fmaf(__uint_as_float(zb), bg_c, bg_off);
+          const float wv = __builtin_amdgcn_exp2f(x);
+          sw += wv;
+          swx = fmaf(wv, -x, swx);
+        }
+        bg_sum += (double)sw;
+        bg_w32 += sw;
+        bg_wx += swx;
+      }
+    }
+    pcnt = append_candidates<DT, DT == 1>(cb, raw, (uint32_t)(e - sl.wb), pcnt, my_pk, my_pid,
+                                           pmax, hist, tkey, (uint32_t)kHistBins, hover);
+  };
+  auto run_pass = [&](auto pos_c) {
+    if constexpr (kResident) {
+      static_for<0, NL>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        Raw<DT> raw;
+        uint32_t mb;
+        res_fetch(stc, raw, mb);
+        res_issue(std::integral_constant<int, st + RD>{});
+        step(pos_c, raw, mb, sl.wb + st * kStep + lane * kChunk);
+      });
+    } else {
+      for (int s0 = 0; s0 < nst; s0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const int st = s0 + i;
+          if (st < nst) {
+            Raw<DT> raw;
+            uint32_t mb;
+            rd.fetch(st, i, raw, mb);
+            step(pos_c, raw, mb, rd.first(st));
+            if (st + D < nst) rd.issue(st + D, i);
+          }
         }
       }
     }
   };
-  const bool pos_t = tS > 0;
-  if (need_bg) {
-    if (pos_t) pass(std::true_type{}, std::true_type{});
-    else pass(std::true_type{}, std::false_type{});
+  const bool pos_pass = tS > 0;
+  if (pos_pass) {
+    ext2 = 0u; ext1 = 0u;
+    run_pass(std::true_type{});
   } else {
-    if (pos_t) pass(std::false_type{}, std::true_type{});
-    else pass(std::false_type{}, std::false_type{});
+    ext2 = 0x7FFF7FFFu; ext1 = 0x7FFFFFFFu;
+    run_pass(std::false_type{});
   }
-  // smallest legal signed value (a negative NaN lies below -inf)
-  if constexpr (DT == 1) {
-    const s16x2 v = as_s2(nmin2);
-    nmin = min((int32_t)v.x, (int32_t)v.y);
-    const uint32_t hmax = max(nmax2 & 0xFFFFu, nmax2 >> 16);
-    if (hmax > 0xFF80u) nmin = -0x7FFF;  // raw bits of a negative NaN
+  // legal negative NaN / legal -inf, from the detectors above
+  uint32_t nan_l = 0u, ninf_l = 0u;
+  if (pos_pass) {
+    const uint32_t hmax = DT == 1 ? max(ext2 & 0xFFFFu, ext2 >> 16) : ext1;
+    const uint32_t ninf_raw = DT == 1 ? 0xFF80u : 0xFF800000u;
+    nan_l = hmax > ninf_raw ? 1u : 0u;
+    ninf_l = hmax == ninf_raw ? 1u : 0u;
   } else {
-    if (nmax1 > 0xFF800000u) nmin = min(nmin, -0x7FFFFFFF);  // raw bits of a negative NaN
+    int32_t lo;
+    if constexpr (DT == 1) {
+      const s16x2 v = as_s2(ext2);
+      lo = min((int32_t)v.x, (int32_t)v.y);
+    } else {
+      lo = (int32_t)ext1;
+    }
+    const int32_t ninf_s = DT == 1 ? -0x7F80 : -0x7F800000;
+    nan_l = lo < ninf_s ? 1u : 0u;
+    ninf_l = 1u;  // a legal -inf cannot be told from an illegal token here
   }
 
   // -- reduce the pass -------------------------------------------------------------
-  nlegal = wave_reduce<OpSum>(nlegal);
-  const uint32_t nmin_u = wave_reduce<OpMin>((uint32_t)nmin ^ 0x80000000u);  // signed order
+  anyl = wave_reduce<OpMax>(anyl);
+  nan_l = wave_reduce<OpMax>(nan_l);
+  ninf_l = wave_reduce<OpMax>(ninf_l);
+  pmax = wave_reduce<OpMax>(pmax);
+  hover = wave_reduce<OpMax>(hover);
   bg_sum = wave_sum_f64(bg_sum);
   const double bg_wx64 = wave_sum_f64((double)bg_wx);
   const double bg_w64 = wave_sum_f64((double)bg_w32);
   if (lane == 0) {
-    red.v[par][w][0] = nlegal;
-    red.v[par][w][1] = nmin_u;
+    red.v[par][w][0] = anyl;
+    red.v[par][w][1] = nan_l | (ninf_l << 1);
     info.cnt[w] = pcnt;
     const uint64_t b0 = __double_as_longlong(bg_sum), b1 = __double_as_longlong(bg_wx64);
     const uint64_t b2 = __double_as_longlong(bg_w64);
     red.v[par][w][2] = (uint32_t)b0; red.v[par][w][3] = (uint32_t)(b0 >> 32);
     red.v[par][w][4] = (uint32_t)b1; red.v[par][w][5] = (uint32_t)(b1 >> 32);
     red.v[par][w][6] = (uint32_t)b2; red.v[par][w][7] = (uint32_t)(b2 >> 32);
+    red.v[par][w][8] = pmax;
+    red.v[par][w][9] = hover;
   }
-  __syncthreads();
-  uint32_t ccount = 0u, my_wcnt = 0u;
-  bool overflow = false, neg_nan = false;
+  __syncthreads();  // pools, histogram and per-wave results complete
+  uint32_t ccount = 0u, my_wcnt = 0u, pool_max = 0u;
+  bool overflow = false, neg_nan = false, has_neginf = false, hist_over = false;
+  bool any_legal = false;
   double bg_err = 0.0;
   {
-    uint32_t nl = 0u, mn = 0xFFFFFFFFu;
+    uint32_t al = 0u, fl = 0u, pm = 0u, ho = 0u;
     double b0 = 0.0, b1 = 0.0, b2 = 0.0;
     for (int ww = 0; ww < kWaves; ++ww) {
-      nl += red.v[par][ww][0];
-      const uint32_t y = red.v[par][ww][1];
-      mn = y < mn ? y : mn;
+      al |= red.v[par][ww][0];
+      fl |= red.v[par][ww][1];
       const uint32_t c = info.cnt[ww];
       if (ww == w) my_wcnt = c;
       ccount += c;
@@ -439,15 +633,18 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       b0 += __longlong_as_double(((uint64_t)red.v[par][ww][3] << 32) | red.v[par][ww][2]);
       b1 += __longlong_as_double(((uint64_t)red.v[par][ww][5] << 32) | red.v[par][ww][4]);
       b2 += __longlong_as_double(((uint64_t)red.v[par][ww][7] << 32) | red.v[par][ww][6]);
+      pm = max(pm, red.v[par][ww][8]);
+      ho |= red.v[par][ww][9];
     }
-    nlegal = uni(nl);
-    const int32_t lowest = (int32_t)(mn ^ 0x80000000u);
-    const int32_t neg_inf_s = DT == 1 ? -0x7F80 : -0x7F800000;
-    neg_nan = uni(lowest < neg_inf_s);
+    any_legal = uni(al != 0u);
+    neg_nan = uni((fl & 1u) != 0u);
+    has_neginf = uni((fl & 2u) != 0u);
     bg_sum = uni(b0);
-    // per term: exp2 error plus the argument's three roundings (ln2 * 3 * 2^-24 |x|),
+    // per term: exp2 error plus the argument's roundings (ln2 * 2 * 2^-24 |x|),
     // plus the fp32 accumulation of 8 terms per step
     bg_err = uni(kExp2Err * b2 + 1.24e-7 * b1 + 4.2e-7 * b2 + 1e-30);
+    pool_max = uni(pm);
+    hist_over = uni(ho != 0u);
   }
   ccount = uni(ccount);
   my_wcnt = uni(my_wcnt);
@@ -460,67 +657,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // pool usable: complete, 16-bit ids fit, not forced off
   const bool pool_ok = !overflow && ccount > 0u && !(a.flags & QS_FLAG_FORCE_MISS) &&
                        !no_trunc && a.seg <= 65536;
+  // the pool holds every finite legal token (the threshold was -inf)
+  const bool pool_all = pool_ok && t_all;
 
-  // -- row statistics: max, argmax, non-finite, -inf count ----------------------
-  // From the pool when it holds the maximum (t never exceeds the sample max),
-  // otherwise from a walk over the row.
-  uint32_t maxk = 0u, max_id = 0xFFFFFFFFu, nfin = nlegal;
-  bool nonfinite = neg_nan;
-  {
-    uint32_t mk = 0u, mid = 0xFFFFFFFFu, mn = 0xFFFFFFFFu, ninf = 0u;
-    auto track = [&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t lm) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((lm >> j) & 1u) {
-          if (key[j] > mk) { mk = key[j]; mid = id[j]; }  // ids ascend along a lane
-          mn = key[j] < mn ? key[j] : mn;
-          ninf += key[j] == K::kNegInf ? 1u : 0u;
-        }
-      }
-    };
-    if (pool_ok) walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane, track);
-    else walk_row<DT, true>(sl, lane, track);
-    const uint32_t wmax = wave_reduce<OpMax>(mk);
-    const uint32_t cid = wave_reduce<OpMin>(mk == wmax ? mid : 0xFFFFFFFFu);
-    mn = wave_reduce<OpMin>(mn);
-    ninf = wave_reduce<OpSum>(ninf);
-    if (lane == 0) {
-      red.v[par][w][0] = wmax; red.v[par][w][1] = cid;
-      red.v[par][w][2] = mn; red.v[par][w][3] = ninf;
-    }
-    __syncthreads();
-    uint32_t gm = 0u, gid = 0xFFFFFFFFu, gmn = 0xFFFFFFFFu, gninf = 0u;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const uint32_t x = red.v[par][ww][0], c = red.v[par][ww][1];
-      if (x > gm || (x == gm && c < gid)) { gm = x; gid = c; }
-      const uint32_t y = red.v[par][ww][2];
-      gmn = y < gmn ? y : gmn;
-      gninf += red.v[par][ww][3];
-    }
-    par ^= 1;
-    maxk = uni(gm);
-    max_id = uni(gid);
-    if (!pool_ok) {
-      nfin = uni(nlegal - gninf);
-      nonfinite = nonfinite || uni(gmn < K::kNegInf);
-    }
-    nonfinite = nonfinite || maxk >= K::kPosInf;
-  }
-
-  // -- row status --------------------------------------------------------------
-  if (nlegal == 0u) { finish_error(QS_ROW_EMPTY); return; }
-  if (nonfinite) { finish_error(QS_ROW_NONFINITE); return; }
-  if (maxk <= K::kNegInf) { finish_error(QS_ROW_ALL_NEG_INF); return; }
-
-  const double m = (double)K::value(maxk);
-  // with a usable pool, |F| >= |Z_t|, so k < |Z_t| already settles k < |F|;
-  // otherwise the row walk above counted |F| exactly
-  const bool topk_on = !greedy && kk > 0 &&
-                       (pool_ok ? (uint32_t)kk < ccount : (uint32_t)kk < nfin);
-
-  // -- source selection (hit test) -------------------------------------------
-  bool use_pool = pool_ok;
-  double w_f = -1.0, w_f_err = 0.0, w_pool = 0.0;
   auto block_sum_f64 = [&](double v) -> double {
     v = wave_sum_f64(v);
     if (lane == 0) {
@@ -535,76 +674,140 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     par ^= 1;
     return uni(t);
   };
-  if (use_pool) {
-    if (greedy) {
-      use_pool = true;
-    } else if (topk_on) {
-      use_pool = true;  // kk < |Z_t|
-    } else if (topp_on && need_bg) {
-      double s = 0.0;
+  auto block_sum_u32 = [&](uint32_t v) -> uint32_t {
+    v = wave_reduce<OpSum>(v);
+    if (lane == 0) red.v[par][w][0] = v;
+    __syncthreads();
+    uint32_t t = 0u;
+    for (int ww = 0; ww < kWaves; ++ww) t += red.v[par][ww][0];
+    par ^= 1;
+    return uni(t);
+  };
+
+  // -- row maximum, non-finite values, |F| ----------------------------------------
+  // With a usable pool the maximum is in it (t never exceeds the sample
+  // maximum) and +inf / positive NaNs at legal positions are candidates;
+  // otherwise one walk over the row.
+  uint32_t maxk = 0u, nfin = 0u;
+  bool nonfinite = neg_nan;
+  // |F| is known on the row path and when the pool holds all of F
+  bool nf_known = true;
+  if (pool_ok) {
+    maxk = pool_max;
+    if (pool_all) nfin = ccount;
+    else nf_known = false;  // counted on the row path if needed
+  } else {
+    uint32_t mk = 0u, mn = 0xFFFFFFFFu, nf = 0u;
+    walk_row<DT, true>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
+                                     uint32_t lm) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((lm >> j) & 1u) {
+          mk = key[j] > mk ? key[j] : mk;
+          mn = key[j] < mn ? key[j] : mn;
+          nf += key[j] > K::kNegInf ? 1u : 0u;
+        }
+      }
+    });
+    mk = wave_reduce<OpMax>(mk);
+    mn = wave_reduce<OpMin>(mn);
+    nf = wave_reduce<OpSum>(nf);
+    if (lane == 0) {
+      red.v[par][w][0] = mk; red.v[par][w][1] = mn; red.v[par][w][2] = nf;
+    }
+    __syncthreads();
+    uint32_t gm = 0u, gmn = 0xFFFFFFFFu, gnf = 0u;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      gm = max(gm, red.v[par][ww][0]);
+      gmn = min(gmn, red.v[par][ww][1]);
+      gnf += red.v[par][ww][2];
+    }
+    par ^= 1;
+    maxk = uni(gm);
+    nfin = uni(gnf);
+    nonfinite = nonfinite || uni(gmn < K::kNegInf);
+  }
+  nonfinite = nonfinite || maxk >= K::kPosInf;
+
+  // -- row status --------------------------------------------------------------
+  if (!any_legal) { finish_error(QS_ROW_EMPTY); return; }
+  if (nonfinite) { finish_error(QS_ROW_NONFINITE); return; }
+  if (maxk <= K::kNegInf) { finish_error(QS_ROW_ALL_NEG_INF); return; }
+
+  const double m = (double)K::value(maxk);
+
+  // -- source selection (hit test) -------------------------------------------
+  // top-k hit: k < |Z_t| <= |F|. Top-p only: the pool must hold a mass of at
+  // least p * W_F, with the background mass below t only known within +-err.
+  bool use_pool = pool_ok;
+  bool mass_test = false;
+  if (use_pool && !greedy) {
+    if (kk > 0 && (uint32_t)kk < ccount) {
+      // top-k hit
+    } else if (pool_all) {
+      // the pool is all of F
+    } else if (need_bg) {
+      mass_test = true;
+    } else {
+      use_pool = false;  // k >= |Z_t| with |F| unknown, or everything kept
+    }
+  }
+  // bf16 pools: fp64 weight of every histogram key (one key per thread)
+  const bool hist_t = DT == 1 && use_pool && !greedy && !hist_over;
+  const int hb = kHistBins - 1 - tid;  // this thread's key (thread 0 holds the top key)
+  uint32_t h_own = 0u;
+  double w_own = 0.0;
+  if constexpr (DT == 1) {
+    if (hist_t) {
+      h_own = hist[hb];
+      const uint32_t key = tkey + (uint32_t)hb;
+      if (h_own && key <= maxk) w_own = weight<DT>(key, m, invT);
+      binw[hb] = w_own;
+    }
+  }
+  if (hist_t) __syncthreads();  // the weight table is read by every wave below
+  double w_f = -1.0, w_f_err = 0.0;
+  if (mass_test) {
+    double s = 0.0;
+    if (hist_t) {
+      s = (double)h_own * w_own;
+    } else {
       walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
                     [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if ((vm >> j) & 1u) s += weight<DT>(key[j], m, invT);
       });
-      w_pool = block_sum_f64(s);
-      const double scale = exp64(((double)bg_ref - m) * invT);
-      w_f = w_pool + bg_sum * scale;
-      w_f_err = bg_err * scale;
-      use_pool = w_pool >= p * (w_f + w_f_err) * (1.0 + 1e-9);
-    } else if (topp_on) {
-      use_pool = false;  // k >= |Z_t| but the mass below t is unknown
-    } else {
-      // everything is kept: the pool must hold all of F, and |F| is unknown
-      use_pool = false;
+    }
+    const double w_pool = block_sum_f64(s);
+    const double scale = exp64(((double)bg_ref - m) * invT);
+    w_f = w_pool + bg_sum * scale;
+    w_f_err = bg_err * scale;
+    use_pool = w_pool >= p * (w_f + w_f_err) * (1.0 + 1e-9);
+  }
+  if (!use_pool) {
+    w_f = -1.0;
+    w_f_err = 0.0;
+    if (!nf_known) {  // count the finite legal tokens of the row
+      uint32_t nf = 0u;
+      walk_row<DT, true>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
+                                       uint32_t lm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          nf += (((lm >> j) & 1u) && key[j] > K::kNegInf) ? 1u : 0u;
+      });
+      nfin = block_sum_u32(nf);
     }
   }
-  if (!use_pool) w_f_err = 0.0;
-  uint32_t nf_exact = nfin;
-  if (!use_pool && pool_ok) {
-    // the row walk above ran on the pool: count |F| on the row now
-    uint32_t ninf = 0u;
-    walk_row<DT, true>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
-                                     uint32_t lm) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ninf += (((lm >> j) & 1u) && key[j] == K::kNegInf) ? 1u : 0u;
-    });
-    ninf = wave_reduce<OpSum>(ninf);
-    if (lane == 0) red.v[par][w][0] = ninf;
-    __syncthreads();
-    uint32_t t = 0u;
-    for (int ww = 0; ww < kWaves; ++ww) t += red.v[par][ww][0];
-    par ^= 1;
-    nf_exact = uni(nlegal - t);
-  }
-  const bool topk_eff = !greedy && kk > 0 && (uint32_t)kk < nf_exact;
+  const bool topk_eff = !greedy && kk > 0 && (uint32_t)kk < (use_pool ? ccount : nfin);
+  const bool use_hist = hist_t && use_pool;
+  const bool scan_mode = use_hist && !(a.flags & QS_FLAG_PIVOT_SEARCH);
   const uint32_t src_lo = use_pool ? tkey : K::kNegInf + 1u;  // every source key >= src_lo
 
-  // -- per-key histogram of a bf16 pool ------------------------------------------
-  const bool use_hist = DT == 1 && use_pool && !greedy && (maxk - src_lo) < (uint32_t)kHistBins;
-  if constexpr (DT == 1) {
-    if (use_hist) {
-    for (int b = tid; b < kHistBins; b += kThreads) hist[b] = 0u;
-    __syncthreads();
-    walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
-                  [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if ((vm >> j) & 1u) atomicAdd(&hist[key[j] - src_lo], 1u);
-    });
-    __syncthreads();
-    }
-  }
-  const uint32_t nbins = use_hist ? maxk - src_lo + 1u : 0u;
-
-  // items of the searches: (key, multiplicity) from the histogram, else tokens
+  // items of the pivot searches: (key, multiplicity) from the histogram, else tokens
   auto for_items = [&](auto&& f) {
     if (DT == 1 && use_hist) {
-      for (uint32_t b = (uint32_t)tid; b < nbins; b += kThreads) {
-        const uint32_t c = hist[DT == 1 ? b : 0u];
-        if (c) f(src_lo + b, c);
-      }
+      if (h_own) f(tkey + (uint32_t)hb, h_own);
     } else {
       auto g = [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
 #pragma unroll
@@ -615,18 +818,23 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       else walk_row<DT, false>(sl, lane, g);
     }
   };
-
   // walk the chosen token source (pool or row), in id order per wave
   auto walk = [&](auto&& f) {
     if (use_pool) walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane, f);
     else walk_row<DT, false>(sl, lane, f);
   };
-
+  // fp64 weight of a source key (histogram keys from the table)
+  auto wkey = [&](uint32_t key) -> double {
+    if constexpr (DT == 1) {
+      if (use_hist) return binw[key - tkey];
+    }
+    return weight<DT>(key, m, invT);
+  };
   // mass of source items with key > lo_excl
   auto mass_above = [&](uint32_t lo_excl) -> double {
     double s = 0.0;
     for_items([&](uint32_t key, uint32_t c) {
-      if (key > lo_excl) s += (double)c * weight<DT>(key, m, invT);
+      if (key > lo_excl) s += (double)c * wkey(key);
     });
     return block_sum_f64(s);
   };
@@ -634,9 +842,29 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   int rounds = 0;
   bool failed = false;
 
-  // -- quaternary three-pivot search on counts (top-k) ---------------------------
+  // -- the k-th largest key (top-k) ----------------------------------------------
   uint32_t kap = 0u, n_keep_k = 0u;
-  if (topk_eff) {
+  if (topk_eff && scan_mode) {
+    // suffix counts S(b) = #pool tokens with key >= tkey + b; the boundary key
+    // is the one with S(b) >= k > S(b) - h(b)
+    const uint32_t incl = wave_incl_u32(h_own, lane);
+    if (lane == 63) red.v[par][w][0] = incl;
+    __syncthreads();
+    uint32_t wex = 0u;
+    for (int ww = 0; ww < w; ++ww) wex += red.v[par][ww][0];
+    const uint32_t S = wex + incl;
+    const uint32_t kq = (uint32_t)kk;
+    if (S >= kq && S - h_own < kq) {
+      info.sel_u[0] = (uint32_t)hb;
+      info.sel_u[1] = S - h_own;
+    }
+    __syncthreads();
+    kap = uni(tkey + info.sel_u[0]);
+    n_keep_k = uni(kq - info.sel_u[1]);
+    par ^= 1;
+    rounds = 1;
+  } else if (topk_eff) {
+    // quaternary three-pivot search on counts (page "Qrita", key design 2)
     uint32_t lo = src_lo - 1u, hi = maxk;
     bool found = false;
     while (!found) {
@@ -710,19 +938,90 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   //    ids of key == pstar --------------------------------------------------
   uint32_t pstar = K::kNegInf;  // keep-all: every source key is above it
   uint32_t n_keep = 0u;
-  double w_p = 0.0, w_star = 0.0;
+  double w_star = 0.0;
   if (greedy) {
     pstar = maxk;
     n_keep = 1u;
     w_star = 1.0;
-    w_p = 1.0;
   } else if (!failed) {
-    const double w_kap = topk_eff ? weight<DT>(kap, m, invT) : 0.0;
-    double w_k;
-    if (topk_eff) w_k = mass_above(kap) + (double)n_keep_k * w_kap;
-    else if (w_f >= 0.0 && use_pool) w_k = w_f;
-    else w_k = mass_above(0u);
-    if (topp_on) {
+    const double w_kap = topk_eff ? wkey(kap) : 0.0;
+    if (topp_on && scan_mode) {
+      // suffix masses over the histogram keys inside the top-k set; the
+      // boundary key is the largest b whose inclusive suffix mass reaches p * W
+      const uint32_t kapb = topk_eff ? kap - tkey : 0u;
+      const uint32_t hp = !topk_eff ? h_own
+                                    : ((uint32_t)hb > kapb ? h_own
+                                                           : ((uint32_t)hb == kapb ? n_keep_k : 0u));
+      const double M = (double)hp * w_own;
+      double ex_l;
+      const double in_l = wave_incl_f64(M, lane, ex_l);
+      if (lane == 63) {
+        const uint64_t b = __double_as_longlong(in_l);
+        red.v[par][w][0] = (uint32_t)b;
+        red.v[par][w][1] = (uint32_t)(b >> 32);
+      }
+      __syncthreads();
+      double wex = 0.0, total = 0.0;  // totals of the waves below, added in wave order
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const double t = __longlong_as_double(((uint64_t)red.v[par][ww][1] << 32) |
+                                              red.v[par][ww][0]);
+        if (ww == w) wex = total;
+        total += t;
+      }
+      total = uni(total);
+      par ^= 1;
+      const double incl = wex + in_l;
+      const double excl = lane > 0 ? wex + ex_l : wex;
+      double w_ref = topk_eff ? total : (w_f >= 0.0 ? w_f : total);
+      double err = topk_eff ? 0.0 : w_f_err;
+      for (int attempt = 0; attempt < 2; ++attempt) {
+        const double target = p * w_ref;
+        if (incl >= target) atomicMax(&info.bsel, hb);
+        __syncthreads();
+        const int bs = info.bsel;
+        if (hb == bs) {
+          info.sel_d[0] = excl;
+          info.sel_d[1] = w_own;
+          info.sel_u[0] = hp;
+        }
+        __syncthreads();
+        const double below = uni(info.sel_d[0]);
+        const double wz = uni(info.sel_d[1]);
+        const uint32_t c = uni(info.sel_u[0]);
+        ++rounds;
+        if (bs < 0 || c == 0u || !(wz > 0.0)) { failed = true; break; }
+        pstar = tkey + (uint32_t)bs;
+        w_star = wz;
+        // smallest count of boundary tokens that reaches the target
+        const double need = (target - below) / wz;
+        uint32_t nk = need <= 1.0 ? 1u : (need >= (double)c ? c : (uint32_t)ceil(need));
+        while (nk > 1u && below + (double)(nk - 1u) * wz >= target) --nk;
+        while (nk < c && below + (double)nk * wz < target) ++nk;
+        n_keep = nk;
+        const double w_p = below + (double)nk * wz;
+        // the same cut for every reference mass in [w_ref - err, w_ref + err]?
+        const double lo_t = p * (w_ref - err), hi_t = p * (w_ref + err);
+        const double prev = below + (double)(nk - 1u) * wz;
+        const bool refine = err > 0.0 && !(prev < lo_t && hi_t <= w_p);
+        if (!refine) break;
+        // exact background mass: fp64 over every finite legal token below t
+        double s = 0.0;
+        walk_row<DT, false>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
+                                          uint32_t vm) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (((vm >> j) & 1u) && key[j] < tkey) s += weight<DT>(key[j], m, invT);
+        });
+        w_ref = total + block_sum_f64(s);
+        err = 0.0;
+        if (tid == 0) info.bsel = -1;
+        __syncthreads();
+      }
+    } else if (topp_on) {
+      double w_k;
+      if (topk_eff) w_k = mass_above(kap) + (double)n_keep_k * w_kap;
+      else if (w_f >= 0.0) w_k = w_f;
+      else w_k = mass_above(0u);
       // Quaternary three-pivot search on fp64 mass inside K. When the top-p
       // reference mass is only known within +-err (the background summed with
       // fp32 exp2), the cut must be the same at both ends of that interval;
@@ -741,15 +1040,15 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           for (int n = 0; n < 3; ++n)
             tau[n] = d >= 4u ? lo + (uint32_t)(((uint64_t)d * (uint64_t)(n + 1)) >> 2)
                              : min(lo + (uint32_t)n, hi - 1u);
-          double M[3] = {0.0, 0.0, 0.0};
+          double Ms[3] = {0.0, 0.0, 0.0};
           MinCnt mc[3] = {{0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}};
           for_items([&](uint32_t x, uint32_t c) {
             if (x > excl && x > tau[0]) {
-              const double wt = (double)c * weight<DT>(x, m, invT);
+              const double wt = (double)c * wkey(x);
 #pragma unroll
               for (int n = 0; n < 3; ++n) {
                 if (x > tau[n]) {
-                  M[n] += wt;
+                  Ms[n] += wt;
                   if (x < mc[n].key) { mc[n].key = x; mc[n].cnt = c; }
                   else if (x == mc[n].key) { mc[n].cnt += c; }
                 }
@@ -758,13 +1057,13 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           });
 #pragma unroll
           for (int n = 0; n < 3; ++n) {
-            M[n] = wave_sum_f64(M[n]);
+            Ms[n] = wave_sum_f64(Ms[n]);
             mc[n] = wave_reduce_mc(mc[n]);
           }
           if (lane == 0) {
 #pragma unroll
             for (int n = 0; n < 3; ++n) {
-              uint64_t b = __double_as_longlong(M[n]);
+              uint64_t b = __double_as_longlong(Ms[n]);
               red.v[par][w][4 * n] = (uint32_t)b;
               red.v[par][w][4 * n + 1] = (uint32_t)(b >> 32);
               red.v[par][w][4 * n + 2] = mc[n].key;
@@ -774,19 +1073,19 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           __syncthreads();
 #pragma unroll
           for (int n = 0; n < 3; ++n) {
-            M[n] = 0.0;
+            Ms[n] = 0.0;
             mc[n] = MinCnt{0xFFFFFFFFu, 0u};
             for (int ww = 0; ww < kWaves; ++ww) {
-              M[n] += __longlong_as_double(((uint64_t)red.v[par][ww][4 * n + 1] << 32) |
-                                           red.v[par][ww][4 * n]);
+              Ms[n] += __longlong_as_double(((uint64_t)red.v[par][ww][4 * n + 1] << 32) |
+                                            red.v[par][ww][4 * n]);
               mc[n] = mc_merge(mc[n], MinCnt{red.v[par][ww][4 * n + 2], red.v[par][ww][4 * n + 3]});
             }
             // the boundary bucket of the top-k set holds only n_keep_k tokens
             if (topk_eff && kap > tau[n]) {
-              M[n] += (double)n_keep_k * w_kap;
+              Ms[n] += (double)n_keep_k * w_kap;
               if (kap < mc[n].key) mc[n] = MinCnt{kap, n_keep_k};
             }
-            M[n] = uni(M[n]);
+            Ms[n] = uni(Ms[n]);
             mc[n].key = uni(mc[n].key);
             mc[n].cnt = uni(mc[n].cnt);
           }
@@ -794,9 +1093,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           ++rounds;
 #pragma unroll
           for (int n = 0; n < 3; ++n) {
-            if (!found && M[n] >= target) {
-              const double wz = weight<DT>(mc[n].key, m, invT);
-              const double below = M[n] - (double)mc[n].cnt * wz;
+            if (!found && Ms[n] >= target) {
+              const double wz = wkey(mc[n].key);
+              const double below = Ms[n] - (double)mc[n].cnt * wz;
               if (below < target) {
                 found = true;
                 pstar = mc[n].key;
@@ -808,7 +1107,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
                 while (nk > 1u && below + (double)(nk - 1u) * wz >= target) --nk;
                 while (nk < c && below + (double)nk * wz < target) ++nk;
                 n_keep = nk;
-                w_p = below + (double)nk * wz;
+                const double w_p = below + (double)nk * wz;
                 // the same cut for every reference mass in [w_k - err, w_k + err]?
                 const double lo_t = p * (w_k - err), hi_t = p * (w_k + err);
                 const double prev = below + (double)(nk - 1u) * wz;
@@ -819,7 +1118,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           if (!found) {
 #pragma unroll
             for (int n = 0; n < 3; ++n) {
-              if (M[n] >= target) lo = tau[n] > lo ? tau[n] : lo;
+              if (Ms[n] >= target) lo = tau[n] > lo ? tau[n] : lo;
               else hi = tau[n] < hi ? tau[n] : hi;
             }
           }
@@ -833,18 +1132,16 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           for (int j = 0; j < 8; ++j)
             if (((vm >> j) & 1u) && key[j] < tkey) s += weight<DT>(key[j], m, invT);
         });
-        w_k = w_pool + block_sum_f64(s);
+        w_k = mass_above(tkey - 1u) + block_sum_f64(s);
         err = 0.0;
       }
     } else if (topk_eff) {
       pstar = kap;
       n_keep = n_keep_k;
       w_star = w_kap;
-      w_p = w_k;
     } else {
       pstar = K::kNegInf;
       n_keep = 0u;
-      w_p = w_k;
     }
   }
   if (failed) {
@@ -853,86 +1150,43 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
   if (pstar == K::kNegInf) n_keep = 0u;
 
-  // -- walk A: per-wave counts of key > pstar and key == pstar, and q mass ------
-  const double inv_wp = 1.0 / w_p;
+  // -- walk A: per-wave counts of key > pstar and key == pstar, and their mass ----
   {
     uint32_t gt = 0u, ties = 0u;
-    double qgt = 0.0;
-    walk([&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
+    double mgt = 0.0;
+    if (!greedy) {
+      walk([&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((vm >> j) & 1u) {
-          if (key[j] > pstar) {
-            ++gt;
-            qgt += weight<DT>(key[j], m, invT) * inv_wp;
-          } else if (key[j] == pstar) {
-            ++ties;
+        for (int j = 0; j < 8; ++j) {
+          if ((vm >> j) & 1u) {
+            if (key[j] > pstar) {
+              ++gt;
+              mgt += wkey(key[j]);
+            } else if (key[j] == pstar) {
+              ++ties;
+            }
           }
         }
-      }
-    });
+      });
+    } else {
+      walk([&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ties += (((vm >> j) & 1u) && key[j] == pstar) ? 1u : 0u;
+      });
+    }
     gt = wave_reduce<OpSum>(gt);
     ties = wave_reduce<OpSum>(ties);
-    qgt = wave_sum_f64(qgt);
+    mgt = wave_sum_f64(mgt);
     if (lane == 0) {
       info.gt[w] = gt;
       info.ties[w] = ties;
-      info.q[w] = qgt;
+      info.mass[w] = mgt;
     }
   }
   __syncthreads();
-  uint32_t total_ties = 0u;
-  for (int ww = 0; ww < kWaves; ++ww) total_ties += info.ties[ww];
-  total_ties = uni(total_ties);
 
-  // -- walk B: id of the n_keep-th boundary token (earliest ids are kept) -------
-  uint32_t id_cut = 0xFFFFFFFFu;
-  if (greedy) {
-    id_cut = max_id;
-  } else if (n_keep < total_ties) {
-    uint32_t before = 0u;
-    int tw = 0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const uint32_t t = info.ties[ww];
-      if (before + t >= n_keep) { tw = ww; break; }
-      before += t;
-    }
-    const uint32_t want = n_keep - before;  // 1-based rank inside wave tw
-    if (w == tw) {
-      uint32_t seen = 0u;
-      bool done = false;
-      walk([&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t vm) {
-        if (done) return;
-        uint32_t tb = 0u;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          tb |= ((((vm >> j) & 1u) && key[j] == pstar) ? 1u : 0u) << j;
-        uint32_t total;
-        const uint32_t excl = wave_excl_small((uint32_t)__popc(tb), total);
-        if (seen + total >= want) {
-          const uint32_t lo_r = seen + excl, hi_r = seen + excl + (uint32_t)__popc(tb);
-          if (lo_r < want && want <= hi_r) {
-            const uint32_t need = want - lo_r;  // 1-based inside this lane
-            uint32_t c = 0u;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              if ((tb >> j) & 1u) {
-                ++c;
-                if (c == need) red.v[par][0][39] = id[j];
-              }
-            }
-          }
-          done = true;
-        }
-        seen += total;
-      });
-    }
-    __syncthreads();
-    id_cut = uni(red.v[par][0][39]);
-    par ^= 1;
-  }
-
-  // sampling uniform
+  // per-wave share of the tie quota (earliest ids first), list offsets, masses,
+  // W_P and the wave whose cumulative mass holds u
   double u = 0.0;
   const bool sampled = SAMPLE && !greedy;
   if (sampled) {
@@ -940,61 +1194,117 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     else u = (double)philox_u24(a.seed[r], a.offset[r]) * (1.0 / 16777216.0);
   }
   u = uni(u);
-
-  // per-wave kept counts -> list offsets, cumulative q, and the wave holding u
-  const double q_star = w_star * inv_wp;
-  uint32_t my_off = 0u, n_p = 0u;
-  double my_cum = 0.0;
-  int sw = -1;
+  // lane i of every wave handles wave i: exclusive prefixes of ties (the
+  // quota goes to the earliest ids, i.e. the lowest waves), kept counts and
+  // masses; the sampled wave is the first whose cumulative probability passes u
+  uint32_t my_off, n_p, my_kt;
+  double w_p, my_cumw;
+  int sw, last_w;
   {
-    uint32_t tb = 0u;
-    double cum = 0.0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const uint32_t t = info.ties[ww];
-      const uint32_t avail = n_keep > tb ? n_keep - tb : 0u;
-      const uint32_t kt = t < avail ? t : avail;
-      tb += t;
-      const uint32_t kept = info.gt[ww] + kt;
-      const double qw = info.q[ww] + (double)kt * q_star;
-      if (ww == w) { my_off = n_p; my_cum = cum; }
-      if (sampled && sw < 0 && kept > 0u && u < cum + qw) sw = ww;
-      n_p += kept;
-      cum += qw;
+    const bool act = lane < kWaves;
+    const uint32_t t = act ? info.ties[lane] : 0u;
+    const uint32_t g = act ? info.gt[lane] : 0u;
+    const double mg = act ? info.mass[lane] : 0.0;
+    const uint32_t tb = wave_incl_u32(t, lane) - t;
+    const uint32_t avail = n_keep > tb ? n_keep - tb : 0u;
+    const uint32_t kt = t < avail ? t : avail;
+    const uint32_t kept = g + kt;
+    const double mw = mg + (double)kt * w_star;
+    const uint32_t kincl = wave_incl_u32(kept, lane);
+    double mex;
+    const double mincl = wave_incl_f64(mw, lane, mex);
+    const int wu = uni(w);
+    my_off = readlane_u32(kincl - kept, wu);
+    my_kt = readlane_u32(kt, wu);
+    my_cumw = readlane_f64(mex, wu);
+    n_p = readlane_u32(kincl, kWaves - 1);
+    w_p = readlane_f64(mincl, kWaves - 1);
+    const uint64_t pos = ballot(act && kept > 0u && mw > 0.0);
+    last_w = pos ? 63 - __clzll((long long)pos) : -1;
+    sw = -1;
+    if (sampled) {
+      const uint64_t hit = ballot(act && kept > 0u && u < mincl * (1.0 / w_p));
+      sw = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
     }
   }
   my_off = uni(my_off);
   n_p = uni(n_p);
-  my_cum = uni(my_cum);
+  my_kt = uni(my_kt);
+  w_p = uni(w_p);
+  my_cumw = uni(my_cumw);
   sw = uni(sw);
+  last_w = uni(last_w);
+  if (greedy) {
+    w_p = 1.0;
+    my_cumw = 0.0;
+  }
+  const double inv_wp = 1.0 / w_p;
 
   // -- walk D: outputs ------------------------------------------------------------
-  zero_outputs();
   int32_t* ids_row = a.cand_ids ? a.cand_ids + (size_t)r * a.cand_cap : nullptr;
   float* probs_row = a.cand_probs ? a.cand_probs + (size_t)r * a.cand_cap : nullptr;
   const uint32_t cap = (uint32_t)a.cand_cap;
+  // this slice's mask words (none for an empty slice at the row end, whose
+  // start word belongs to the wave before it)
+  const int sw0 = sl.wb >> 5, sw1 = sl.we > sl.wb ? (sl.we + 31) >> 5 : sw0;
+  uint32_t* const my_stage = stage[w];
+  if (mask_row && stage_ok) {
+    for (int i = lane; i < sw1 - sw0; i += 64) my_stage[i] = 0u;
+  }
+  if (dense_row || (mask_row && !stage_ok)) {
+    // zero in memory first (the scatter below lands after these stores)
+    if (mask_row && !stage_ok && sl.we > sl.wb)
+      for (int i = sw0 + lane; i < sw1; i += 64) mask_row[i] = 0u;
+    if (dense_row)
+      for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  // set bits of keep-mask word wi: in the LDS stage (workgroup-scope atomic),
+  // or directly in memory (device-scope atomic) when the slice does not fit
+  auto or_mask_word = [&](int wi, uint32_t bits) {
+    if (stage_ok)
+      __hip_atomic_fetch_or(my_stage + (wi - sw0), bits, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
+    else
+      __hip_atomic_fetch_or(mask_row + wi, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   uint32_t pos_base = my_off;
-  double cbase = my_cum;
-  int my_token = -1;         // set in wave sw
-  int last_pos_id = -1;      // last kept id with q > 0 in this wave
+  uint32_t ties_seen = 0u;
+  double cbase = my_cumw * inv_wp;
+  int my_token = -1;       // set in wave sw
+  int last_pos_id = -1;    // last kept id with q > 0 in this wave
   walk([&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t vm) {
-    uint32_t pb = 0u;
+    uint32_t tb = 0u, gb = 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool in = ((vm >> j) & 1u) &&
-                      (key[j] > pstar || (key[j] == pstar && n_keep > 0u && id[j] <= id_cut));
-      pb |= (in ? 1u : 0u) << j;
+      const bool v = (vm >> j) & 1u;
+      tb |= ((v && key[j] == pstar && n_keep > 0u) ? 1u : 0u) << j;
+      gb |= ((v && key[j] > pstar) ? 1u : 0u) << j;
     }
+    // ties keep their rank order: the first my_kt ties of this wave are kept
+    uint32_t ttot;
+    uint32_t trank = ties_seen + wave_excl_small((uint32_t)__popc(tb), ttot);
+    uint32_t pb = gb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((tb >> j) & 1u) {
+        if (trank < my_kt) pb |= 1u << j;
+        ++trank;
+      }
+    }
+    ties_seen += ttot;
     uint32_t total;
     uint32_t pos = pos_base + wave_excl_small((uint32_t)__popc(pb), total);
     double qv[8];
     double lane_sum = 0.0;
-    uint32_t mword = 0u;
     int mwi = -1;
+    uint32_t mword = 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       qv[j] = 0.0;
       if ((pb >> j) & 1u) {
-        const double q = greedy ? 1.0 : weight<DT>(key[j], m, invT) * inv_wp;
+        const double q = greedy ? 1.0 : wkey(key[j]) * inv_wp;
         qv[j] = q;
         lane_sum += q;
         const float qf = (float)q;
@@ -1004,7 +1314,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         if (q > 0.0) last_pos_id = (int)id[j];
         const int wi = (int)(id[j] >> 5);
         if (wi != mwi) {
-          if (mwi >= 0 && mask_row) atomicOr(mask_row + mwi, mword);
+          if (mwi >= 0 && mask_row) or_mask_word(mwi, mword);
           mwi = wi;
           mword = 0u;
         }
@@ -1012,7 +1322,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         ++pos;
       }
     }
-    if (mwi >= 0 && mask_row) atomicOr(mask_row + mwi, mword);
+    if (mwi >= 0 && mask_row) or_mask_word(mwi, mword);
     pos_base += total;
     if (w == sw && my_token < 0) {
       const double incl = wave_incl_scan_f64(lane_sum, lane);
@@ -1024,49 +1334,37 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         c += qv[j];
         if (hit < 0 && ((pb >> j) & 1u) && u < c) hit = (int)id[j];
       }
-      const uint64_t hb = ballot(hit >= 0);
-      if (hb) {
-        const int fl = __ffsll((unsigned long long)hb) - 1;
+      const uint64_t hbits = ballot(hit >= 0);
+      if (hbits) {
+        const int fl = __ffsll((unsigned long long)hbits) - 1;
         my_token = __shfl(hit, fl, 64);
       }
       cbase += wtotal;
     }
   });
-
-  // token: from wave sw; if rounding left u at or above the total, the last
-  // kept id with q > 0
-  {
-    const uint32_t lpu = wave_reduce<OpMax>((uint32_t)(last_pos_id + 1));
-    if (lane == 0) {
-      red.v[par][w][0] = lpu;
-      red.v[par][w][1] = (uint32_t)(my_token + 1);
+  // this wave's mask words
+  if (mask_row && stage_ok) {
+    for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
+  }
+  // the token: from wave sw; if rounding left u at or above wave sw's last
+  // cumulative sum, that wave's last kept id with q > 0; if u lies past every
+  // wave, the last kept id with q > 0 of the row
+  const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
+  if (SAMPLE && lane == 0) {
+    if (greedy) {
+      if (my_kt > 0u) a.tokens[r] = last_id;  // the one kept token lies in this wave
+    } else if (w == sw) {
+      a.tokens[r] = my_token >= 0 ? my_token : last_id;
+    } else if (sw < 0 && w == last_w) {
+      a.tokens[r] = last_id;
     }
   }
-  __syncthreads();
-  int token = -1;
-  if (greedy) {
-    token = (int)max_id;
-  } else if (sampled) {
-    if (sw >= 0) {
-      token = (int)red.v[par][sw][1] - 1;
-      // u fell past wave sw's last cumulative sum only by rounding
-      if (token < 0 && red.v[par][sw][0] > 0u) token = (int)red.v[par][sw][0] - 1;
-    }
-    if (token < 0) {
-      for (int ww = kWaves - 1; ww >= 0 && token < 0; --ww)
-        if (red.v[par][ww][0] > 0u) token = (int)red.v[par][ww][0] - 1;
-    }
-  }
-  par ^= 1;
 
   if (tid == 0) {
     const bool over = (a.cand_ids || a.cand_probs) ? n_p > cap : false;
     a.status[r] = over ? QS_ROW_CAND_OVERFLOW : QS_ROW_OK;
     if (a.cand_count) a.cand_count[r] = (int32_t)n_p;
-    if (SAMPLE) {
-      a.tokens[r] = token;
-      if (sampled && !a.uniforms) a.offset[r] = a.offset[r] + 1u;
-    }
+    if (SAMPLE && sampled && !a.uniforms) a.offset[r] = a.offset[r] + 1u;
     if (a.dbg) {
       a.dbg[4 * r + 0] = use_pool ? 0 : 1;
       a.dbg[4 * r + 1] = rounds;
@@ -1136,21 +1434,51 @@ __global__ void __launch_bounds__(kThreads) argmax_rows_kernel(ArgmaxArgs a) {
 
 // ---------------------------------------------------------------------------
 // Launchers (host side of this translation unit).
+
+// Slice length of the streamed pass: V split in 16, rounded up to 32 tokens.
 int seg_for(int V) {
   int s = (V + kWaves - 1) / kWaves;
   return (s + 31) & ~31;
 }
 
-hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st) {
+namespace {
+
+// Steps of 512 tokens per wave slice when the row is held in registers.
+int resident_steps(int V) {
+  const int per_wave = (V + kWaves - 1) / kWaves;
+  return (per_wave + kStep - 1) / kStep;
+}
+
+template <int DT, bool S>
+hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
+#ifdef QS_DEV_ONE
+  if (DT != QS_DEV_DT || !S) return hipErrorInvalidValue;
+  a.seg = resident_steps(a.V) * kStep;
+  hipLaunchKernelGGL((filter_rows_kernel<QS_DEV_DT, true, QS_DEV_NL>), dim3((unsigned)B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+#else
   dim3 grid((unsigned)B), block(kThreads);
-  if (dtype == QS_F32) {
-    if (sample) hipLaunchKernelGGL((filter_rows_kernel<0, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((filter_rows_kernel<0, false>), grid, block, 0, st, a);
+  const int n = resident_steps(a.V);
+  const bool stream = (a.flags & QS_FLAG_STREAM) != 0u;
+  if (!stream && n <= kResidentTier[DT][0]) {
+    a.seg = n * kStep;
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0]>), grid, block, 0, st, a);
+  } else if (!stream && n <= kResidentTier[DT][1]) {
+    a.seg = n * kStep;
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1]>), grid, block, 0, st, a);
   } else {
-    if (sample) hipLaunchKernelGGL((filter_rows_kernel<1, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((filter_rows_kernel<1, false>), grid, block, 0, st, a);
+    a.seg = seg_for(a.V);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0>), grid, block, 0, st, a);
   }
   return hipGetLastError();
+#endif
+}
+
+}  // namespace
+
+hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st) {
+  if (dtype == QS_F32) return sample ? launch_dt<0, true>(a, B, st) : launch_dt<0, false>(a, B, st);
+  return sample ? launch_dt<1, true>(a, B, st) : launch_dt<1, false>(a, B, st);
 }
 
 hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st) {

@@ -135,6 +135,16 @@ struct RowReader {
   }
 };
 
+// Stand-in for RowReader where the row is held in registers instead.
+template <int DT>
+struct NoReader {
+  int n = 0;
+  __device__ __forceinline__ NoReader(const Slice&, int) {}
+  __device__ __forceinline__ void issue(int, int) {}
+  __device__ __forceinline__ void fetch(int, int, Raw<DT>&, uint32_t& mb) const { mb = 0u; }
+  __device__ __forceinline__ int first(int) const { return 0; }
+};
+
 // Walk a slice in id order with a D-deep prefetch; f(raw, mb, e) per step.
 template <int DT, int D, class F>
 __device__ __forceinline__ void stream_slice(const Slice& s, int lane, F&& f) {
@@ -244,11 +254,19 @@ __device__ __forceinline__ uint32_t raw_of(const Raw<DT>& raw, uint32_t j) {
   }
 }
 
-template <int DT>
+// Candidate extraction: lane holds candidate bits cb (bit j = token e + j) and
+// the raw bits of its 8 tokens; append them, in id order, to this wave's pool
+// at pool_cnt (entries past the capacity are counted, not stored). Also keeps
+// the largest key seen (pmax) and, with HIST, counts every candidate in the
+// per-key histogram hist[key - hist_lo] (keys past the last bin set hover).
+// Returns the new count (every lane gets the same value).
+template <int DT, bool HIST>
 __device__ __forceinline__ uint32_t append_candidates(
     uint32_t cb, const Raw<DT>& raw, uint32_t e_local, uint32_t pool_cnt,
-    typename PoolLayout<DT>::KeyT* pk, uint16_t* pid) {
+    typename PoolLayout<DT>::KeyT* pk, uint16_t* pid, uint32_t& pmax,
+    uint32_t* hist, uint32_t hist_lo, uint32_t hist_bins, uint32_t& hover) {
   using KeyT = typename PoolLayout<DT>::KeyT;
+  using K = Keys<DT>;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<DT>::kPerWave;
   const uint32_t c = (uint32_t)__popc(cb);
   const uint64_t any = ballot(c != 0u);
@@ -265,9 +283,17 @@ __device__ __forceinline__ uint32_t append_candidates(
     if (cb) {
       const uint32_t j = (uint32_t)__builtin_ctz(cb);
       cb &= cb - 1u;
+      const uint32_t rb = raw_of<DT>(raw, j);
       if (pos < kCap) {
-        pk[pos] = (KeyT)raw_of<DT>(raw, j);
+        pk[pos] = (KeyT)rb;
         pid[pos] = (uint16_t)(e_local + j);
+      }
+      const uint32_t key = K::of(rb);
+      pmax = key > pmax ? key : pmax;
+      if constexpr (HIST) {
+        const uint32_t b = key - hist_lo;
+        if (b < hist_bins) atomicAdd(hist + b, 1u);
+        else hover = 1u;
       }
       ++pos;
     }
