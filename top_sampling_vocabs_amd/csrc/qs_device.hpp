@@ -176,6 +176,53 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (a + b) + (c + d);
 }
 
+// Inclusive prefix sums over the 64 lanes with DPP: shifts by 1, 2, 4, 8
+// within each row of 16 lanes (lanes shifted in from outside the row read 0),
+// then row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and
+// row_bcast:31 adds lane 31 to rows 2 and 3. incl_shift1 moves every lane's
+// value to the next lane (0 into lane 0).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppWfShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_rm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_rm_f64(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = dpp_rm<CTRL, ROW_MASK>((uint32_t)b);
+  const uint32_t hi = dpp_rm<CTRL, ROW_MASK>((uint32_t)(b >> 32));
+  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t scan_incl_u32(uint32_t x) {
+  x += dpp_rm<kDppRowShr1, 0xF>(x);
+  x += dpp_rm<kDppRowShr2, 0xF>(x);
+  x += dpp_rm<kDppRowShr4, 0xF>(x);
+  x += dpp_rm<kDppRowShr8, 0xF>(x);
+  x += dpp_rm<kDppRowBcast15, 0xA>(x);
+  x += dpp_rm<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ double scan_incl_f64(double x) {
+  x += dpp_rm_f64<kDppRowShr1, 0xF>(x);
+  x += dpp_rm_f64<kDppRowShr2, 0xF>(x);
+  x += dpp_rm_f64<kDppRowShr4, 0xF>(x);
+  x += dpp_rm_f64<kDppRowShr8, 0xF>(x);
+  x += dpp_rm_f64<kDppRowBcast15, 0xA>(x);
+  x += dpp_rm_f64<kDppRowBcast31, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ double incl_shift1_f64(double incl) {
+  return dpp_rm_f64<kDppWfShr1, 0xF>(incl);
+}
+
 // (minimum key, number of occurrences of that minimum) pairs.
 struct MinCnt {
   uint32_t key;

@@ -169,6 +169,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     int32_t bsel;
     uint32_t sel_u[2];
     double sel_d[2];
+    uint32_t sc_u[8];   // single-wave scan results
+    double sc_d[2];
   } info;
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
@@ -176,7 +178,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = uni(tid >> 6);  // wave index, kept in a scalar register
   const int lane = tid & 63;
   int par = 0;
 
@@ -269,26 +271,42 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   using Reader = std::conditional_t<kResident, NoReader<DT>, RowReader<DT, D>>;
   Reader rd(sl, lane);
   const int nst = kResident ? NL : rd.n;
-  uint32_t s0mb = 0u;
+  constexpr int kMW = NL * (kStep / 32);  // packed-mask words of a resident slice
+  constexpr int kML = kResident ? (kMW + 63) / 64 : 1;
+  uint32_t mw[kML];
   if constexpr (kResident) {
+    // the slice's packed-mask words come with the sample: the pass needs them
+    // from its first step. Without a bitmask the word loads read the row start
+    // (16 bytes at least) and are ignored, so that the loads have no branch.
+    const uint32_t* const mwsrc = bmrow ? bmrow : reinterpret_cast<const uint32_t*>(sl.row);
+    const int w0 = sl.wb >> 5;
+    const int wlim = bmrow ? min(W, (sl.we + 31) >> 5) : 0;  // words of this slice
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+      const int wi = w0 + lane + 64 * i;
+      mw[i] = mwsrc[(lane + 64 * i < kMW && wi < wlim) ? wi : 0];
+    }
     res_issue(std::integral_constant<int, 0>{});
-    const int e0 = min(lane_e, last_piece);
-    s0mb = sl.mrow ? (uint32_t)sl.mrow[e0 >> 3] : 0xFFu;
   } else {
     if (nst > 0) rd.issue(0, 0);
   }
 
   // -- tables ----------------------------------------------------------------------
-  if constexpr (DT == 1) {  // pair masks of every legal byte: 0xFFFF per legal token
-    if (tid < 256) {
+  // Pair masks of every legal byte (0xFFFF per legal token). Every wave writes
+  // the whole table with the same values, so each wave may read it after its
+  // own writes without waiting for the others.
+  if constexpr (DT == 1) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t e = (uint32_t)(lane + 64 * q4);
       uint32_t v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        v[q] = ((((uint32_t)tid >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
-               ((((uint32_t)tid >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
-      lut[tid] = make_uint4(v[0], v[1], v[2], v[3]);
+        v[q] = (((e >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
+               (((e >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+      lut[e] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    hist[tid] = 0u;
+    hist[tid] = 0u;  // used after the pass barrier
   }
   if (tid == 0) info.bsel = -1;
 
@@ -305,8 +323,11 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         raw.r[4] = buf[0][kPieces - 1].x; raw.r[5] = buf[0][kPieces - 1].y;
         raw.r[6] = buf[0][kPieces - 1].z; raw.r[7] = buf[0][kPieces - 1].w;
       }
+      // byte `lane` of the slice's mask words: word lane/4 is held by lane lane/4
+      const uint32_t wd = (uint32_t)__shfl((int)mw[0], lane >> 2, 64);
+      const uint32_t b0 = bmrow ? (wd >> ((lane & 3) * 8)) & 0xFFu : 0xFFu;
       const int rem = sl.we - lane_e;
-      mb = s0mb & (rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u));
+      mb = b0 & (rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u));
     } else {
       rd.fetch(0, 0, raw, mb);
     }
@@ -322,45 +343,34 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     }
   }
 
-  // -- the rest of the row: packed-mask words of the slice and the ring -----------
-  constexpr int kMW = NL * (kStep / 32);  // packed-mask words of a resident slice
-  constexpr int kML = kResident ? (kMW + 63) / 64 : 1;
-  uint32_t mw[kML];
-  if constexpr (kResident) {
-    // without a bitmask the word loads read the row start (16 bytes at least)
-    // and are ignored, so that the load sequence has no branch
-    const uint32_t* const mwsrc = bmrow ? bmrow : reinterpret_cast<const uint32_t*>(sl.row);
-    const int w0 = sl.wb >> 5;
-    const int wlim = bmrow ? min(W, (sl.we + 31) >> 5) : 0;  // words of this slice
-#pragma unroll
-    for (int i = 0; i < kML; ++i) {
-      const int wi = w0 + lane + 64 * i;
-      mw[i] = mwsrc[(lane + 64 * i < kMW && wi < wlim) ? wi : 0];
-    }
-    static_for<1, RD>(res_issue);
-  } else {
-#pragma unroll
-    for (int i = 1; i < D; ++i)
-      if (i < nst) rd.issue(i, i);
-  }
 
-  // -- the threshold, while the row's loads are in flight ------------------------
+  // -- the row's threshold ------------------------------------------------------------
+  // The 16 step-0 samples (8192 tokens) are combined after one barrier; the
+  // rest of the row is requested only after it, so that every sample returns
+  // at unloaded latency, and the threshold is computed while the ring fills.
   {
-    double st[4] = {s_n, s_sum, s_sq, s_all};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st[i] = wave_sum_f64(st[i]);
+    const double st0 = wave_sum_f64(s_n), st1 = wave_sum_f64(s_sum);
+    const double st2 = wave_sum_f64(s_sq), st3 = wave_sum_f64(s_all);
     const uint32_t mx = wave_reduce<OpMax>(s_maxk);
     if (lane == 0) {
+      const double stv[4] = {st0, st1, st2, st3};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint64_t b = __double_as_longlong(st[i]);
+        const uint64_t b = __double_as_longlong(stv[i]);
         red.v[par][w][2 * i] = (uint32_t)b;
         red.v[par][w][2 * i + 1] = (uint32_t)(b >> 32);
       }
       red.v[par][w][8] = mx;
     }
   }
-  __syncthreads();  // sample partials, the pair-mask table, the zeroed histogram, bsel
+  __syncthreads();  // sample partials, the zeroed histogram, bsel
+  if constexpr (kResident) {
+    static_for<1, RD>(res_issue);
+  } else {
+#pragma unroll
+    for (int i = 1; i < D; ++i)
+      if (i < nst) rd.issue(i, i);
+  }
   {
     // lane i holds wave i's partials; the same combination order in every wave
     const bool act = lane < kWaves;
@@ -411,8 +421,13 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   };
 
   const double ms = s_n >= 1.0 ? (double)K::value(s_maxk) : 0.0;
-  const double tval = truncation_value(s_n, s_sum, s_sq, ms, s_all > 0.0 ? s_n / s_all : 0.0,
-                                       V, greedy, topk_req, kk, topp_on, p, invT);
+  // fewer than 32 legal finite sample tokens (a sparse mask): keep every legal
+  // finite token
+  const double tval = s_n < 32.0 && !greedy
+                          ? -__builtin_inf()
+                          : truncation_value(s_n, s_sum, s_sq, ms,
+                                             s_all > 0.0 ? s_n / s_all : 0.0, V, greedy,
+                                             topk_req, kk, topp_on, p, invT);
   // threshold as a key; no_trunc compacts nothing
   const bool t_all = !(tval > -__builtin_inf());
   uint32_t tkey = t_all ? K::kNegInf + 1u : K::of(raw_floor<DT>(tval));
@@ -426,7 +441,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const float bg_c = (float)(1.4426950408889634 * invT);
 
   // -- the pass ------------------------------------------------------------------
-  uint32_t anyl = 0u, pcnt = 0u, pmax = 0u, hover = 0u;
+  uint32_t anyl = 0u, pcnt = 0u;
   // Non-finite detectors over legal tokens (illegal tokens never trigger them):
   // POS pass: the largest raw bits read as unsigned (> the -inf pattern: a
   // negative NaN; equal: a -inf); NEG pass: the smallest signed value (below
@@ -434,12 +449,10 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   uint32_t ext2 = 0u;                        // bf16, packed per half
   uint32_t ext1 = 0u;                        // fp32
   double bg_sum = 0.0;     // sum of exp2((z - t) c) over legal finite z < t
-  float bg_wx = 0.0f;      // sum of w |x| (error bound)
-  float bg_w32 = 0.0f;     // sum of w in fp32 (error bound)
   PKey* const my_pk = pool_key + w * kCap;
   uint16_t* const my_pid = pool_id + w * kCap;
   // background terms: x = z c - t c, excluded tokens read as a large negative
-  // finite value so that w = 0 and w x = 0
+  // finite value so that w = 0
   const float bg_off = -bg_ref * bg_c;
   constexpr uint32_t kSent2 = 0xC47AC47Au;   // bf16 pair (-1000, -1000)
   constexpr uint32_t kSent1 = 0xC47A0000u;   // fp32 -1000
@@ -483,20 +496,15 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       if (need_bg) {  // legal tokens below t; the others read as the sentinel
         const uint4 nb4 = lut[mb & ~cb];
         const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
-        float sw = 0.0f, swx = 0.0f;
+        float sw = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t zb = bfi(nb[q], raw.r[q], kSent2);
           const float xlo = fmaf(__uint_as_float(zb << 16), bg_c, bg_off);
           const float xhi = fmaf(__uint_as_float(zb & 0xFFFF0000u), bg_c, bg_off);
-          const float wlo = __builtin_amdgcn_exp2f(xlo);
-          const float whi = __builtin_amdgcn_exp2f(xhi);
-          sw += wlo + whi;
-          swx = fmaf(wlo, -xlo, fmaf(whi, -xhi, swx));
+          sw += __builtin_amdgcn_exp2f(xlo) + __builtin_amdgcn_exp2f(xhi);
         }
         bg_sum += (double)sw;
-        bg_w32 += sw;
-        bg_wx += swx;
       }
     } else {
       const int32_t tm1 = tS - 1;
@@ -523,22 +531,16 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       for (int j = 0; j < 8; ++j) cb |= (dl[j] & 1u) << j;
       if (need_bg) {
         const uint32_t nb = mb & ~cb;
-        float sw = 0.0f, swx = 0.0f;
+        float sw = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t zb = ((nb >> j) & 1u) ? raw.r[j] : kSent1;
-          const float x = fmaf(__uint_as_float(zb), bg_c, bg_off);
-          const float wv = __builtin_amdgcn_exp2f(x);
-          sw += wv;
-          swx = fmaf(wv, -x, swx);
+          sw += __builtin_amdgcn_exp2f(fmaf(__uint_as_float(zb), bg_c, bg_off));
         }
         bg_sum += (double)sw;
-        bg_w32 += sw;
-        bg_wx += swx;
       }
     }
-    pcnt = append_candidates<DT, DT == 1>(cb, raw, (uint32_t)(e - sl.wb), pcnt, my_pk, my_pid,
-                                           pmax, hist, tkey, (uint32_t)kHistBins, hover);
+    pcnt = append_pool<DT>(cb, raw, (uint32_t)(e - sl.wb), pcnt, my_pk, my_pid);
   };
   auto run_pass = [&](auto pos_c) {
     if constexpr (kResident) {
@@ -598,67 +600,120 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   anyl = wave_reduce<OpMax>(anyl);
   nan_l = wave_reduce<OpMax>(nan_l);
   ninf_l = wave_reduce<OpMax>(ninf_l);
-  pmax = wave_reduce<OpMax>(pmax);
-  hover = wave_reduce<OpMax>(hover);
   bg_sum = wave_sum_f64(bg_sum);
-  const double bg_wx64 = wave_sum_f64((double)bg_wx);
-  const double bg_w64 = wave_sum_f64((double)bg_w32);
   if (lane == 0) {
     red.v[par][w][0] = anyl;
-    red.v[par][w][1] = nan_l | (ninf_l << 1);
-    info.cnt[w] = pcnt;
-    const uint64_t b0 = __double_as_longlong(bg_sum), b1 = __double_as_longlong(bg_wx64);
-    const uint64_t b2 = __double_as_longlong(bg_w64);
+    red.v[par][w][1] = nan_l | (ninf_l << 1) | ((t_all ? 1u : 0u) << 2);
+    const uint64_t b0 = __double_as_longlong(bg_sum);
     red.v[par][w][2] = (uint32_t)b0; red.v[par][w][3] = (uint32_t)(b0 >> 32);
-    red.v[par][w][4] = (uint32_t)b1; red.v[par][w][5] = (uint32_t)(b1 >> 32);
-    red.v[par][w][6] = (uint32_t)b2; red.v[par][w][7] = (uint32_t)(b2 >> 32);
-    red.v[par][w][8] = pmax;
-    red.v[par][w][9] = hover;
+    red.v[par][w][4] = tkey;
+    info.cnt[w] = pcnt;
   }
-  __syncthreads();  // pools, histogram and per-wave results complete
-  uint32_t ccount = 0u, my_wcnt = 0u, pool_max = 0u;
-  bool overflow = false, neg_nan = false, has_neginf = false, hist_over = false;
-  bool any_legal = false;
-  double bg_err = 0.0;
+  __syncthreads();  // pools and per-wave results complete
+  // lane i of every wave reads wave i's results
+  const bool act16 = lane < kWaves;
+  const int pw = par;  // the per-wave pass results stay in red.v[pw]
+  bool overflow, neg_nan, has_neginf, any_legal, all_tall;
+  uint32_t ccount_all, my_wcnt, t_eff;
   {
-    uint32_t al = 0u, fl = 0u, pm = 0u, ho = 0u;
-    double b0 = 0.0, b1 = 0.0, b2 = 0.0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      al |= red.v[par][ww][0];
-      fl |= red.v[par][ww][1];
-      const uint32_t c = info.cnt[ww];
-      if (ww == w) my_wcnt = c;
-      ccount += c;
-      overflow = overflow || c > kCap;
-      b0 += __longlong_as_double(((uint64_t)red.v[par][ww][3] << 32) | red.v[par][ww][2]);
-      b1 += __longlong_as_double(((uint64_t)red.v[par][ww][5] << 32) | red.v[par][ww][4]);
-      b2 += __longlong_as_double(((uint64_t)red.v[par][ww][7] << 32) | red.v[par][ww][6]);
-      pm = max(pm, red.v[par][ww][8]);
-      ho |= red.v[par][ww][9];
-    }
-    any_legal = uni(al != 0u);
-    neg_nan = uni((fl & 1u) != 0u);
-    has_neginf = uni((fl & 2u) != 0u);
-    bg_sum = uni(b0);
-    // per term: exp2 error plus the argument's roundings (ln2 * 2 * 2^-24 |x|),
-    // plus the fp32 accumulation of 8 terms per step
-    bg_err = uni(kExp2Err * b2 + 1.24e-7 * b1 + 4.2e-7 * b2 + 1e-30);
-    pool_max = uni(pm);
-    hist_over = uni(ho != 0u);
+    const uint32_t fl = act16 ? red.v[pw][lane][1] : 4u;
+    const uint32_t cn = act16 ? info.cnt[lane] : 0u;
+    any_legal = uni(wave_reduce<OpMax>(act16 ? red.v[pw][lane][0] : 0u) != 0u);
+    neg_nan = uni(wave_reduce<OpMax>(fl & 1u) != 0u);
+    has_neginf = uni(wave_reduce<OpMax>((fl >> 1) & 1u) != 0u);
+    all_tall = uni(wave_reduce<OpMin>((fl >> 2) & 1u) != 0u);
+    overflow = uni(wave_reduce<OpMax>(cn > kCap ? 1u : 0u) != 0u);
+    ccount_all = uni(wave_reduce<OpSum>(cn));
+    t_eff = uni(wave_reduce<OpMax>(act16 ? red.v[pw][lane][4] : 0u));
+    my_wcnt = uni(info.cnt[w]);
   }
-  ccount = uni(ccount);
-  my_wcnt = uni(my_wcnt);
-  overflow = uni(overflow);
+  (void)has_neginf;
   par ^= 1;
 
   const PKey* pk = my_pk;
   const uint16_t* pid = my_pid;
   const int my_cnt = (int)min(my_wcnt, kCap);
   // pool usable: complete, 16-bit ids fit, not forced off
-  const bool pool_ok = !overflow && ccount > 0u && !(a.flags & QS_FLAG_FORCE_MISS) &&
+  const bool pool_ok = !overflow && ccount_all > 0u && !(a.flags & QS_FLAG_FORCE_MISS) &&
                        !no_trunc && a.seg <= 65536;
-  // the pool holds every finite legal token (the threshold was -inf)
-  const bool pool_all = pool_ok && t_all;
+  // the row's truncation threshold: the highest wave threshold (every pool
+  // holds all of its slice's legal tokens at or above it)
+  const uint32_t wave_tkey = tkey;
+  tkey = t_eff;
+  // the pool holds every finite legal token (every threshold was -inf)
+  const bool pool_all = pool_ok && all_tall;
+
+  // -- the pool at the row's threshold ---------------------------------------------
+  // Count and histogram (bf16) the entries at or above it and take their
+  // maximum; entries below it (kept by waves with lower thresholds) join the
+  // background mass, summed in fp64 relative to the threshold value.
+  uint32_t ccount = 0u, pool_max = 0u;
+  bool hist_over = false;
+  double bgm = 0.0, bgb = 0.0;  // background mass below t and its error bound,
+                                // relative to the row maximum (top-k off only)
+  if (pool_ok) {
+    const double tv_eff = (double)K::value(tkey);
+    uint32_t ge = 0u, mxk = 0u, hov = 0u;
+    double xm = 0.0;
+    walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
+                  [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((vm >> j) & 1u) {
+          if (key[j] >= tkey) {
+            ++ge;
+            mxk = key[j] > mxk ? key[j] : mxk;
+            if constexpr (DT == 1) {
+              const uint32_t b = key[j] - tkey;
+              if (b < (uint32_t)kHistBins) atomicAdd(hist + b, 1u);
+              else hov = 1u;
+            }
+          } else if (need_bg) {
+            xm += exp64(((double)K::value(key[j]) - tv_eff) * invT);
+          }
+        }
+      }
+    });
+    ge = wave_reduce<OpSum>(ge);
+    mxk = wave_reduce<OpMax>(mxk);
+    hov = wave_reduce<OpMax>(hov);
+    xm = wave_sum_f64(xm);
+    if (lane == 0) {
+      red.v[par][w][0] = ge; red.v[par][w][1] = mxk; red.v[par][w][2] = hov;
+      const uint64_t bx = __double_as_longlong(xm);
+      red.v[par][w][3] = (uint32_t)bx; red.v[par][w][4] = (uint32_t)(bx >> 32);
+    }
+    __syncthreads();  // the histogram is complete
+    ccount = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
+    pool_max = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u));
+    hist_over = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][2] : 0u) != 0u);
+    if (need_bg) {
+      // wave i's background was summed relative to its own threshold; the
+      // error bound per term: the hardware exp2 (4 ulp), the fp32 sums of 8
+      // terms, and the argument's roundings (|dx| <= 2^-24 (|t c| + 2|x|),
+      // with w |x| <= 1 / (e ln 2) per term)
+      const double m_ = (double)K::value(pool_max);
+      const uint32_t tki = act16 ? red.v[pw][lane][4] : K::kNegInf + 1u;
+      const double tvi = (double)K::value(tki);
+      const double bgi = act16 ? __longlong_as_double(((uint64_t)red.v[pw][lane][3] << 32) |
+                                                      red.v[pw][lane][2])
+                               : 0.0;
+      const double xmi = act16 ? __longlong_as_double(((uint64_t)red.v[par][lane][4] << 32) |
+                                                      red.v[par][lane][3])
+                               : 0.0;
+      const double sc = bgi > 0.0 ? exp64((tvi - m_) * invT) : 0.0;
+      const double nslice = act16 ? (double)max(0, min(V, (lane + 1) * a.seg) -
+                                                   min(V, lane * a.seg))
+                                  : 0.0;
+      const double cterm = fabs(tvi * (double)bg_c) * 4.1315e-8;  // ln2 2^-24 |t c|
+      const double bnd = bgi * (kExp2Err + 4.2e-7 + cterm) + nslice * 4.4e-8;
+      bgm = uni(wave_sum_f64(bgi * sc)) +
+            uni(wave_sum_f64(xmi)) * exp64((tv_eff - m_) * invT);
+      bgb = uni(wave_sum_f64(bnd * sc)) + 1e-300;
+    }
+    par ^= 1;
+  }
+  (void)wave_tkey;
 
   auto block_sum_f64 = [&](double v) -> double {
     v = wave_sum_f64(v);
@@ -767,22 +822,171 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
   if (hist_t) __syncthreads();  // the weight table is read by every wave below
   double w_f = -1.0, w_f_err = 0.0;
-  if (mass_test) {
-    double s = 0.0;
+  int rounds = 0;
+  bool failed = false;
+  // The boundary (pstar, n_keep, w_star): keep key > pstar and the first n_keep
+  // ids of key == pstar, whose weight is w_star. `settled` once it is known.
+  bool settled = false;
+  uint32_t kap = 0u, n_keep_k = 0u;
+  uint32_t pstar = K::kNegInf;  // keep-all: every source key is above it
+  uint32_t n_keep = 0u;
+  double w_star = 0.0;
+  // -- single-wave scans of the bf16 pool histogram ---------------------------
+  // Wave 0 alone reads the 1024 key bins, 16 per lane from the top key down,
+  // and finds the top-k boundary (suffix counts reaching k: the page's stop
+  // test N_tau >= k > N_tau - N_zm evaluated at every key) and the top-p
+  // boundary (suffix fp64 masses reaching p * W) with DPP prefix sums; the
+  // other waves wait at the barrier that publishes the result.
+  if (hist_t && !(a.flags & QS_FLAG_PIVOT_SEARCH) && use_pool) {
+    const bool tk = kk > 0 && (uint32_t)kk < ccount;
+    double bg_mass = bgm;
+    double bg_bound = bgb;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      if (w == 0) {
+        // pass 1: lane l sums bins 1023-16l .. 1008-16l; a DPP prefix over the
+        // lanes finds the group of 16 bins holding the boundary; pass 2: lane
+        // i < 16 takes bin i of that group and a 16-lane prefix finds the bin.
+        const int b0 = kHistBins - 1 - 16 * lane;
+        const uint4* const h4 = reinterpret_cast<const uint4*>(hist + (b0 - 15));
+        uint32_t kapb = 0u, nkk = 0u;
+        if (tk) {
+          uint32_t ls = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 v = h4[q];
+            ls += v.x + v.y + v.z + v.w;
+          }
+          const uint32_t incl = scan_incl_u32(ls);
+          const int L = __ffsll((unsigned long long)ballot(incl >= (uint32_t)kk)) - 1;
+          const uint32_t gex = readlane_u32(incl - ls, L);  // tokens above group L
+          const int bi = kHistBins - 1 - 16 * L - (lane & 15);
+          const uint32_t hi = lane < 16 ? hist[bi] : 0u;
+          const uint32_t gin = gex + scan_incl_u32(hi);  // lanes >= 16 hold junk
+          const uint64_t f = ballot(lane < 16 && gin >= (uint32_t)kk) ;
+          const int i = __ffsll((unsigned long long)f) - 1;
+          kapb = (uint32_t)(kHistBins - 1 - 16 * L - i);
+          nkk = (uint32_t)kk - (readlane_u32(gin, i) - readlane_u32(hi, i));
+        }
+        // restricted count of bin b: inside the top-k set only
+        auto hpf = [&](uint32_t b, uint32_t h) -> uint32_t {
+          return !tk ? h : (b > kapb ? h : (b == kapb ? nkk : 0u));
+        };
+        uint32_t ok = 1u, pb = 0xFFFFFFFFu, nk = 0u, refine = 0u, bad = 0u;
+        double wz = 0.0, w_ref = 0.0;
+        if (topp_on) {
+          double ls = 0.0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 v = h4[q];
+            const uint32_t hq[4] = {v.x, v.y, v.z, v.w};  // bins b0-15+4q .. b0-12+4q
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int b = b0 - 15 + 4 * q + j;
+              ls += (double)hpf((uint32_t)b, hq[j]) * binw[b];
+            }
+          }
+          const double incl = scan_incl_f64(ls);
+          const double excl = incl_shift1_f64(incl);
+          const double total = readlane_f64(incl, 63);
+          double err = 0.0;
+          w_ref = total;
+          if (mass_test) {
+            w_ref = total + bg_mass;
+            err = bg_bound;
+            ok = total >= p * (w_ref + err) * (1.0 + 1e-9) ? 1u : 0u;
+          }
+          if (ok) {
+            const double target = p * w_ref;
+            const uint64_t bal = ballot(incl >= target);
+            const int L = bal ? __ffsll((unsigned long long)bal) - 1 : 63;
+            const double gex = readlane_f64(excl, L);  // mass above group L
+            const int bi = kHistBins - 1 - 16 * L - (lane & 15);
+            const uint32_t hp = lane < 16 ? hpf((uint32_t)bi, hist[bi]) : 0u;
+            const double wb = lane < 16 ? binw[bi] : 0.0;
+            const double Mi = (double)hp * wb;
+            const double gin = scan_incl_f64(Mi);
+            const double run = gex + gin;  // mass down to and including bin bi
+            const uint64_t f = ballot(lane < 16 && Mi > 0.0 && run >= target);
+            const uint64_t any = ballot(lane < 16 && Mi > 0.0);
+            // the first bin whose inclusive mass reaches the target; if rounding
+            // leaves none in the group, its last weighted bin
+            const int i = f ? __ffsll((unsigned long long)f) - 1
+                            : (any ? 63 - __clzll((long long)any) : -1);
+            if (i < 0) {
+              bad = 1u;
+            } else {
+              pb = (uint32_t)(kHistBins - 1 - 16 * L - i);
+              const double below = gex + (readlane_f64(gin, i) - readlane_f64(Mi, i));
+              wz = readlane_f64(wb, i);
+              const uint32_t c = readlane_u32(hp, i);
+              // smallest count of boundary tokens that reaches the target
+              const double need = (target - below) / wz;
+              nk = need <= 1.0 ? 1u : (need >= (double)c ? c : (uint32_t)ceil(need));
+              while (nk > 1u && below + (double)(nk - 1u) * wz >= target) --nk;
+              while (nk < c && below + (double)nk * wz < target) ++nk;
+              const double w_p = below + (double)nk * wz;
+              // the same cut for every reference mass in [w_ref - err, w_ref + err]?
+              const double lo_t = p * (w_ref - err), hi_t = p * (w_ref + err);
+              const double prev = below + (double)(nk - 1u) * wz;
+              refine = (err > 0.0 && !(prev < lo_t && hi_t <= w_p)) ? 1u : 0u;
+            }
+          }
+        } else if (tk) {
+          pb = kapb;
+          nk = nkk;
+          wz = binw[kapb];
+        }
+        if (lane == 0) {
+          info.sc_u[0] = ok; info.sc_u[1] = kapb; info.sc_u[2] = nkk; info.sc_u[3] = pb;
+          info.sc_u[4] = nk; info.sc_u[5] = refine; info.sc_u[6] = bad;
+          info.sc_d[0] = wz; info.sc_d[1] = w_ref;
+        }
+      }
+      __syncthreads();
+      const bool ok = uni(info.sc_u[0]) != 0u;
+      const bool refine = uni(info.sc_u[5]) != 0u;
+      rounds = attempt + 1;
+      if (!ok) { use_pool = false; break; }
+      if (uni(info.sc_u[6]) != 0u) { failed = true; settled = true; break; }
+      if (!refine) {
+        settled = true;
+        if (tk) { kap = tkey + uni(info.sc_u[1]); n_keep_k = uni(info.sc_u[2]); }
+        const uint32_t pbv = uni(info.sc_u[3]);
+        if (pbv != 0xFFFFFFFFu) {
+          pstar = tkey + pbv;
+          n_keep = uni(info.sc_u[4]);
+          w_star = uni(info.sc_d[0]);
+        }
+        w_f = uni(info.sc_d[1]);
+        break;
+      }
+      // exact background mass: fp64 over every finite legal token below t
+      double sx = 0.0;
+      walk_row<DT, false>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
+                                        uint32_t vm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (((vm >> j) & 1u) && key[j] < tkey) sx += weight<DT>(key[j], m, invT);
+      });
+      bg_mass = block_sum_f64(sx);
+      bg_bound = 0.0;
+    }
+  }
+  if (mass_test && !settled && use_pool) {
+    double sx = 0.0;
     if (hist_t) {
-      s = (double)h_own * w_own;
+      sx = (double)h_own * w_own;
     } else {
       walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
                     [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if ((vm >> j) & 1u) s += weight<DT>(key[j], m, invT);
+          if (((vm >> j) & 1u) && key[j] >= tkey) sx += weight<DT>(key[j], m, invT);
       });
     }
-    const double w_pool = block_sum_f64(s);
-    const double scale = exp64(((double)bg_ref - m) * invT);
-    w_f = w_pool + bg_sum * scale;
-    w_f_err = bg_err * scale;
+    const double w_pool = block_sum_f64(sx);
+    w_f = w_pool + bgm;
+    w_f_err = bgb;
     use_pool = w_pool >= p * (w_f + w_f_err) * (1.0 + 1e-9);
   }
   if (!use_pool) {
@@ -801,7 +1005,6 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
   const bool topk_eff = !greedy && kk > 0 && (uint32_t)kk < (use_pool ? ccount : nfin);
   const bool use_hist = hist_t && use_pool;
-  const bool scan_mode = use_hist && !(a.flags & QS_FLAG_PIVOT_SEARCH);
   const uint32_t src_lo = use_pool ? tkey : K::kNegInf + 1u;  // every source key >= src_lo
 
   // items of the pivot searches: (key, multiplicity) from the histogram, else tokens
@@ -839,31 +1042,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     return block_sum_f64(s);
   };
 
-  int rounds = 0;
-  bool failed = false;
-
   // -- the k-th largest key (top-k) ----------------------------------------------
-  uint32_t kap = 0u, n_keep_k = 0u;
-  if (topk_eff && scan_mode) {
-    // suffix counts S(b) = #pool tokens with key >= tkey + b; the boundary key
-    // is the one with S(b) >= k > S(b) - h(b)
-    const uint32_t incl = wave_incl_u32(h_own, lane);
-    if (lane == 63) red.v[par][w][0] = incl;
-    __syncthreads();
-    uint32_t wex = 0u;
-    for (int ww = 0; ww < w; ++ww) wex += red.v[par][ww][0];
-    const uint32_t S = wex + incl;
-    const uint32_t kq = (uint32_t)kk;
-    if (S >= kq && S - h_own < kq) {
-      info.sel_u[0] = (uint32_t)hb;
-      info.sel_u[1] = S - h_own;
-    }
-    __syncthreads();
-    kap = uni(tkey + info.sel_u[0]);
-    n_keep_k = uni(kq - info.sel_u[1]);
-    par ^= 1;
-    rounds = 1;
-  } else if (topk_eff) {
+  if (topk_eff && !settled) {
     // quaternary three-pivot search on counts (page "Qrita", key design 2)
     uint32_t lo = src_lo - 1u, hi = maxk;
     bool found = false;
@@ -936,88 +1116,13 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
 
   // -- final boundary (pstar, n_keep): keep key > pstar, and the first n_keep
   //    ids of key == pstar --------------------------------------------------
-  uint32_t pstar = K::kNegInf;  // keep-all: every source key is above it
-  uint32_t n_keep = 0u;
-  double w_star = 0.0;
   if (greedy) {
     pstar = maxk;
     n_keep = 1u;
     w_star = 1.0;
-  } else if (!failed) {
+  } else if (!failed && !settled) {
     const double w_kap = topk_eff ? wkey(kap) : 0.0;
-    if (topp_on && scan_mode) {
-      // suffix masses over the histogram keys inside the top-k set; the
-      // boundary key is the largest b whose inclusive suffix mass reaches p * W
-      const uint32_t kapb = topk_eff ? kap - tkey : 0u;
-      const uint32_t hp = !topk_eff ? h_own
-                                    : ((uint32_t)hb > kapb ? h_own
-                                                           : ((uint32_t)hb == kapb ? n_keep_k : 0u));
-      const double M = (double)hp * w_own;
-      double ex_l;
-      const double in_l = wave_incl_f64(M, lane, ex_l);
-      if (lane == 63) {
-        const uint64_t b = __double_as_longlong(in_l);
-        red.v[par][w][0] = (uint32_t)b;
-        red.v[par][w][1] = (uint32_t)(b >> 32);
-      }
-      __syncthreads();
-      double wex = 0.0, total = 0.0;  // totals of the waves below, added in wave order
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const double t = __longlong_as_double(((uint64_t)red.v[par][ww][1] << 32) |
-                                              red.v[par][ww][0]);
-        if (ww == w) wex = total;
-        total += t;
-      }
-      total = uni(total);
-      par ^= 1;
-      const double incl = wex + in_l;
-      const double excl = lane > 0 ? wex + ex_l : wex;
-      double w_ref = topk_eff ? total : (w_f >= 0.0 ? w_f : total);
-      double err = topk_eff ? 0.0 : w_f_err;
-      for (int attempt = 0; attempt < 2; ++attempt) {
-        const double target = p * w_ref;
-        if (incl >= target) atomicMax(&info.bsel, hb);
-        __syncthreads();
-        const int bs = info.bsel;
-        if (hb == bs) {
-          info.sel_d[0] = excl;
-          info.sel_d[1] = w_own;
-          info.sel_u[0] = hp;
-        }
-        __syncthreads();
-        const double below = uni(info.sel_d[0]);
-        const double wz = uni(info.sel_d[1]);
-        const uint32_t c = uni(info.sel_u[0]);
-        ++rounds;
-        if (bs < 0 || c == 0u || !(wz > 0.0)) { failed = true; break; }
-        pstar = tkey + (uint32_t)bs;
-        w_star = wz;
-        // smallest count of boundary tokens that reaches the target
-        const double need = (target - below) / wz;
-        uint32_t nk = need <= 1.0 ? 1u : (need >= (double)c ? c : (uint32_t)ceil(need));
-        while (nk > 1u && below + (double)(nk - 1u) * wz >= target) --nk;
-        while (nk < c && below + (double)nk * wz < target) ++nk;
-        n_keep = nk;
-        const double w_p = below + (double)nk * wz;
-        // the same cut for every reference mass in [w_ref - err, w_ref + err]?
-        const double lo_t = p * (w_ref - err), hi_t = p * (w_ref + err);
-        const double prev = below + (double)(nk - 1u) * wz;
-        const bool refine = err > 0.0 && !(prev < lo_t && hi_t <= w_p);
-        if (!refine) break;
-        // exact background mass: fp64 over every finite legal token below t
-        double s = 0.0;
-        walk_row<DT, false>(sl, lane, [&](const uint32_t (&key)[8], const uint32_t (&)[8],
-                                          uint32_t vm) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (((vm >> j) & 1u) && key[j] < tkey) s += weight<DT>(key[j], m, invT);
-        });
-        w_ref = total + block_sum_f64(s);
-        err = 0.0;
-        if (tid == 0) info.bsel = -1;
-        __syncthreads();
-      }
-    } else if (topp_on) {
+    if (topp_on) {
       double w_k;
       if (topk_eff) w_k = mass_above(kap) + (double)n_keep_k * w_kap;
       else if (w_f >= 0.0) w_k = w_f;

@@ -235,6 +235,42 @@ __device__ __forceinline__ void walk_pool(const typename PoolLayout<DT>::KeyT* p
 // ---------------------------------------------------------------------------
 // Candidate extraction: lane holds candidate bits cb (bit j = token e + j) and
 // the raw bits of its 8 tokens; append them, in id order, to this wave's pool
+// at pool_cnt (entries past the capacity are counted, not stored). Returns
+// the new count (every lane gets the same value).
+template <int DT>
+__device__ __forceinline__ uint32_t append_pool(uint32_t cb, const Raw<DT>& raw,
+                                                uint32_t e_local, uint32_t pool_cnt,
+                                                typename PoolLayout<DT>::KeyT* pk,
+                                                uint16_t* pid) {
+  using KeyT = typename PoolLayout<DT>::KeyT;
+  constexpr uint32_t kCap = (uint32_t)PoolLayout<DT>::kPerWave;
+  const uint32_t c = (uint32_t)__popc(cb);
+  const uint64_t any = ballot(c != 0u);
+  if (!any) return pool_cnt;
+  uint32_t excl, total;
+  if (!ballot(c > 1u)) {  // at most one candidate per lane: one ballot
+    excl = count_below(any);
+    total = (uint32_t)__popcll(any);
+  } else {
+    excl = wave_excl_small(c, total);
+  }
+  uint32_t pos = pool_cnt + excl;
+  while (ballot(cb != 0u)) {
+    if (cb) {
+      const uint32_t j = (uint32_t)__builtin_ctz(cb);
+      cb &= cb - 1u;
+      if (pos < kCap) {
+        pk[pos] = (KeyT)raw_of<DT>(raw, j);
+        pid[pos] = (uint16_t)(e_local + j);
+      }
+      ++pos;
+    }
+  }
+  return pool_cnt + total;
+}
+
+// Candidate extraction: lane holds candidate bits cb (bit j = token e + j) and
+// the raw bits of its 8 tokens; append them, in id order, to this wave's pool
 // at pool_cnt. Returns the new count (every lane gets the same value).
 template <int DT>
 __device__ __forceinline__ uint32_t raw_of(const Raw<DT>& raw, uint32_t j) {
