@@ -55,6 +55,16 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
 }
 
 constexpr int kHistBins = kThreads;   // bf16 pool histogram: one key per thread
+
+// Background histogram of bf16 rows with top-k off: one bin per bf16 value of
+// magnitude in [2^-12, 512) and sign, plus a lump below and above that range
+// per sign. Bin of a token: i = clamp(mag - (kBgMagLo - 1), 0, kBgExact + 1)
+// with mag = bits & 0x7FFF, plus kBgSide for a negative sign.
+constexpr uint32_t kBgMagLo = 0x3980u;            // magnitude bits of 2^-12
+constexpr uint32_t kBgExact = 21u * 128u;         // exact bins per sign (21 binades)
+constexpr uint32_t kBgSide = kBgExact + 2u;       // bins per sign
+constexpr int kBgBins = 2 * (int)kBgSide;
+static_assert(kBgMagLo + kBgExact == 0x4400u, "the upper lump starts at 512");
 // Register-resident tiers (steps of 512 tokens per wave slice), per dtype:
 // fp32 rows take two 16-byte loads per step, bf16 rows one.
 constexpr int kResidentTier[2][2] = {{5, 10}, {5, 20}};
@@ -160,6 +170,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint4 lut[DT == 1 ? 256 : 1];
   __shared__ uint32_t hist[kHB];
   __shared__ double binw[kHB];
+  __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins : 4];
   __shared__ RedScratch red;
   __shared__ struct {
     uint32_t cnt[kWaves];
@@ -307,6 +318,11 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       lut[e] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     hist[tid] = 0u;  // used after the pass barrier
+    if (need_bg) {   // filled by the pass
+      static_assert(kBgBins % 4 == 0, "the background histogram is cleared in 16-byte units");
+      uint4* const b4 = reinterpret_cast<uint4*>(bgh);
+      for (int i = tid; i < kBgBins / 4; i += kThreads) b4[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   if (tid == 0) info.bsel = -1;
 
@@ -448,13 +464,12 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // -inf: a negative NaN).
   uint32_t ext2 = 0u;                        // bf16, packed per half
   uint32_t ext1 = 0u;                        // fp32
-  double bg_sum = 0.0;     // sum of exp2((z - t) c) over legal finite z < t
+  double bg_sum = 0.0;     // fp32 rows: sum of exp2((z - t) c) over legal finite z < t
   PKey* const my_pk = pool_key + w * kCap;
   uint16_t* const my_pid = pool_id + w * kCap;
-  // background terms: x = z c - t c, excluded tokens read as a large negative
-  // finite value so that w = 0
+  // fp32 background terms: x = z c - t c, excluded tokens read as a large
+  // negative finite value so that w = 0
   const float bg_off = -bg_ref * bg_c;
-  constexpr uint32_t kSent2 = 0xC47AC47Au;   // bf16 pair (-1000, -1000)
   constexpr uint32_t kSent1 = 0xC47A0000u;   // fp32 -1000
 
   // One step: 8 tokens per lane. A legal token is a candidate iff its signed
@@ -493,18 +508,22 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
       cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
                                    __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
-      if (need_bg) {  // legal tokens below t; the others read as the sentinel
-        const uint4 nb4 = lut[mb & ~cb];
-        const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
-        float sw = 0.0f;
+      if (need_bg) {  // count the legal tokens below t in the background histogram
+        const uint32_t nbm = mb & ~cb;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t zb = bfi(nb[q], raw.r[q], kSent2);
-          const float xlo = fmaf(__uint_as_float(zb << 16), bg_c, bg_off);
-          const float xhi = fmaf(__uint_as_float(zb & 0xFFFF0000u), bg_c, bg_off);
-          sw += __builtin_amdgcn_exp2f(xlo) + __builtin_amdgcn_exp2f(xhi);
+          const uint32_t d = raw.r[q];
+          uint32_t bi = bits_of(__builtin_elementwise_sub_sat(
+              as_u2(d & 0x7FFF7FFFu), as_u2((kBgMagLo - 1u) * 0x10001u)));
+          bi = bits_of(__builtin_elementwise_min(as_u2(bi), as_u2((kBgExact + 1u) * 0x10001u)));
+          bi += ((d >> 15) & 0x00010001u) * kBgSide;
+          if ((nbm >> (2 * q)) & 1u)
+            __hip_atomic_fetch_add(bgh + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+          if ((nbm >> (2 * q + 1)) & 1u)
+            __hip_atomic_fetch_add(bgh + (bi >> 16), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        bg_sum += (double)sw;
       }
     } else {
       const int32_t tm1 = tS - 1;
@@ -603,28 +622,25 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   bg_sum = wave_sum_f64(bg_sum);
   if (lane == 0) {
     red.v[par][w][0] = anyl;
-    red.v[par][w][1] = nan_l | (ninf_l << 1) | ((t_all ? 1u : 0u) << 2);
+    red.v[par][w][1] = nan_l | (ninf_l << 1);
     const uint64_t b0 = __double_as_longlong(bg_sum);
     red.v[par][w][2] = (uint32_t)b0; red.v[par][w][3] = (uint32_t)(b0 >> 32);
-    red.v[par][w][4] = tkey;
     info.cnt[w] = pcnt;
   }
   __syncthreads();  // pools and per-wave results complete
   // lane i of every wave reads wave i's results
   const bool act16 = lane < kWaves;
   const int pw = par;  // the per-wave pass results stay in red.v[pw]
-  bool overflow, neg_nan, has_neginf, any_legal, all_tall;
-  uint32_t ccount_all, my_wcnt, t_eff;
+  bool overflow, neg_nan, has_neginf, any_legal;
+  uint32_t ccount_all, my_wcnt;
   {
-    const uint32_t fl = act16 ? red.v[pw][lane][1] : 4u;
+    const uint32_t fl = act16 ? red.v[pw][lane][1] : 0u;
     const uint32_t cn = act16 ? info.cnt[lane] : 0u;
     any_legal = uni(wave_reduce<OpMax>(act16 ? red.v[pw][lane][0] : 0u) != 0u);
     neg_nan = uni(wave_reduce<OpMax>(fl & 1u) != 0u);
     has_neginf = uni(wave_reduce<OpMax>((fl >> 1) & 1u) != 0u);
-    all_tall = uni(wave_reduce<OpMin>((fl >> 2) & 1u) != 0u);
     overflow = uni(wave_reduce<OpMax>(cn > kCap ? 1u : 0u) != 0u);
     ccount_all = uni(wave_reduce<OpSum>(cn));
-    t_eff = uni(wave_reduce<OpMax>(act16 ? red.v[pw][lane][4] : 0u));
     my_wcnt = uni(info.cnt[w]);
   }
   (void)has_neginf;
@@ -636,84 +652,105 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // pool usable: complete, 16-bit ids fit, not forced off
   const bool pool_ok = !overflow && ccount_all > 0u && !(a.flags & QS_FLAG_FORCE_MISS) &&
                        !no_trunc && a.seg <= 65536;
-  // the row's truncation threshold: the highest wave threshold (every pool
-  // holds all of its slice's legal tokens at or above it)
-  const uint32_t wave_tkey = tkey;
-  tkey = t_eff;
-  // the pool holds every finite legal token (every threshold was -inf)
-  const bool pool_all = pool_ok && all_tall;
+  // the pool holds every finite legal token (the threshold was -inf)
+  const bool pool_all = pool_ok && t_all;
 
-  // -- the pool at the row's threshold ---------------------------------------------
-  // Count and histogram (bf16) the entries at or above it and take their
-  // maximum; entries below it (kept by waves with lower thresholds) join the
-  // background mass, summed in fp64 relative to the threshold value.
+  // -- the pool and the background ---------------------------------------------------
+  // Count and histogram (bf16) the pool entries and take their maximum. Rows
+  // with top-k off also need the mass of the legal tokens below t, relative
+  // to the row maximum, with an error bound: bf16 rows weigh every bin of the
+  // background histogram in fp64 (exact bins; the lumps contribute their
+  // weight range to the bound); fp32 rows take the pass's fp32 terms.
   uint32_t ccount = 0u, pool_max = 0u;
   bool hist_over = false;
-  double bgm = 0.0, bgb = 0.0;  // background mass below t and its error bound,
-                                // relative to the row maximum (top-k off only)
+  double bgm = 0.0, bgb = 0.0;
   if (pool_ok) {
-    const double tv_eff = (double)K::value(tkey);
+    const double tv = (double)K::value(tkey);
     uint32_t ge = 0u, mxk = 0u, hov = 0u;
-    double xm = 0.0;
     walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
                   [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if ((vm >> j) & 1u) {
-          if (key[j] >= tkey) {
-            ++ge;
-            mxk = key[j] > mxk ? key[j] : mxk;
-            if constexpr (DT == 1) {
-              const uint32_t b = key[j] - tkey;
-              if (b < (uint32_t)kHistBins) atomicAdd(hist + b, 1u);
-              else hov = 1u;
-            }
-          } else if (need_bg) {
-            xm += exp64(((double)K::value(key[j]) - tv_eff) * invT);
+          ++ge;
+          mxk = key[j] > mxk ? key[j] : mxk;
+          if constexpr (DT == 1) {
+            const uint32_t b = key[j] - tkey;
+            if (b < (uint32_t)kHistBins) atomicAdd(hist + b, 1u);
+            else hov = 1u;
           }
         }
       }
     });
+    double bx = 0.0, bb = 0.0;  // background mass relative to w(t) = 1, bound
+    if constexpr (DT == 1) {
+      if (need_bg) {
+        for (int i = tid; i < kBgBins; i += kThreads) {
+          const uint32_t c = bgh[i];
+          if (c == 0u) continue;
+          const uint32_t side = (uint32_t)i >= kBgSide ? 1u : 0u;
+          const uint32_t j = (uint32_t)i - side * kBgSide;
+          const double cd = (double)c;
+          if (j >= 1u && j <= kBgExact) {  // one bf16 value
+            const uint32_t bits = (side << 15) | (kBgMagLo - 1u + j);
+            const double v = (double)__uint_as_float(bits << 16);
+            bx += cd * exp64((v - tv) * invT);
+          } else if (j == 0u) {            // |z| < 2^-12
+            const double e = 0.000244140625;
+            bx += cd * exp64(-tv * invT);
+            bb += cd * (exp64((e - tv) * invT) - exp64((-e - tv) * invT));
+          } else {                         // |z| >= 512 (and infinities, NaN)
+            bb += cd * (side ? exp64((-512.0 - tv) * invT) : 1.0);
+          }
+        }
+      }
+    }
     ge = wave_reduce<OpSum>(ge);
     mxk = wave_reduce<OpMax>(mxk);
     hov = wave_reduce<OpMax>(hov);
-    xm = wave_sum_f64(xm);
+    bx = wave_sum_f64(bx);
+    bb = wave_sum_f64(bb);
     if (lane == 0) {
       red.v[par][w][0] = ge; red.v[par][w][1] = mxk; red.v[par][w][2] = hov;
-      const uint64_t bx = __double_as_longlong(xm);
-      red.v[par][w][3] = (uint32_t)bx; red.v[par][w][4] = (uint32_t)(bx >> 32);
+      const uint64_t b0 = __double_as_longlong(bx), b1 = __double_as_longlong(bb);
+      red.v[par][w][3] = (uint32_t)b0; red.v[par][w][4] = (uint32_t)(b0 >> 32);
+      red.v[par][w][5] = (uint32_t)b1; red.v[par][w][6] = (uint32_t)(b1 >> 32);
     }
     __syncthreads();  // the histogram is complete
     ccount = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
     pool_max = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u));
     hist_over = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][2] : 0u) != 0u);
     if (need_bg) {
-      // wave i's background was summed relative to its own threshold; the
-      // error bound per term: the hardware exp2 (4 ulp), the fp32 sums of 8
-      // terms, and the argument's roundings (|dx| <= 2^-24 (|t c| + 2|x|),
-      // with w |x| <= 1 / (e ln 2) per term)
-      const double m_ = (double)K::value(pool_max);
-      const uint32_t tki = act16 ? red.v[pw][lane][4] : K::kNegInf + 1u;
-      const double tvi = (double)K::value(tki);
-      const double bgi = act16 ? __longlong_as_double(((uint64_t)red.v[pw][lane][3] << 32) |
-                                                      red.v[pw][lane][2])
-                               : 0.0;
-      const double xmi = act16 ? __longlong_as_double(((uint64_t)red.v[par][lane][4] << 32) |
-                                                      red.v[par][lane][3])
-                               : 0.0;
-      const double sc = bgi > 0.0 ? exp64((tvi - m_) * invT) : 0.0;
-      const double nslice = act16 ? (double)max(0, min(V, (lane + 1) * a.seg) -
-                                                   min(V, lane * a.seg))
-                                  : 0.0;
-      const double cterm = fabs(tvi * (double)bg_c) * 4.1315e-8;  // ln2 2^-24 |t c|
-      const double bnd = bgi * (kExp2Err + 4.2e-7 + cterm) + nslice * 4.4e-8;
-      bgm = uni(wave_sum_f64(bgi * sc)) +
-            uni(wave_sum_f64(xmi)) * exp64((tv_eff - m_) * invT);
-      bgb = uni(wave_sum_f64(bnd * sc)) + 1e-300;
+      double bxs, bbs;
+      if constexpr (DT == 1) {
+        bxs = uni(wave_sum_f64(act16 ? __longlong_as_double(((uint64_t)red.v[par][lane][4] << 32) |
+                                                            red.v[par][lane][3])
+                                     : 0.0));
+        bbs = uni(wave_sum_f64(act16 ? __longlong_as_double(((uint64_t)red.v[par][lane][6] << 32) |
+                                                            red.v[par][lane][5])
+                                     : 0.0));
+        bbs += 1e-12 * bxs;  // fp64 weights and sums
+      } else {
+        // per wave: the hardware exp2 (4 ulp), the fp32 sums of 8 terms, and
+        // the argument's roundings (|dx| <= 2^-24 (|t c| + 2|x|), with
+        // w |x| <= 1 / (e ln 2) per term)
+        const double bgi = act16 ? __longlong_as_double(((uint64_t)red.v[pw][lane][3] << 32) |
+                                                        red.v[pw][lane][2])
+                                 : 0.0;
+        const double nslice = act16 ? (double)max(0, min(V, (lane + 1) * a.seg) -
+                                                     min(V, lane * a.seg))
+                                    : 0.0;
+        const double cterm = fabs(tv * (double)bg_c) * 4.1315e-8;  // ln2 2^-24 |t c|
+        bxs = uni(wave_sum_f64(bgi));
+        bbs = uni(wave_sum_f64(bgi * (kExp2Err + 4.2e-7 + cterm) + nslice * 4.4e-8));
+      }
+      // tv <= the pool maximum: the scale is at most 1
+      const double sc = exp64((tv - (double)K::value(pool_max)) * invT);
+      bgm = bxs * sc;
+      bgb = bbs * sc + 1e-300;
     }
     par ^= 1;
   }
-  (void)wave_tkey;
 
   auto block_sum_f64 = [&](double v) -> double {
     v = wave_sum_f64(v);
