@@ -32,7 +32,7 @@ definition written out: a stable sort by (-logit, token id) of each full row,
 then prefix slices and fp64 cumulative sums. There is no truncation, pivoting,
 blocking or fusion here.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * top-p boundary is ">= p" (cumulative mass *reaching* p; worked answer to
   exercise 7 on the lecture page keeps 3 tokens when the sum hits 0.9 exactly);
 * ranking uses the exact logit z, not a rounded z/T;
