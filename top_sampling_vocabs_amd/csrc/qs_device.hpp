@@ -108,17 +108,6 @@ __device__ __forceinline__ double uni(double v) {
 }
 __device__ __forceinline__ bool uni(bool v) { return uni((uint32_t)v) != 0u; }
 
-// Exclusive prefix over lanes of a value in [0, 15], and the wave total, from
-// four bit-sliced ballots.
-__device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t& total) {
-  uint64_t b0 = ballot(c & 1u), b1 = ballot(c & 2u), b2 = ballot(c & 4u),
-           b3 = ballot(c & 8u);
-  total = (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) +
-                     8 * __popcll(b3));
-  return count_below(b0) + 2u * count_below(b1) + 4u * count_below(b2) +
-         8u * count_below(b3);
-}
-
 // ---------------------------------------------------------------------------
 // Wave64 all-reductions. Inside each 16-lane row: DPP quad_perm xor-1,
 // quad_perm xor-2, row_half_mirror, row_mirror (every lane of the row ends
@@ -248,17 +237,6 @@ __device__ __forceinline__ MinCnt wave_reduce_mc(MinCnt v) {
   MinCnt c{readlane_u32(v.key, 32), readlane_u32(v.cnt, 32)};
   MinCnt d{readlane_u32(v.key, 48), readlane_u32(v.cnt, 48)};
   return mc_merge(mc_merge(a, b), mc_merge(c, d));
-}
-
-// Inclusive scan of doubles over the lanes of a wave (shuffle-up ladder; used
-// once per sampled row).
-__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    double o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
 }
 
 // ---------------------------------------------------------------------------

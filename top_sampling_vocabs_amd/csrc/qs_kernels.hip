@@ -131,28 +131,6 @@ __device__ __forceinline__ uint32_t raw_floor(double t) {
   return h;
 }
 
-// Inclusive prefix over the lanes of a wave (ascending lanes); excl gets the
-// inclusive value of the lane below (0 in lane 0), so that neighbouring
-// partial sums are the same floating-point values.
-__device__ __forceinline__ double wave_incl_f64(double x, int lane, double& excl) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  const double b = __shfl_up(x, 1, 64);
-  excl = lane > 0 ? b : 0.0;
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
 // ---------------------------------------------------------------------------
 // NL > 0: the row is held in registers, NL steps of 512 tokens per wave slice.
 // NL == 0: the row streams through a prefetch ring.
@@ -237,23 +215,6 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     }
   };
 
-  // -- parameters ------------------------------------------------------------
-  const float Tf = a.T[r];
-  const int kk = a.k[r];
-  const float pf = a.p[r];
-  if (!(isfinite(Tf) && Tf >= 0.0f) || kk < 0 || !(pf > 0.0f && pf <= 1.0f)) {
-    finish_error(QS_ROW_BAD_PARAM);
-    return;
-  }
-  const bool greedy = (Tf == 0.0f);
-  const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
-  const double p = (double)pf;
-  const bool topp_on = !greedy && pf < 1.0f;
-  // top-k is requested for k in [1, V); whether k < |F| is known after the pass
-  const bool topk_req = !greedy && kk > 0 && kk < V;
-  const bool need_bg = topp_on && !topk_req;
-  const bool no_trunc = (a.flags & QS_FLAG_NO_TRUNCATION) != 0u;
-
   // -- the sample: step 0 of every slice ----------------------------------------
   // The first 512 tokens of each of the 16 slices (8192 tokens) are the only
   // request in flight until they have returned, so they come back at unloaded
@@ -301,6 +262,23 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   } else {
     if (nst > 0) rd.issue(0, 0);
   }
+
+  // -- parameters ------------------------------------------------------------
+  const float Tf = a.T[r];
+  const int kk = a.k[r];
+  const float pf = a.p[r];
+  if (!(isfinite(Tf) && Tf >= 0.0f) || kk < 0 || !(pf > 0.0f && pf <= 1.0f)) {
+    finish_error(QS_ROW_BAD_PARAM);
+    return;
+  }
+  const bool greedy = (Tf == 0.0f);
+  const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
+  const double p = (double)pf;
+  const bool topp_on = !greedy && pf < 1.0f;
+  // top-k is requested for k in [1, V); whether k < |F| is known after the pass
+  const bool topk_req = !greedy && kk > 0 && kk < V;
+  const bool need_bg = topp_on && !topk_req;
+  const bool no_trunc = (a.flags & QS_FLAG_NO_TRUNCATION) != 0u;
 
   // -- tables ----------------------------------------------------------------------
   // Pair masks of every legal byte (0xFFFF per legal token). Every wave writes
@@ -360,10 +338,20 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
 
 
+  // the rest of the ring: requested once this wave's sample has returned
+  if constexpr (kResident) {
+    static_for<1, RD>(res_issue);
+  } else {
+#pragma unroll
+    for (int i = 1; i < D; ++i)
+      if (i < nst) rd.issue(i, i);
+  }
+
   // -- the row's threshold ------------------------------------------------------------
-  // The 16 step-0 samples (8192 tokens) are combined after one barrier; the
-  // rest of the row is requested only after it, so that every sample returns
-  // at unloaded latency, and the threshold is computed while the ring fills.
+  // The 16 step-0 samples (8192 tokens) are combined after one barrier. Each
+  // wave requests the rest of its ring as soon as its own sample has returned
+  // (every sample was requested first, alone), so the threshold is computed
+  // while the ring fills.
   {
     const double st0 = wave_sum_f64(s_n), st1 = wave_sum_f64(s_sum);
     const double st2 = wave_sum_f64(s_sq), st3 = wave_sum_f64(s_all);
@@ -380,13 +368,6 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     }
   }
   __syncthreads();  // sample partials, the zeroed histogram, bsel
-  if constexpr (kResident) {
-    static_for<1, RD>(res_issue);
-  } else {
-#pragma unroll
-    for (int i = 1; i < D; ++i)
-      if (i < nst) rd.issue(i, i);
-  }
   {
     // lane i holds wave i's partials; the same combination order in every wave
     const bool act = lane < kWaves;
@@ -628,6 +609,15 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     info.cnt[w] = pcnt;
   }
   __syncthreads();  // pools and per-wave results complete
+  // the draw's random input: vector loads (a lane-varying address of the same
+  // element), so that waits for LDS results do not also wait for them
+  double u_in = 0.0;
+  uint64_t seed_in = 0u, off_in = 0u;
+  if (SAMPLE) {
+    const uint32_t z = __builtin_amdgcn_mbcnt_lo(0u, 0u);  // 0 in every lane
+    if (a.uniforms) u_in = a.uniforms[r + z];
+    else { seed_in = a.seed[r + z]; off_in = a.offset[r + z]; }
+  }
   // lane i of every wave reads wave i's results
   const bool act16 = lane < kWaves;
   const int pw = par;  // the per-wave pass results stay in red.v[pw]
@@ -685,22 +675,40 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     double bx = 0.0, bb = 0.0;  // background mass relative to w(t) = 1, bound
     if constexpr (DT == 1) {
       if (need_bg) {
-        for (int i = tid; i < kBgBins; i += kThreads) {
-          const uint32_t c = bgh[i];
-          if (c == 0u) continue;
-          const uint32_t side = (uint32_t)i >= kBgSide ? 1u : 0u;
-          const uint32_t j = (uint32_t)i - side * kBgSide;
-          const double cd = (double)c;
-          if (j >= 1u && j <= kBgExact) {  // one bf16 value
-            const uint32_t bits = (side << 15) | (kBgMagLo - 1u + j);
-            const double v = (double)__uint_as_float(bits << 16);
-            bx += cd * exp64((v - tv) * invT);
-          } else if (j == 0u) {            // |z| < 2^-12
-            const double e = 0.000244140625;
-            bx += cd * exp64(-tv * invT);
-            bb += cd * (exp64((e - tv) * invT) - exp64((-e - tv) * invT));
-          } else {                         // |z| >= 512 (and infinities, NaN)
-            bb += cd * (side ? exp64((-512.0 - tv) * invT) : 1.0);
+        // exact bins in runs of 8 magnitudes: one binade, equal spacing d, so
+        // the weights of a run are w0, w0 rho, ..., w0 rho^7 with
+        // rho = exp(+-d / T) (Horner over the counts)
+        constexpr int kRunsPerSide = (int)kBgExact / 8;
+        static_assert(kBgExact % 8 == 0 && (kBgMagLo & 127u) == 0u, "runs stay in one binade");
+        if (tid < 2 * kRunsPerSide) {
+          const uint32_t side = tid >= kRunsPerSide ? 1u : 0u;
+          const uint32_t j0 = 1u + 8u * ((uint32_t)tid - side * (uint32_t)kRunsPerSide);
+          const uint32_t* const hb = bgh + side * kBgSide + j0;
+          uint32_t c[8], any = 0u;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { c[i] = hb[i]; any |= c[i]; }
+          if (any) {
+            const uint32_t mag0 = kBgMagLo - 1u + j0;
+            const double v0 = (double)__uint_as_float(((side << 15) | mag0) << 16);
+            const double d = ldexp(1.0, (int)(mag0 >> 7) - 134);  // 2^(e - 127 - 7)
+            const double rho = exp64((side ? -d : d) * invT);
+            double h = (double)c[7];
+#pragma unroll
+            for (int i = 6; i >= 0; --i) h = fma(h, rho, (double)c[i]);
+            bx = h * exp64((v0 - tv) * invT);
+          }
+        } else if (tid < 2 * kRunsPerSide + 4) {  // the lumps
+          const uint32_t q = (uint32_t)(tid - 2 * kRunsPerSide);
+          const uint32_t side = q >> 1;
+          const double cd = (double)bgh[side * kBgSide + ((q & 1u) ? kBgExact + 1u : 0u)];
+          if (cd > 0.0) {
+            if ((q & 1u) == 0u) {   // |z| < 2^-12
+              const double e = 0.000244140625;
+              bx = cd * exp64(-tv * invT);
+              bb = cd * (exp64((e - tv) * invT) - exp64((-e - tv) * invT));
+            } else {                // |z| >= 512 (and infinities, NaN)
+              bb = cd * (side ? exp64((-512.0 - tv) * invT) : 1.0);
+            }
           }
         }
       }
@@ -1332,8 +1340,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   double u = 0.0;
   const bool sampled = SAMPLE && !greedy;
   if (sampled) {
-    if (a.uniforms) u = a.uniforms[r];
-    else u = (double)philox_u24(a.seed[r], a.offset[r]) * (1.0 / 16777216.0);
+    if (a.uniforms) u = u_in;
+    else u = (double)philox_u24(seed_in, off_in) * (1.0 / 16777216.0);
   }
   u = uni(u);
   // lane i of every wave handles wave i: exclusive prefixes of ties (the
@@ -1347,14 +1355,14 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     const uint32_t t = act ? info.ties[lane] : 0u;
     const uint32_t g = act ? info.gt[lane] : 0u;
     const double mg = act ? info.mass[lane] : 0.0;
-    const uint32_t tb = wave_incl_u32(t, lane) - t;
+    const uint32_t tb = scan_incl_u32(t) - t;
     const uint32_t avail = n_keep > tb ? n_keep - tb : 0u;
     const uint32_t kt = t < avail ? t : avail;
     const uint32_t kept = g + kt;
     const double mw = mg + (double)kt * w_star;
-    const uint32_t kincl = wave_incl_u32(kept, lane);
-    double mex;
-    const double mincl = wave_incl_f64(mw, lane, mex);
+    const uint32_t kincl = scan_incl_u32(kept);
+    const double mincl = scan_incl_f64(mw);
+    const double mex = incl_shift1_f64(mincl);  // the lane below's inclusive sum
     const int wu = uni(w);
     my_off = readlane_u32(kincl - kept, wu);
     my_kt = readlane_u32(kt, wu);
@@ -1425,19 +1433,24 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       gb |= ((v && key[j] > pstar) ? 1u : 0u) << j;
     }
     // ties keep their rank order: the first my_kt ties of this wave are kept
-    uint32_t ttot;
-    uint32_t trank = ties_seen + wave_excl_small((uint32_t)__popc(tb), ttot);
     uint32_t pb = gb;
+    if (ballot(tb != 0u)) {
+      const uint32_t tc = (uint32_t)__popc(tb);
+      const uint32_t tincl = scan_incl_u32(tc);
+      uint32_t trank = ties_seen + tincl - tc;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((tb >> j) & 1u) {
-        if (trank < my_kt) pb |= 1u << j;
-        ++trank;
+      for (int j = 0; j < 8; ++j) {
+        if ((tb >> j) & 1u) {
+          if (trank < my_kt) pb |= 1u << j;
+          ++trank;
+        }
       }
+      ties_seen += readlane_u32(tincl, 63);
     }
-    ties_seen += ttot;
-    uint32_t total;
-    uint32_t pos = pos_base + wave_excl_small((uint32_t)__popc(pb), total);
+    const uint32_t pc = (uint32_t)__popc(pb);
+    const uint32_t pincl = scan_incl_u32(pc);
+    const uint32_t total = readlane_u32(pincl, 63);
+    uint32_t pos = pos_base + pincl - pc;
     double qv[8];
     double lane_sum = 0.0;
     int mwi = -1;
@@ -1467,8 +1480,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     if (mwi >= 0 && mask_row) or_mask_word(mwi, mword);
     pos_base += total;
     if (w == sw && my_token < 0) {
-      const double incl = wave_incl_scan_f64(lane_sum, lane);
-      const double wtotal = __shfl(incl, 63, 64);
+      const double incl = scan_incl_f64(lane_sum);
+      const double wtotal = readlane_f64(incl, 63);
       double c = cbase + (incl - lane_sum);
       int hit = -1;
 #pragma unroll

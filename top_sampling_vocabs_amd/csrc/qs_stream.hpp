@@ -251,18 +251,21 @@ __device__ __forceinline__ uint32_t append_pool(uint32_t cb, const Raw<DT>& raw,
   if (!ballot(c > 1u)) {  // at most one candidate per lane: one ballot
     excl = count_below(any);
     total = (uint32_t)__popcll(any);
-  } else {
-    excl = wave_excl_small(c, total);
+  } else {                // DPP prefix of the per-lane counts
+    const uint32_t incl = scan_incl_u32(c);
+    excl = incl - c;
+    total = readlane_u32(incl, 63);
   }
+  // entries past the capacity overwrite the last slot: an overflowing pool is
+  // never read (the row takes the full-row path)
   uint32_t pos = pool_cnt + excl;
   while (ballot(cb != 0u)) {
     if (cb) {
       const uint32_t j = (uint32_t)__builtin_ctz(cb);
       cb &= cb - 1u;
-      if (pos < kCap) {
-        pk[pos] = (KeyT)raw_of<DT>(raw, j);
-        pid[pos] = (uint16_t)(e_local + j);
-      }
+      const uint32_t q = min(pos, kCap - 1u);
+      pk[q] = (KeyT)raw_of<DT>(raw, j);
+      pid[q] = (uint16_t)(e_local + j);
       ++pos;
     }
   }
@@ -288,53 +291,6 @@ __device__ __forceinline__ uint32_t raw_of(const Raw<DT>& raw, uint32_t j) {
     uint32_t cd = (j & 2u) ? d : c;
     return (j & 4u) ? cd : ab;
   }
-}
-
-// Candidate extraction: lane holds candidate bits cb (bit j = token e + j) and
-// the raw bits of its 8 tokens; append them, in id order, to this wave's pool
-// at pool_cnt (entries past the capacity are counted, not stored). Also keeps
-// the largest key seen (pmax) and, with HIST, counts every candidate in the
-// per-key histogram hist[key - hist_lo] (keys past the last bin set hover).
-// Returns the new count (every lane gets the same value).
-template <int DT, bool HIST>
-__device__ __forceinline__ uint32_t append_candidates(
-    uint32_t cb, const Raw<DT>& raw, uint32_t e_local, uint32_t pool_cnt,
-    typename PoolLayout<DT>::KeyT* pk, uint16_t* pid, uint32_t& pmax,
-    uint32_t* hist, uint32_t hist_lo, uint32_t hist_bins, uint32_t& hover) {
-  using KeyT = typename PoolLayout<DT>::KeyT;
-  using K = Keys<DT>;
-  constexpr uint32_t kCap = (uint32_t)PoolLayout<DT>::kPerWave;
-  const uint32_t c = (uint32_t)__popc(cb);
-  const uint64_t any = ballot(c != 0u);
-  if (!any) return pool_cnt;
-  uint32_t excl, total;
-  if (!ballot(c > 1u)) {  // at most one candidate per lane: one ballot
-    excl = count_below(any);
-    total = (uint32_t)__popcll(any);
-  } else {
-    excl = wave_excl_small(c, total);
-  }
-  uint32_t pos = pool_cnt + excl;
-  while (ballot(cb != 0u)) {
-    if (cb) {
-      const uint32_t j = (uint32_t)__builtin_ctz(cb);
-      cb &= cb - 1u;
-      const uint32_t rb = raw_of<DT>(raw, j);
-      if (pos < kCap) {
-        pk[pos] = (KeyT)rb;
-        pid[pos] = (uint16_t)(e_local + j);
-      }
-      const uint32_t key = K::of(rb);
-      pmax = key > pmax ? key : pmax;
-      if constexpr (HIST) {
-        const uint32_t b = key - hist_lo;
-        if (b < hist_bins) atomicAdd(hist + b, 1u);
-        else hover = 1u;
-      }
-      ++pos;
-    }
-  }
-  return pool_cnt + total;
 }
 
 }  // namespace qs
