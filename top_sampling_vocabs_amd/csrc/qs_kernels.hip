@@ -148,7 +148,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint4 lut[DT == 1 ? 256 : 1];
   __shared__ uint32_t hist[kHB];
   __shared__ double binw[kHB];
-  __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins : 4];
+  // the background histogram plus one dump bin per lane (excluded tokens)
+  __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
   __shared__ struct {
     uint32_t cnt[kWaves];
@@ -490,7 +491,11 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
                                    __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
       if (need_bg) {  // count the legal tokens below t in the background histogram
-        const uint32_t nbm = mb & ~cb;
+        // excluded tokens (illegal, or candidates) go to this lane's dump bin:
+        // no branch per token
+        const uint4 nb4 = lut[mb & ~cb];
+        const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
+        const uint32_t dump2 = (uint32_t)(kBgBins + lane) * 0x10001u;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t d = raw.r[q];
@@ -498,12 +503,11 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
               as_u2(d & 0x7FFF7FFFu), as_u2((kBgMagLo - 1u) * 0x10001u)));
           bi = bits_of(__builtin_elementwise_min(as_u2(bi), as_u2((kBgExact + 1u) * 0x10001u)));
           bi += ((d >> 15) & 0x00010001u) * kBgSide;
-          if ((nbm >> (2 * q)) & 1u)
-            __hip_atomic_fetch_add(bgh + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-          if ((nbm >> (2 * q + 1)) & 1u)
-            __hip_atomic_fetch_add(bgh + (bi >> 16), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+          bi = bfi(nb[q], bi, dump2);
+          __hip_atomic_fetch_add(bgh + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(bgh + (bi >> 16), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
     } else {
