@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time K eager launches instead of one replay of a HIP graph "
                          "holding the K launches")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the headline line, print one line timing the path "
+                         "switches (the Qrita page's ablation runs) on the headline "
+                         "workload and at the page's ablation shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, also run plain device copies of the "
                          "logits (known bytes) so counter runs can scale FETCH/WRITE sizes")
@@ -98,8 +102,14 @@ class Prepared:
             P(self.status.data_ptr()), None, flags, stream)
         self.lib = lib
 
-    def call(self, stream=None):
-        args = self.args if stream is None else self.args[:-1] + (stream,)
+    def call(self, stream=None, flags=None, debug=None):
+        args = self.args
+        if flags is not None:
+            args = args[:-2] + (flags, args[-1])
+        if debug is not None:
+            args = args[:-3] + (ctypes.c_void_p(debug.data_ptr()),) + args[-2:]
+        if stream is not None:
+            args = args[:-1] + (stream,)
         rc = self.lib.qs_sample(*args)
         if rc != 0:
             raise RuntimeError(f"qs_sample returned {rc}")
@@ -162,6 +172,90 @@ def copy_calibration(preps, reps=20):
             "gbs_rw": round(2 * nbytes / (ms / 1e3) / 1e9, 1)}
 
 
+def time_graph(preps, K, flags=None):
+    """Capture K launches (input sets in rotation) in one HIP graph on a side
+    stream, replay it once untimed, then time one replay between two events on
+    that stream. Returns (total ms, graph, capture stream)."""
+    import torch
+    cs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(K):
+                preps[i % len(preps)].call(sp, flags=flags)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        a.record(cs)
+        graph.replay()
+        b.record(cs)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b), graph, cs
+
+
+# Path switches of the library and the Qrita page's ablation runs they mirror
+# (its runs C, I and J drop duplicate handling, sort the candidates, or sort
+# the full row: not paths of this library).
+ABLATION_RUNS = [
+    ("A", "full path: truncation hit, histogram scan (bf16) / quaternary search (fp32)", 0),
+    ("B", "single streamed tier instead of the register tiers", 8),
+    ("D", "forced fallback: quaternary searches over the full row", 1),
+    ("E", "no truncation: quaternary searches over the full row", 2),
+    ("F", "truncation hit, binary pivot (one pivot per round)", 16 | 4),
+    ("G", "forced fallback, binary pivot", 16 | 1),
+    ("Q", "truncation hit, quaternary search on bf16 pools instead of the histogram scan", 4),
+]
+
+
+def ablation(args, lib, stream):
+    """Time every path switch on the headline workload and at the page's
+    ablation shape; every switch gives identical outputs (the path-invariance
+    test), so only time, search rounds and fallback rows differ."""
+    import torch
+    out = []
+    for name in ("headline", "pages_ablation_shape"):
+        if name == "headline":
+            sets = [workloads.make(args.workload, seed=workloads.BASE_SEED + args.workload + 1000 * i)
+                    for i in range(args.sets)]
+        else:
+            sets = [workloads.make_ablation(seed=workloads.BASE_SEED + 100 + 1000 * i)
+                    for i in range(args.sets)]
+        preps = [Prepared(lib, w, args.cand_cap, 0, stream) for w in sets]
+        nbytes = workloads.bytes_read(sets[0])
+        B = sets[0].B
+        dbg = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+        for run, what, flags in ABLATION_RUNS:
+            for i in range(args.warmup):
+                preps[i % len(preps)].call(flags=flags)
+            preps[0].call(flags=flags, debug=dbg)
+            torch.cuda.synchronize()
+            d = dbg.cpu().numpy()
+            st = preps[0].status.cpu().numpy()
+            ok = st == 0
+            total_ms, _, _ = time_graph(preps, args.steps, flags=flags)
+            ms = total_ms / args.steps
+            out.append({"workload": name, "run": run, "what": what, "flags": flags,
+                        "ms_per_step": round(ms, 5),
+                        "rows_per_s": round(B / (ms / 1e3), 1),
+                        "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+                        "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "fallback_rows": int((d[ok, 0] == 1).sum()),
+                        "rounds_mean": round(float(d[ok, 1].mean()), 3) if ok.any() else None,
+                        "rounds_max": int(d[ok, 1].max()) if ok.any() else None})
+            print(f"# {name} run {run}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        del preps
+        torch.cuda.empty_cache()
+    line = {"ablation": out, "steps": args.steps, "warmup": args.warmup,
+            "input_sets": args.sets, "launch": "hip_graph",
+            "shapes": {"headline": WORKLOAD_NAMES[args.workload],
+                       "pages_ablation_shape": "B=1024 V=128256 fp32 N(0,2^2), k=50, p=0.9, T=1"}}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(w, rows):
     import oracle
     t0 = time.perf_counter()
@@ -182,6 +276,9 @@ def main():
     import top_sampling_vocabs_amd as qs
     lib = qs.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.ablation:
+        ablation(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        return
     cfg = args.workload
     base = workloads.make(cfg)
     sets = [base] + [workloads.make(cfg, seed=workloads.BASE_SEED + cfg + 1000 * i)
@@ -220,9 +317,8 @@ def main():
     else:
         # The K launches (input sets in rotation) captured in one HIP graph on
         # a side stream; one untimed replay, then the timed replay between two
-        # events on that stream. The replayed outputs are checked against the
-        # same K launches run eagerly (Philox offsets restarted for both).
-        cs = torch.cuda.Stream()
+        # events on that stream. A further replay from restarted Philox offsets
+        # is checked against the same K launches run eagerly.
         for p_ in preps:
             p_.offset.zero_()
         torch.cuda.synchronize()
@@ -230,13 +326,12 @@ def main():
             preps[i % n_sets].call()
         torch.cuda.synchronize()
         eager_out = [p_.outputs() for p_ in preps]
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cs):
-            with torch.cuda.graph(graph, stream=cs):
-                sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-                for i in range(K):
-                    preps[i % n_sets].call(sp)
+        for p_ in preps:
+            p_.offset.zero_()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        total_ms, graph, cs = time_graph(preps, K)
+        wall = time.perf_counter() - t0
         for p_ in preps:
             p_.offset.zero_()
         torch.cuda.synchronize()
@@ -246,17 +341,6 @@ def main():
         for p_, ref in zip(preps, eager_out):
             for a_, b_ in zip(p_.outputs(), ref):
                 assert torch.equal(a_, b_), "graph replay differs from eager launches"
-        start_all = torch.cuda.Event(enable_timing=True)
-        end_all = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(cs):
-            start_all.record(cs)
-            graph.replay()
-            end_all.record(cs)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        total_ms = start_all.elapsed_time(end_all)
         per = np.full(K, total_ms / K)
         launch_mode = "hip_graph"
     ms_step = total_ms / K

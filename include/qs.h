@@ -83,6 +83,8 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
                                       (instead of the histogram scan)           */
 #define QS_FLAG_STREAM         8u  /* stream the row even when it fits in
                                       registers                                 */
+#define QS_FLAG_BINARY_PIVOT  16u  /* one pivot per search round (the interval's
+                                      midpoint) instead of three (ablation)     */
 
 /* Filter a batch: kept-candidate mask and renormalised probabilities.
  *

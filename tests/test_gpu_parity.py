@@ -117,11 +117,14 @@ def test_path_invariance(qs):
     """Forced fallback and no truncation run every search over the full row; the
     pivot-search switch replaces the histogram scan by the quaternary search;
     the stream switch reads the row through the prefetch ring instead of the
-    register-resident pass. Every variant gives bitwise identical outputs (page
-    "Qrita" ablation runs D and E compute the same result as run A)."""
+    register-resident pass; the binary-pivot switch searches with one pivot per
+    round. Every variant gives bitwise identical outputs (page "Qrita" ablation
+    runs D to G compute the same result as run A)."""
     import torch
     variants = (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION, qs.FLAG_PIVOT_SEARCH,
-                qs.FLAG_STREAM, qs.FLAG_STREAM | qs.FLAG_PIVOT_SEARCH)
+                qs.FLAG_STREAM, qs.FLAG_STREAM | qs.FLAG_PIVOT_SEARCH,
+                qs.FLAG_BINARY_PIVOT | qs.FLAG_PIVOT_SEARCH,
+                qs.FLAG_BINARY_PIVOT | qs.FLAG_FORCE_MISS)
     for cfg in (1, 2, 3, 5):
         w = workloads.make(cfg, **SMALL[cfg])
         d = to_device(w)
@@ -135,8 +138,14 @@ def test_path_invariance(qs):
             assert lists_equal(base, alt), (cfg, flags)
             dbg = alt["debug"].cpu().numpy()
             ok = base["status"].cpu().numpy() == 0
-            if flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION):
+            if flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION,
+                         qs.FLAG_BINARY_PIVOT | qs.FLAG_FORCE_MISS):
                 assert (dbg[ok, 0] == 1).all()  # every OK row took the full-row path
+            if flags == qs.FLAG_BINARY_PIVOT | qs.FLAG_FORCE_MISS:
+                # one pivot per round never needs fewer rounds than three
+                quad = run_all(qs, d, uniforms=uni, flags=qs.FLAG_FORCE_MISS, V=w.V)
+                qr = quad["debug"].cpu().numpy()[ok, 1]
+                assert (dbg[ok, 1] >= qr).all(), (cfg, dbg[ok, 1], qr)
 
 
 def lists_equal(a, b):

@@ -31,6 +31,7 @@ FLAG_FORCE_MISS = 1
 FLAG_NO_TRUNCATION = 2
 FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
+FLAG_BINARY_PIVOT = 16
 
 EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_version")
 

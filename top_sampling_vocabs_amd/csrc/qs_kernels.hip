@@ -1091,6 +1091,11 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     return block_sum_f64(s);
   };
 
+  // ablation switch: one pivot per round (the midpoint of the key interval)
+  // instead of three at its quarters (page "Qrita", ablation table, binary
+  // pivot runs); the stop tests are unchanged, only the round count grows
+  const bool binary_pivot = (a.flags & QS_FLAG_BINARY_PIVOT) != 0u;
+
   // -- the k-th largest key (top-k) ----------------------------------------------
   if (topk_eff && !settled) {
     // quaternary three-pivot search on counts (page "Qrita", key design 2)
@@ -1102,8 +1107,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       uint32_t tau[3];
 #pragma unroll
       for (int n = 0; n < 3; ++n)
-        tau[n] = d >= 4u ? lo + (uint32_t)(((uint64_t)d * (uint64_t)(n + 1)) >> 2)
-                         : min(lo + (uint32_t)n, hi - 1u);
+        tau[n] = binary_pivot ? lo + (d >> 1)
+                 : d >= 4u    ? lo + (uint32_t)(((uint64_t)d * (uint64_t)(n + 1)) >> 2)
+                              : min(lo + (uint32_t)n, hi - 1u);
       uint32_t N[3] = {0u, 0u, 0u};
       MinCnt mc[3] = {{0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}};
       for_items([&](uint32_t x, uint32_t c) {
@@ -1192,8 +1198,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           uint32_t tau[3];
 #pragma unroll
           for (int n = 0; n < 3; ++n)
-            tau[n] = d >= 4u ? lo + (uint32_t)(((uint64_t)d * (uint64_t)(n + 1)) >> 2)
-                             : min(lo + (uint32_t)n, hi - 1u);
+            tau[n] = binary_pivot ? lo + (d >> 1)
+                     : d >= 4u    ? lo + (uint32_t)(((uint64_t)d * (uint64_t)(n + 1)) >> 2)
+                                  : min(lo + (uint32_t)n, hi - 1u);
           double Ms[3] = {0.0, 0.0, 0.0};
           MinCnt mc[3] = {{0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}, {0xFFFFFFFFu, 0u}};
           for_items([&](uint32_t x, uint32_t c) {

@@ -178,6 +178,27 @@ def make(cfg, B=None, V=None, seed=None):
                     offsets=np.zeros(B, np.uint64))
 
 
+# Shape of the ablation table on the Qrita page (B=1024, V=128256, k=50, p=0.9).
+ABLATION_SHAPE = (1024, 128256)
+
+
+def make_ablation(B=None, V=None, seed=None):
+    """Inputs at the shape of the Qrita page's ablation table: B=1024,
+    V=128256 (that page's first model's vocabulary), top-k 50, top-p 0.9,
+    T = 1, no bitmask. The page does not describe its logits; fp32 N(0, 2^2)
+    i.i.d. values stand in for them. Not one of the five parity workloads: it
+    only feeds bench.py --ablation."""
+    fb, fv = ABLATION_SHAPE
+    B = fb if B is None else int(B)
+    V = fv if V is None else int(V)
+    rng = np.random.default_rng(BASE_SEED + 100 if seed is None else seed)
+    logits = np.float32(2.0) * rng.standard_normal((B, V), dtype=np.float32)
+    return Workload(cfg=0, dtype="f32", logits=np.ascontiguousarray(logits),
+                    T=np.ones(B, np.float32), k=np.full(B, 50, np.int32),
+                    p=np.full(B, 0.9, np.float32), bitmask=None, seeds=_seeds(0, B),
+                    offsets=np.zeros(B, np.uint64))
+
+
 def bytes_read(w):
     """Algorithmic bytes one filter+sample pass must read: the logits once, the
     bitmask once, and the per-row parameters (T, k, p: 4 B each; seed, offset:
