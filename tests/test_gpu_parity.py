@@ -359,3 +359,43 @@ def test_parity_full_size(qs, cfg, rows):
         kinds = np.arange(w.B) % 3
         assert (dbg[kinds == 0, 0] == 0).mean() > 0.9
         assert dbg[:, 1].max() <= 2 * 17
+
+
+def test_topp_background_extremes(qs):
+    """Rows with top-k off whose background (legal tokens below the truncation
+    threshold) lies outside the exact bf16 value bins: values of magnitude
+    >= 512 or below 2^-12, exact zeros, legal -inf, +inf, and very large or
+    very small temperatures. Their mass test and top-p cut go through the error
+    bound and, where it is too wide, the exact fp64 walk or the full row; every
+    output must still match the oracle."""
+    rng = np.random.default_rng(77)
+    B, V = 14, 9000
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    T = np.ones(B, np.float32)
+    p = np.full(B, 0.9, np.float32)
+    z[0] += 1000.0                      # background >= 512 above zero
+    z[1] -= 1000.0                      # background <= -512
+    z[2] *= 1e-4                        # most values below 2^-12
+    z[3, rng.random(V) < 0.5] = 0.0     # exact zeros
+    z[4, rng.random(V) < 0.2] = -np.inf # legal -inf
+    z[5, 17] = np.inf                   # +inf at a legal position
+    T[6] = 50.0                         # nearly flat weights
+    T[7] = 0.05                         # sharply peaked weights
+    p[8], p[9], p[10] = 0.999, 0.01, 0.5
+    z[11, :40] = 600.0                  # ties far above the rest
+    z[12] = np.where(rng.random(V) < 0.5, 600.0, -600.0)
+    T[13], z[13] = 0.5, z[13] * 1e-3    # tiny values, small temperature
+    bits = workloads._random_bitmask(rng, B, V, 0.3)
+    bits[5, 17] = True
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=np.zeros(B, np.int32), p=p,
+                           bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rep, out = check_workload(qs, w, seed=5)
+    st = out["status"].cpu().numpy()
+    assert st[5] == oracle.ROW_NONFINITE
+    dbg = out["debug"].cpu().numpy()
+    # candidate keys spanning more than the 1024-key histogram: some rows are
+    # settled by pivot rounds on the pool (more rounds than the two scans)
+    assert (dbg[:, 1] >= 3).any(), dbg.tolist()
