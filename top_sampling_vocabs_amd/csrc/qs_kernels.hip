@@ -339,9 +339,13 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
 
 
-  // the rest of the ring: requested once this wave's sample has returned
+  // the next ring steps: requested once this wave's sample has returned. A
+  // resident ring requests only its first steps before the sample barrier and
+  // the rest after it, so that the other waves' samples are not queued behind
+  // a full flood
+  constexpr int kEarly = RD < 4 ? RD : 4;
   if constexpr (kResident) {
-    static_for<1, RD>(res_issue);
+    static_for<1, kEarly>(res_issue);
   } else {
 #pragma unroll
     for (int i = 1; i < D; ++i)
@@ -349,10 +353,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
 
   // -- the row's threshold ------------------------------------------------------------
-  // The 16 step-0 samples (8192 tokens) are combined after one barrier. Each
-  // wave requests the rest of its ring as soon as its own sample has returned
-  // (every sample was requested first, alone), so the threshold is computed
-  // while the ring fills.
+  // The 16 step-0 samples (8192 tokens) are combined after one barrier; the
+  // ring keeps filling meanwhile, so the threshold is computed while data
+  // arrives.
   {
     const double st0 = wave_sum_f64(s_n), st1 = wave_sum_f64(s_sum);
     const double st2 = wave_sum_f64(s_sq), st3 = wave_sum_f64(s_all);
@@ -369,6 +372,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     }
   }
   __syncthreads();  // sample partials, the zeroed histogram, bsel
+  if constexpr (kResident) static_for<kEarly, RD>(res_issue);
   {
     // lane i holds wave i's partials; the same combination order in every wave
     const bool act = lane < kWaves;
