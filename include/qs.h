@@ -105,7 +105,9 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
  * row_status   [B] int32 out, required (qs_row_status)
  * debug_stats  [B][4] int32 out, optional: {path (0 candidate pool, 1 full
  *              row), search rounds, |Z_t| (candidates above the truncation
- *              threshold), |P|}
+ *              threshold), |P|}; bf16 rows settled by the value histogram
+ *              report path 0 with 0 rounds and |Z_t| = the tokens at or above
+ *              the final boundary value
  * flags        QS_FLAG_* bits, 0 normally
  */
 QS_API int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V,

@@ -67,11 +67,13 @@ constexpr int kBgBins = 2 * (int)kBgSide;
 static_assert(kBgMagLo + kBgExact == 0x4400u, "the upper lump starts at 512");
 // Register-resident tiers (steps of 512 tokens per wave slice), per dtype:
 // fp32 rows take two 16-byte loads per step, bf16 rows one.
-constexpr int kResidentTier[2][2] = {{5, 10}, {5, 20}};
+constexpr int kResidentTier[2][2] = {{5, 10}, {5, 19}};
 // Register ring depth (steps in flight per wave) of those tiers.
 constexpr int kRingDepth[2] = {5, 10};
 constexpr int kStageWords = 320;      // packed-mask words of one slice held in LDS
 static_assert(kResidentMaxSteps * (kStep / 32) <= kStageWords, "stage holds a resident slice");
+
+#include "qs_select.hpp"
 
 // Relative error bound of one hardware exp2 (v_exp_f32), taken as 4 ulp.
 constexpr double kExp2Err = 2.384185791015625e-07;  // 2^-22
@@ -151,17 +153,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // the background histogram plus one dump bin per lane (excluded tokens)
   __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
-  __shared__ struct {
-    uint32_t cnt[kWaves];
-    uint32_t gt[kWaves];
-    uint32_t ties[kWaves];
-    double mass[kWaves];
-    int32_t bsel;
-    uint32_t sel_u[2];
-    double sel_d[2];
-    uint32_t sc_u[8];   // single-wave scan results
-    double sc_d[2];
-  } info;
+  __shared__ RowInfo info;
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
   uint16_t* const pool_id = reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap);
@@ -215,6 +207,19 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       }
     }
   };
+
+  // -- bf16 rows held in registers: the value-histogram path ---------------------
+  // (rows it cannot settle exactly, and the path switches, take the general
+  // path below)
+  if constexpr (DT == 1 && kResident) {
+    if (a.flags == 0u) {
+      if (select_row<SAMPLE, NL>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
+                                 pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
+                                 info))
+        return;
+      __syncthreads();  // the general path reuses the LDS
+    }
+  }
 
   // -- the sample: step 0 of every slice ----------------------------------------
   // The first 512 tokens of each of the 16 slices (8192 tokens) are the only

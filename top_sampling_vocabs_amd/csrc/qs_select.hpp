@@ -1,0 +1,661 @@
+// Value-histogram path of the filter/sample kernel for bf16 rows held in
+// registers.
+//
+// The kept set is the one a full stable sort by (-z, id) gives (page "Qrita",
+// key design 3). Here it is found without a sort, a truncation threshold or a
+// pivot search:
+//  1. the whole slice is requested at once and stays in VGPRs; every legal
+//     token is counted, as its step arrives, in an LDS histogram with one bin
+//     per bf16 value of magnitude in [2^-24, 512) and sign;
+//  2. block-wide prefix sums over the bins, in descending value order, of the
+//     counts and of the fp64 masses exp((v - m) / T) give the k-th largest
+//     value with its tie quota (the page's stop test, evaluated at every value
+//     at once) and then the value at which the descending mass of the top-k
+//     set reaches p W_K, with the count of its ties that is needed;
+//  3. one walk over the registers appends the tokens at or above that value to
+//     the wave's id-ordered pool; the tie walk, the 16-wave prefix and the
+//     output walk then write the mask, the id-ordered lists and the token.
+// A row this path cannot settle exactly returns false and takes the general
+// path: greedy rows, legal values outside the bins (magnitude >= 512 or below
+// 2^-24, infinities, NaN), a boundary at or below zero, a weight table or a
+// pool that would not fit.
+// Included by the kernels' translation unit inside namespace qs, after its
+// packed 16-bit helpers.
+#pragma once
+
+// Per-row scalars shared through LDS by the general and the histogram paths.
+struct RowInfo {
+  uint32_t cnt[kWaves];
+  uint32_t gt[kWaves];
+  uint32_t ties[kWaves];
+  double mass[kWaves];
+  int32_t bsel;
+  uint32_t sel_u[2];
+  double sel_d[2];
+  uint32_t sc_u[8];   // single-wave scan results
+  double sc_d[2];
+  uint64_t claim;      // (rank << 32 | ties needed) of the top-p boundary, min wins
+};
+
+namespace sel {
+constexpr uint32_t kMagLo = 0x3380u;            // magnitude bits of 2^-24
+constexpr uint32_t kExact = 33u * 128u;         // exact bins per sign: 33 binades
+constexpr uint32_t kTop = 16u + kExact;         // bin of the magnitudes >= 512 (and inf, NaN)
+constexpr uint32_t kSide = 4256u;               // bins per sign, a multiple of 16
+constexpr int kBins = 2 * (int)kSide;           // 8512 bins
+constexpr int kRho = 2 * (int)kExact;           // exact values in descending order
+constexpr int kRuns = kRho / 16;                // 528 runs of 16 consecutive values
+constexpr int kTab = 2048;                      // weights from the maximum to the boundary
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+static_assert(kMagLo + kExact == 0x4400u, "the exact bins end at 512");
+static_assert((kMagLo & 127u) == 0u && kSide % 16u == 0u, "runs of 16 stay in one binade");
+
+// Value rank rho (0 = the largest exact value) of exact bin j of a side:
+// positive j = 16 .. kTop-1 -> rho = kTop-1-j; negative -> kExact + j - 16.
+// A run of 16 ranks starting at 16 t covers one aligned group of 16 bins.
+__device__ __forceinline__ uint32_t run_bin0(int t) {
+  return t < (int)(kExact / 16) ? kTop - 16u - 16u * (uint32_t)t
+                                : kSide + 16u + 16u * (uint32_t)(t - (int)(kExact / 16));
+}
+// bf16 magnitude bits of rank rho, and its sign
+__device__ __forceinline__ uint32_t rho_mag(uint32_t rho) {
+  return rho < kExact ? kMagLo + kExact - 1u - rho : kMagLo + (rho - kExact);
+}
+__device__ __forceinline__ double rho_value(uint32_t rho) {
+  const uint32_t bits = rho_mag(rho) | (rho < kExact ? 0u : 0x8000u);
+  return (double)__uint_as_float(bits << 16);
+}
+}  // namespace sel
+
+template <bool SAMPLE, int NL>
+__device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl, int r, int w,
+                                           int lane, int tid, int W, const uint32_t* bmrow,
+                                           uint32_t* mask_row, float* dense_row,
+                                           uint8_t* pool_raw, uint32_t (*stage)[kStageWords],
+                                           uint4* lut, double* wtab, RedScratch& red,
+                                           RowInfo& info) {
+  using K = Keys<1>;
+  using PKey = typename PoolLayout<1>::KeyT;
+  constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
+  constexpr int kMW = NL * (kStep / 32);
+  constexpr int kML = (kMW + 63) / 64;
+  int par = 0;
+
+  // -- requests: the slice's mask words, then every step of the slice ----------------
+  const int last_piece = sl.we > sl.wb ? (sl.we - 1) & ~7 : 0;
+  const int lane_e = sl.wb + lane * kChunk;
+  uint32_t mw[kML];
+  {
+    const uint32_t* const mwsrc = bmrow ? bmrow : reinterpret_cast<const uint32_t*>(sl.row);
+    const int w0 = sl.wb >> 5;
+    const int wlim = bmrow ? min(W, (sl.we + 31) >> 5) : 0;
+#pragma unroll
+    for (int i = 0; i < kML; ++i) {
+      const int wi = w0 + lane + 64 * i;
+      const bool in = lane + 64 * i < kMW && wi < wlim;
+      const uint32_t v = mwsrc[in ? wi : 0];
+      mw[i] = in ? v : 0u;
+    }
+  }
+  // every step of the slice gets its own registers. The first kEarly steps are
+  // requested now, the rest of the first kLook after the table barrier, and
+  // step st + kLook once step st has been counted, so that the requests never
+  // stall the wave for long
+  constexpr int kLook = NL < 10 ? NL : 10;
+  constexpr int kEarly = kLook < 4 ? kLook : 4;
+  uint4 xs[NL];
+  auto issue = [&](auto stc) {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (st < NL) {
+      const int ep = min(lane_e + st * kStep, last_piece);
+      xs[st] = *reinterpret_cast<const uint4*>(chunk_ptr<1>(sl.row, ep));
+    }
+  };
+  static_for<0, kEarly>(issue);
+
+  // -- tables: legal pair masks, the cleared histogram, this slice's mask words ------
+  uint32_t* const hist = reinterpret_cast<uint32_t*>(pool_raw);  // kBins + 64 dump bins
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const uint32_t e = (uint32_t)(lane + 64 * q4);
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (((e >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
+             (((e >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+    lut[e] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  {
+    uint4* const h4 = reinterpret_cast<uint4*>(hist);
+    for (int i = tid; i < sel::kBins / 4; i += kThreads) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid == 0) info.claim = ~0ull;
+  __syncthreads();  // cleared histogram
+  static_for<kEarly, kLook>(issue);
+
+  // -- the pass: count every legal token in its value bin ------------------------------
+  // legal bits of step st: byte (lane & 3) of slice word 16 st + lane / 4, held
+  // by lane (st & 3) * 16 + lane / 4 in mw[st / 4]
+  auto legal_bits = [&](int st) -> uint32_t {
+    uint32_t m8 = 0xFFu;
+    if (bmrow) {
+      const uint32_t wd = (uint32_t)__shfl((int)mw[st >> 2], (st & 3) * 16 + (lane >> 2), 64);
+      m8 = (wd >> ((lane & 3) * 8)) & 0xFFu;
+    }
+    if (sl.wb + (st + 1) * kStep > sl.we) {  // a step that ends past the slice
+      const int rem = sl.we - (lane_e + st * kStep);
+      m8 &= rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u);
+    }
+    return m8;
+  };
+  uint32_t n_legal = 0u;
+  const uint32_t dump2 = (uint32_t)(sel::kBins + lane) * 0x10001u;
+  static_for<0, NL>([&](auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const uint32_t mb = legal_bits(st);
+    n_legal += (uint32_t)__popc(mb);
+    issue(std::integral_constant<int, st + kLook>{});
+    const uint4 nb4 = lut[mb];
+    const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
+    const uint32_t d4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t d = d4[q];
+      uint32_t bi = bits_of(__builtin_elementwise_sub_sat(
+          as_u2(d & 0x7FFF7FFFu), as_u2((sel::kMagLo - 16u) * 0x10001u)));
+      bi = bits_of(__builtin_elementwise_min(as_u2(bi), as_u2(sel::kTop * 0x10001u)));
+      bi += ((d >> 15) & 0x00010001u) * sel::kSide;
+      bi = bfi(nb[q], bi, dump2);
+      __hip_atomic_fetch_add(hist + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(hist + (bi >> 16), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  });
+  // the mask words move to LDS for the compaction walk (frees their registers)
+  if (bmrow) {
+#pragma unroll
+    for (int i = 0; i < kML; ++i)
+      if (lane + 64 * i < kMW) stage[w][lane + 64 * i] = mw[i];
+  }
+
+  // -- parameters (only the scans below need them) -------------------------------------
+  const float Tf = a.T[r];
+  const int kk = a.k[r];
+  const float pf = a.p[r];
+  n_legal = wave_reduce<OpSum>(n_legal);
+  if (lane == 0) red.v[par][w][0] = n_legal;
+  __syncthreads();  // the histogram is complete
+  // invalid parameters and greedy rows: the general path (which reports them)
+  if (!(isfinite(Tf) && Tf > 0.0f) || kk < 0 || !(pf > 0.0f && pf <= 1.0f)) return false;
+  const double invT = 1.0 / (double)Tf;
+  const double p = (double)pf;
+  const bool topp_on = pf < 1.0f;
+  const bool act16 = lane < kWaves;
+  n_legal = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
+  par ^= 1;
+  if (n_legal == 0u) return false;  // the general path reports the empty row
+
+  // -- runs of 16 values: counts, first value, lumps -----------------------------------
+  // Thread t < kRuns owns ranks 16 t .. 16 t + 15. Its counts are read from LDS
+  // again in every phase (the row is still held in VGPRs).
+  const bool run_t = tid < sel::kRuns;
+  auto load_run = [&](uint32_t (&c)[16]) {
+    const uint4* const h4 = reinterpret_cast<const uint4*>(hist + sel::run_bin0(tid));
+    uint32_t asc[16];  // bin order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = h4[q];
+      asc[4 * q] = v.x; asc[4 * q + 1] = v.y; asc[4 * q + 2] = v.z; asc[4 * q + 3] = v.w;
+    }
+    // rank order: positive runs descend through their bins, negative runs ascend
+    const bool pos = tid < (int)(sel::kExact / 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = pos ? asc[15 - i] : asc[i];
+  };
+  // count of rank 16 tid + i (rolled loops below read it from LDS)
+  auto run_count = [&](int i) -> uint32_t {
+    const uint32_t b0 = sel::run_bin0(tid);
+    return hist[tid < (int)(sel::kExact / 16) ? b0 + 15u - (uint32_t)i : b0 + (uint32_t)i];
+  };
+  uint32_t ct = 0u, first = sel::kNone;
+  if (run_t) {
+    uint32_t c[16];
+    load_run(c);
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      ct += c[i];
+      if (c[i]) first = (uint32_t)(16 * tid + i);
+    }
+  }
+  // the lumps: magnitudes below 2^-24 (zeros among them), and >= 512 with the
+  // infinities and NaN (bins 0..15 and the top bin of each side)
+  uint32_t tiny = 0u, huge = 0u;
+  if (tid >= sel::kRuns && tid < sel::kRuns + 34) {
+    const int q = tid - sel::kRuns;
+    const uint32_t side = q >= 17 ? sel::kSide : 0u;
+    const int j = q % 17;
+    const uint32_t v = hist[side + (j < 16 ? (uint32_t)j : sel::kTop)];
+    if (j < 16) tiny = v; else huge = v;
+  }
+  {
+    const uint32_t cs = wave_reduce<OpSum>(ct);
+    const uint32_t fm = wave_reduce<OpMin>(first);
+    const uint32_t ts = wave_reduce<OpSum>(tiny);
+    const uint32_t hm = wave_reduce<OpMax>(huge);
+    if (lane == 0) {
+      red.v[par][w][0] = cs; red.v[par][w][1] = fm; red.v[par][w][2] = ts; red.v[par][w][3] = hm;
+    }
+  }
+  __syncthreads();
+  const uint32_t n_ex = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
+  const uint32_t rho_top = uni(wave_reduce<OpMin>(act16 ? red.v[par][lane][1] : sel::kNone));
+  const uint32_t n_tiny = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][2] : 0u));
+  const bool huge_any = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][3] : 0u)) != 0u;
+  par ^= 1;
+  // the tiny values lie below every positive exact value: with a positive
+  // maximum they only enter the total mass, within a bound
+  if (huge_any || n_ex + n_tiny != n_legal || rho_top >= sel::kExact) return false;
+  const uint32_t n_fin = n_legal;
+
+  // -- fp64 masses relative to the maximum, block prefix sums in rank order -------------
+  const double m = sel::rho_value(rho_top);
+  // this run's 16 values are one spacing d apart, descending: their weights
+  // are w0, w0 rh, ..., w0 rh^15 with w0 = exp((v0 - m) / T), rh = exp(-d / T)
+  auto run_w0 = [&]() { return exp64((sel::rho_value(16u * (uint32_t)tid) - m) * invT); };
+  auto run_rh = [&]() {
+    const uint32_t mag0 = sel::rho_mag(16u * (uint32_t)tid);
+    return exp64(-ldexp(1.0, (int)(mag0 >> 7) - 134) * invT);
+  };
+  double mt = 0.0;
+  if (run_t && ct) {
+    uint32_t c[16];
+    load_run(c);
+    const uint32_t rho0 = 16u * (uint32_t)tid;
+    const double w0 = run_w0();
+    const double rh = run_rh();
+    double h = (double)c[15];
+#pragma unroll
+    for (int i = 14; i >= 0; --i) h = fma(h, rh, (double)c[i]);
+    mt = w0 * h;
+    // the weight table: every rank from the maximum down, as far as it reaches
+    if (rho0 + 16u > rho_top && rho0 < rho_top + (uint32_t)sel::kTab) {
+      double wi = w0;
+#pragma unroll 1
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t rho = rho0 + (uint32_t)i;
+        if (rho >= rho_top && rho < rho_top + (uint32_t)sel::kTab) wtab[rho - rho_top] = wi;
+        wi *= rh;
+      }
+    }
+  }
+  uint32_t c_excl;
+  double m_excl, w_f;
+  {
+    const uint32_t ci = scan_incl_u32(ct);
+    const double mi = scan_incl_f64(mt);
+    if (lane == 63) {
+      red.v[par][w][0] = ci;
+      const uint64_t b = __double_as_longlong(mi);
+      red.v[par][w][1] = (uint32_t)b; red.v[par][w][2] = (uint32_t)(b >> 32);
+    }
+    __syncthreads();  // wave totals, the weight table
+    // lane i holds wave i's totals: exclusive prefix over the waves
+    const uint32_t tc = act16 ? red.v[par][lane][0] : 0u;
+    const double tm = act16 ? __longlong_as_double(((uint64_t)red.v[par][lane][2] << 32) |
+                                                   red.v[par][lane][1])
+                            : 0.0;
+    const uint32_t tci = scan_incl_u32(tc);
+    const double tmi = scan_incl_f64(tm);
+    const double tme = incl_shift1_f64(tmi);
+    const int wu = uni(w);
+    c_excl = readlane_u32(tci - tc, wu) + ci - ct;
+    m_excl = readlane_f64(tme, wu) + (mi - mt);
+    w_f = uni(readlane_f64(tmi, kWaves - 1));
+    par ^= 1;
+  }
+  // the tiny values' mass: n_tiny w(0), within n_tiny (w(2^-24) - w(-2^-24))
+  double w_f_err = 0.0;
+  if (n_tiny) {
+    const double e = 5.9604644775390625e-08;  // 2^-24
+    w_f += (double)n_tiny * exp64(-m * invT);
+    w_f_err = (double)n_tiny * (exp64((e - m) * invT) - exp64((-e - m) * invT));
+  }
+
+  // -- top-k: the rank of the k-th largest value and its tie quota ----------------------
+  const bool topk_on = kk > 0 && (uint32_t)kk < n_fin;
+  uint32_t rho_k = sel::kNone, nk_k = 0u;
+  double w_kap = 0.0, w_k = w_f;
+  if (topk_on) {
+    const uint32_t kq = (uint32_t)kk;
+    if (run_t && c_excl < kq && kq <= c_excl + ct) {
+      uint32_t cum = c_excl;
+      const double rh = run_rh();
+      double mb = m_excl, wi = run_w0();
+#pragma unroll 1
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t ci = run_count(i);
+        if (cum < kq && kq <= cum + ci) {
+          info.sel_u[0] = (uint32_t)(16 * tid + i);
+          info.sel_u[1] = kq - cum;
+          info.sel_d[0] = mb + (double)(kq - cum) * wi;
+          info.sel_d[1] = wi;
+        }
+        cum += ci;
+        mb += (double)ci * wi;
+        wi *= rh;
+      }
+    }
+    __syncthreads();
+    rho_k = uni(info.sel_u[0]);
+    nk_k = uni(info.sel_u[1]);
+    w_k = uni(info.sel_d[0]);
+    w_kap = uni(info.sel_d[1]);
+    if (rho_k >= sel::kExact) return false;  // the k-th value is not positive
+    w_f_err = 0.0;                           // the top-k set is exact
+  }
+
+  // -- top-p on the top-k set: the rank where the descending mass reaches p W_K ---------
+  uint32_t rho_s, n_keep;
+  double w_star;
+  if (topp_on) {
+    // the first value whose inclusive descending mass reaches the target; the
+    // claim goes through an atomic minimum so that adjacent runs, whose sums
+    // round differently, cannot both set it
+    // with the tiny values' mass only bounded, the cut must be the same for
+    // every reference mass in [w_k - err, w_k + err]
+    const double target = p * (w_k + w_f_err), target_lo = p * (w_k - w_f_err);
+    if (run_t && ct && m_excl < target) {
+      const double rh = run_rh();
+      double mb = m_excl, wi = run_w0();
+#pragma unroll 1
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t rho = (uint32_t)(16 * tid + i);
+        // tokens of this value inside the top-k set
+        const uint32_t ci = !topk_on || rho < rho_k ? run_count(i) : (rho == rho_k ? nk_k : 0u);
+        if (ci && mb < target && mb + (double)ci * wi >= target) {
+          const double need = (target - mb) / wi;
+          uint32_t nk = need <= 1.0 ? 1u : (need >= (double)ci ? ci : (uint32_t)ceil(need));
+          while (nk > 1u && mb + (double)(nk - 1u) * wi >= target) --nk;
+          while (nk < ci && mb + (double)nk * wi < target) ++nk;
+          // the lower reference must give the same value and count; otherwise
+          // claim 0 (a count of 0 never occurs in a real claim, and it wins)
+          const bool same = mb < target_lo && mb + (double)nk * wi >= target_lo &&
+                            (nk == 1u || mb + (double)(nk - 1u) * wi < target_lo);
+          __hip_atomic_fetch_min(&info.claim, same ? ((uint64_t)rho << 32) | nk : 0ull,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        mb += (double)ci * wi;
+        wi *= rh;
+      }
+    }
+    __syncthreads();
+    const uint64_t cl = info.claim;
+    rho_s = uni((uint32_t)(cl >> 32));
+    n_keep = uni((uint32_t)cl);
+    // rounding left the target above every prefix, or the bound on the tiny
+    // values' mass leaves the cut open: the general path
+    if (rho_s == sel::kNone || n_keep == 0u || rho_s < rho_top ||
+        rho_s >= rho_top + (uint32_t)sel::kTab)
+      return false;
+    w_star = wtab[rho_s - rho_top];
+  } else if (topk_on) {
+    rho_s = rho_k;
+    n_keep = nk_k;
+    w_star = w_kap;
+  } else {
+    return false;  // everything kept: the general path
+  }
+  // the boundary value must be positive and the weight table must reach it
+  if (rho_s >= sel::kExact || rho_s >= rho_top + (uint32_t)sel::kTab) return false;
+  const uint32_t raw_star = sel::rho_mag(rho_s);        // bf16 bits of the boundary value
+  const uint32_t pstar = K::of(raw_star);
+  const uint32_t tab_base = sel::kMagLo + sel::kExact - 1u - rho_top;  // wtab[tab_base - raw]
+
+  // -- compaction: tokens at or above the boundary, in id order, to the wave's pool ------
+  const uint8_t* const stage_bytes = reinterpret_cast<const uint8_t*>(stage[w]) + lane;
+  auto legal_bits_lds = [&](int st) -> uint32_t {
+    uint32_t m8 = bmrow ? (uint32_t)stage_bytes[st * 64] : 0xFFu;
+    if (sl.wb + (st + 1) * kStep > sl.we) {
+      const int rem = sl.we - (lane_e + st * kStep);
+      m8 &= rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u);
+    }
+    return m8;
+  };
+  PKey* const my_pk = reinterpret_cast<PKey*>(pool_raw) + w * kCap;
+  uint16_t* const my_pid =
+      reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap) + w * kCap;
+  __syncthreads();  // the histogram (under the pools) is no longer read
+  uint32_t pcnt = 0u;
+  const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
+  static_for<0, NL>([&](auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const uint32_t mb = legal_bits_lds(st);
+    const uint4 pm4 = lut[mb];
+    const uint32_t pm[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
+    Raw<1> raw;
+    raw.r[0] = xs[st].x; raw.r[1] = xs[st].y; raw.r[2] = xs[st].z; raw.r[3] = xs[st].w;
+    uint32_t dl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // illegal tokens read as the lowest signed value; positive raw bits
+      // order like their values, negative ones lie below every positive one
+      const uint32_t rl = bfi(pm[q], raw.r[q], 0x80008000u);
+      dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(rl)));  // <0 iff kept
+    }
+    const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
+    const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
+    const uint32_t cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
+                                                __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
+    pcnt = append_pool<1>(cb, raw, (uint32_t)(lane_e + st * kStep - sl.wb), pcnt, my_pk, my_pid);
+  });
+  // per wave: tokens above the boundary and their mass, ties at it
+  const int my_cnt = (int)min(pcnt, kCap);
+  uint32_t gt = 0u, ties = 0u;
+  double mgt = 0.0;
+  walk_pool<1>(my_pk, my_pid, my_cnt, (uint32_t)sl.wb, lane,
+               [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((vm >> j) & 1u) {
+        if (key[j] > pstar) {
+          ++gt;
+          mgt += wtab[tab_base - K::raw(key[j])];
+        } else {
+          ++ties;
+        }
+      }
+    }
+  });
+  gt = wave_reduce<OpSum>(gt);
+  ties = wave_reduce<OpSum>(ties);
+  mgt = wave_sum_f64(mgt);
+  if (lane == 0) {
+    info.cnt[w] = pcnt;
+    info.gt[w] = gt;
+    info.ties[w] = ties;
+    info.mass[w] = mgt;
+  }
+  // the draw's random input (lane-varying address of one element: a vector load)
+  double u_in = 0.0;
+  uint64_t seed_in = 0u, off_in = 0u;
+  if (SAMPLE) {
+    const uint32_t z = __builtin_amdgcn_mbcnt_lo(0u, 0u);  // 0 in every lane
+    if (a.uniforms) u_in = a.uniforms[r + z];
+    else { seed_in = a.seed[r + z]; off_in = a.offset[r + z]; }
+  }
+  __syncthreads();
+  {
+    const bool over = uni(wave_reduce<OpMax>(act16 && info.cnt[lane] > kCap ? 1u : 0u)) != 0u;
+    if (over) return false;
+  }
+
+  // -- tie quota per wave, list offsets, masses, the sampled wave -----------------------
+  double u = 0.0;
+  if (SAMPLE) {
+    if (a.uniforms) u = u_in;
+    else u = (double)philox_u24(seed_in, off_in) * (1.0 / 16777216.0);
+  }
+  u = uni(u);
+  uint32_t my_off, n_p, my_kt, n_z = 0u;
+  double w_p, my_cumw;
+  int sw, last_w;
+  {
+    const uint32_t t = act16 ? info.ties[lane] : 0u;
+    const uint32_t g = act16 ? info.gt[lane] : 0u;
+    const double mg = act16 ? info.mass[lane] : 0.0;
+    n_z = uni(wave_reduce<OpSum>(act16 ? info.cnt[lane] : 0u));
+    const uint32_t tb = scan_incl_u32(t) - t;
+    const uint32_t avail = n_keep > tb ? n_keep - tb : 0u;
+    const uint32_t kt = t < avail ? t : avail;
+    const uint32_t kept = g + kt;
+    const double mw = mg + (double)kt * w_star;
+    const uint32_t kincl = scan_incl_u32(kept);
+    const double mincl = scan_incl_f64(mw);
+    const double mex = incl_shift1_f64(mincl);
+    const int wu = uni(w);
+    my_off = readlane_u32(kincl - kept, wu);
+    my_kt = readlane_u32(kt, wu);
+    my_cumw = readlane_f64(mex, wu);
+    n_p = readlane_u32(kincl, kWaves - 1);
+    w_p = readlane_f64(mincl, kWaves - 1);
+    const uint64_t pos = ballot(act16 && kept > 0u && mw > 0.0);
+    last_w = pos ? 63 - __clzll((long long)pos) : -1;
+    sw = -1;
+    if (SAMPLE) {
+      const uint64_t hit = ballot(act16 && kept > 0u && u < mincl * (1.0 / w_p));
+      sw = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+    }
+  }
+  my_off = uni(my_off);
+  n_p = uni(n_p);
+  my_kt = uni(my_kt);
+  w_p = uni(w_p);
+  my_cumw = uni(my_cumw);
+  sw = uni(sw);
+  last_w = uni(last_w);
+  const double inv_wp = 1.0 / w_p;
+
+  // -- outputs --------------------------------------------------------------------------
+  int32_t* ids_row = a.cand_ids ? a.cand_ids + (size_t)r * a.cand_cap : nullptr;
+  float* probs_row = a.cand_probs ? a.cand_probs + (size_t)r * a.cand_cap : nullptr;
+  const uint32_t cap = (uint32_t)a.cand_cap;
+  // this slice's mask words, gathered in LDS (a resident slice always fits)
+  const int sw0 = sl.wb >> 5, sw1 = sl.we > sl.wb ? (sl.we + 31) >> 5 : sw0;
+  uint32_t* const my_stage = stage[w];
+  if (mask_row) {
+    for (int i = lane; i < sw1 - sw0; i += 64) my_stage[i] = 0u;
+  }
+  if (dense_row) {  // zero in memory first (the scatter below lands after these stores)
+    for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  uint32_t pos_base = my_off;
+  uint32_t ties_seen = 0u;
+  double cbase = my_cumw * inv_wp;
+  int my_token = -1;
+  int last_pos_id = -1;
+  walk_pool<1>(my_pk, my_pid, my_cnt, (uint32_t)sl.wb, lane,
+               [&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t vm) {
+    uint32_t tb = 0u, gb = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool v = (vm >> j) & 1u;
+      tb |= ((v && key[j] == pstar) ? 1u : 0u) << j;
+      gb |= ((v && key[j] > pstar) ? 1u : 0u) << j;
+    }
+    // the first my_kt ties of this wave (in id order) are kept
+    uint32_t pb = gb;
+    if (ballot(tb != 0u)) {
+      const uint32_t tc = (uint32_t)__popc(tb);
+      const uint32_t tincl = scan_incl_u32(tc);
+      uint32_t trank = ties_seen + tincl - tc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((tb >> j) & 1u) {
+          if (trank < my_kt) pb |= 1u << j;
+          ++trank;
+        }
+      }
+      ties_seen += readlane_u32(tincl, 63);
+    }
+    const uint32_t pc = (uint32_t)__popc(pb);
+    const uint32_t pincl = scan_incl_u32(pc);
+    const uint32_t total = readlane_u32(pincl, 63);
+    uint32_t pos = pos_base + pincl - pc;
+    double qv[8];
+    double lane_sum = 0.0;
+    int mwi = -1;
+    uint32_t mword = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qv[j] = 0.0;
+      if ((pb >> j) & 1u) {
+        const double q = wtab[tab_base - K::raw(key[j])] * inv_wp;
+        qv[j] = q;
+        lane_sum += q;
+        const float qf = (float)q;
+        if (ids_row && pos < cap) ids_row[pos] = (int32_t)id[j];
+        if (probs_row && pos < cap) probs_row[pos] = qf;
+        if (dense_row) dense_row[id[j]] = qf;
+        if (q > 0.0) last_pos_id = (int)id[j];
+        const int wi = (int)(id[j] >> 5);
+        if (wi != mwi) {
+          if (mwi >= 0 && mask_row)
+            __hip_atomic_fetch_or(my_stage + (mwi - sw0), mword, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+          mwi = wi;
+          mword = 0u;
+        }
+        mword |= 1u << (id[j] & 31u);
+        ++pos;
+      }
+    }
+    if (mwi >= 0 && mask_row)
+      __hip_atomic_fetch_or(my_stage + (mwi - sw0), mword, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
+    pos_base += total;
+    if (SAMPLE && w == sw && my_token < 0) {
+      const double incl = scan_incl_f64(lane_sum);
+      const double wtotal = readlane_f64(incl, 63);
+      double cu = cbase + (incl - lane_sum);
+      int hit = -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cu += qv[j];
+        if (hit < 0 && ((pb >> j) & 1u) && u < cu) hit = (int)id[j];
+      }
+      const uint64_t hbits = ballot(hit >= 0);
+      if (hbits) {
+        const int fl = __ffsll((unsigned long long)hbits) - 1;
+        my_token = __shfl(hit, fl, 64);
+      }
+      cbase += wtotal;
+    }
+  });
+  if (mask_row) {
+    for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
+  }
+  // the token: from wave sw; if rounding left u at or above wave sw's last
+  // cumulative sum, that wave's last kept id with q > 0; if u lies past every
+  // wave, the last kept id with q > 0 of the row
+  const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
+  if (SAMPLE && lane == 0) {
+    if (w == sw) a.tokens[r] = my_token >= 0 ? my_token : last_id;
+    else if (sw < 0 && w == last_w) a.tokens[r] = last_id;
+  }
+  if (tid == 0) {
+    const bool over = (a.cand_ids || a.cand_probs) ? n_p > cap : false;
+    a.status[r] = over ? QS_ROW_CAND_OVERFLOW : QS_ROW_OK;
+    if (a.cand_count) a.cand_count[r] = (int32_t)n_p;
+    if (SAMPLE && !a.uniforms) a.offset[r] = a.offset[r] + 1u;
+    if (a.dbg) {
+      a.dbg[4 * r + 0] = 0;
+      a.dbg[4 * r + 1] = 0;
+      a.dbg[4 * r + 2] = (int32_t)n_z;
+      a.dbg[4 * r + 3] = (int32_t)n_p;
+    }
+  }
+  return true;
+}
