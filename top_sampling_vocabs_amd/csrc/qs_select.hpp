@@ -149,6 +149,9 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     return m8;
   };
   uint32_t n_legal = 0u;
+  // the largest legal raw bits read as signed 16-bit: positive values order
+  // like their bits, negative ones lie below every positive one
+  uint32_t vmax2 = 0x80008000u;
   const uint32_t dump2 = (uint32_t)(sel::kBins + lane) * 0x10001u;
   static_for<0, NL>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
@@ -158,33 +161,39 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint4 nb4 = lut[mb];
     const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
     const uint32_t d4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+    uint32_t dm[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t d = d4[q];
+      // illegal tokens (and the slice's padding) now read as -0: below every
+      // positive boundary, so the later walks need no mask
+      const uint32_t d = bfi(nb[q], d4[q], 0x80008000u);
+      dm[q] = d;
+      vmax2 = bits_of(__builtin_elementwise_max(as_s2(vmax2), as_s2(d)));
+      __asm__ volatile("" : "+v"(vmax2));  // fold now: the operands are not held to the end
       uint32_t bi = bits_of(__builtin_elementwise_sub_sat(
           as_u2(d & 0x7FFF7FFFu), as_u2((sel::kMagLo - 16u) * 0x10001u)));
       bi = bits_of(__builtin_elementwise_min(as_u2(bi), as_u2(sel::kTop * 0x10001u)));
-      bi += ((d >> 15) & 0x00010001u) * sel::kSide;
+      bi = bits_of((as_u2(d) >> 15) * (unsigned short)sel::kSide + as_u2(bi));
       bi = bfi(nb[q], bi, dump2);
+      __asm__ volatile("" : "+v"(bi));  // two plain 16-bit extracts for the addresses
       __hip_atomic_fetch_add(hist + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(hist + (bi >> 16), 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    xs[st] = make_uint4(dm[0], dm[1], dm[2], dm[3]);
   });
-  // the mask words move to LDS for the compaction walk (frees their registers)
-  if (bmrow) {
-#pragma unroll
-    for (int i = 0; i < kML; ++i)
-      if (lane + 64 * i < kMW) stage[w][lane + 64 * i] = mw[i];
-  }
 
   // -- parameters (only the scans below need them) -------------------------------------
   const float Tf = a.T[r];
   const int kk = a.k[r];
   const float pf = a.p[r];
   n_legal = wave_reduce<OpSum>(n_legal);
-  if (lane == 0) red.v[par][w][0] = n_legal;
+  {
+    const s16x2 v = as_s2(vmax2);
+    const uint32_t vm = wave_reduce<OpMax>((uint32_t)(max((int32_t)v.x, (int32_t)v.y) + 0x8000));
+    if (lane == 0) { red.v[par][w][0] = n_legal; red.v[par][w][1] = vm; }
+  }
   __syncthreads();  // the histogram is complete
   // invalid parameters and greedy rows: the general path (which reports them)
   if (!(isfinite(Tf) && Tf > 0.0f) || kk < 0 || !(pf > 0.0f && pf <= 1.0f)) return false;
@@ -193,10 +202,13 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const bool topp_on = pf < 1.0f;
   const bool act16 = lane < kWaves;
   n_legal = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
+  // the largest legal value, as raw bits (below 0x8000: positive)
+  const int32_t raw_max =
+      (int32_t)uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u)) - 0x8000;
   par ^= 1;
   if (n_legal == 0u) return false;  // the general path reports the empty row
 
-  // -- runs of 16 values: counts, first value, lumps -----------------------------------
+  // -- runs of 16 values ----------------------------------------------------------------
   // Thread t < kRuns owns ranks 16 t .. 16 t + 15. Its counts are read from LDS
   // again in every phase (the row is still held in VGPRs).
   const bool run_t = tid < sel::kRuns;
@@ -218,16 +230,12 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint32_t b0 = sel::run_bin0(tid);
     return hist[tid < (int)(sel::kExact / 16) ? b0 + 15u - (uint32_t)i : b0 + (uint32_t)i];
   };
-  uint32_t ct = 0u, first = sel::kNone;
-  if (run_t) {
-    uint32_t c[16];
-    load_run(c);
-#pragma unroll
-    for (int i = 15; i >= 0; --i) {
-      ct += c[i];
-      if (c[i]) first = (uint32_t)(16 * tid + i);
-    }
-  }
+  // the maximum must be a positive exact value (below it: no positive token,
+  // or only values below 2^-24; at or above 512: large values, +inf, NaN)
+  if (raw_max < (int32_t)sel::kMagLo || raw_max >= (int32_t)(sel::kMagLo + sel::kExact))
+    return false;
+  const uint32_t rho_top = sel::kMagLo + sel::kExact - 1u - (uint32_t)raw_max;
+  uint32_t ct = 0u;
   // the lumps: magnitudes below 2^-24 (zeros among them), and >= 512 with the
   // infinities and NaN (bins 0..15 and the top bin of each side)
   uint32_t tiny = 0u, huge = 0u;
@@ -238,25 +246,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint32_t v = hist[side + (j < 16 ? (uint32_t)j : sel::kTop)];
     if (j < 16) tiny = v; else huge = v;
   }
-  {
-    const uint32_t cs = wave_reduce<OpSum>(ct);
-    const uint32_t fm = wave_reduce<OpMin>(first);
-    const uint32_t ts = wave_reduce<OpSum>(tiny);
-    const uint32_t hm = wave_reduce<OpMax>(huge);
-    if (lane == 0) {
-      red.v[par][w][0] = cs; red.v[par][w][1] = fm; red.v[par][w][2] = ts; red.v[par][w][3] = hm;
-    }
-  }
-  __syncthreads();
-  const uint32_t n_ex = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][0] : 0u));
-  const uint32_t rho_top = uni(wave_reduce<OpMin>(act16 ? red.v[par][lane][1] : sel::kNone));
-  const uint32_t n_tiny = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][2] : 0u));
-  const bool huge_any = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][3] : 0u)) != 0u;
-  par ^= 1;
-  // the tiny values lie below every positive exact value: with a positive
-  // maximum they only enter the total mass, within a bound
-  if (huge_any || n_ex + n_tiny != n_legal || rho_top >= sel::kExact) return false;
-  const uint32_t n_fin = n_legal;
 
   // -- fp64 masses relative to the maximum, block prefix sums in rank order -------------
   const double m = sel::rho_value(rho_top);
@@ -268,12 +257,21 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     return exp64(-ldexp(1.0, (int)(mag0 >> 7) - 134) * invT);
   };
   double mt = 0.0;
+  if (run_t) {
+    const uint4* const h4 = reinterpret_cast<const uint4*>(hist + sel::run_bin0(tid));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = h4[q];
+      ct += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+  __asm__ volatile("" ::: "memory");  // the counts are read again below, not held
   if (run_t && ct) {
-    uint32_t c[16];
-    load_run(c);
     const uint32_t rho0 = 16u * (uint32_t)tid;
     const double w0 = run_w0();
     const double rh = run_rh();
+    uint32_t c[16];
+    load_run(c);
     double h = (double)c[15];
 #pragma unroll
     for (int i = 14; i >= 0; --i) h = fma(h, rh, (double)c[i]);
@@ -289,15 +287,19 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       }
     }
   }
-  uint32_t c_excl;
+  uint32_t c_excl, n_ex, n_tiny;
+  bool huge_any;
   double m_excl, w_f;
   {
     const uint32_t ci = scan_incl_u32(ct);
     const double mi = scan_incl_f64(mt);
+    const uint32_t ts = wave_reduce<OpSum>(tiny);
+    const uint32_t hm = wave_reduce<OpMax>(huge);
     if (lane == 63) {
       red.v[par][w][0] = ci;
       const uint64_t b = __double_as_longlong(mi);
       red.v[par][w][1] = (uint32_t)b; red.v[par][w][2] = (uint32_t)(b >> 32);
+      red.v[par][w][3] = ts; red.v[par][w][4] = hm;
     }
     __syncthreads();  // wave totals, the weight table
     // lane i holds wave i's totals: exclusive prefix over the waves
@@ -312,8 +314,15 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     c_excl = readlane_u32(tci - tc, wu) + ci - ct;
     m_excl = readlane_f64(tme, wu) + (mi - mt);
     w_f = uni(readlane_f64(tmi, kWaves - 1));
+    n_ex = uni(readlane_u32(tci, kWaves - 1));
+    n_tiny = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][3] : 0u));
+    huge_any = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][4] : 0u)) != 0u;
     par ^= 1;
   }
+  // the tiny values lie below every positive exact value: with a positive
+  // maximum they only enter the total mass, within a bound
+  if (huge_any || n_ex + n_tiny != n_legal) return false;
+  const uint32_t n_fin = n_legal;
   // the tiny values' mass: n_tiny w(0), within n_tiny (w(2^-24) - w(-2^-24))
   double w_f_err = 0.0;
   if (n_tiny) {
@@ -413,15 +422,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t tab_base = sel::kMagLo + sel::kExact - 1u - rho_top;  // wtab[tab_base - raw]
 
   // -- compaction: tokens at or above the boundary, in id order, to the wave's pool ------
-  const uint8_t* const stage_bytes = reinterpret_cast<const uint8_t*>(stage[w]) + lane;
-  auto legal_bits_lds = [&](int st) -> uint32_t {
-    uint32_t m8 = bmrow ? (uint32_t)stage_bytes[st * 64] : 0xFFu;
-    if (sl.wb + (st + 1) * kStep > sl.we) {
-      const int rem = sl.we - (lane_e + st * kStep);
-      m8 &= rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u);
-    }
-    return m8;
-  };
   PKey* const my_pk = reinterpret_cast<PKey*>(pool_raw) + w * kCap;
   uint16_t* const my_pid =
       reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap) + w * kCap;
@@ -430,18 +430,14 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
   static_for<0, NL>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
-    const uint32_t mb = legal_bits_lds(st);
-    const uint4 pm4 = lut[mb];
-    const uint32_t pm[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
     Raw<1> raw;
     raw.r[0] = xs[st].x; raw.r[1] = xs[st].y; raw.r[2] = xs[st].z; raw.r[3] = xs[st].w;
     uint32_t dl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      // illegal tokens read as the lowest signed value; positive raw bits
-      // order like their values, negative ones lie below every positive one
-      const uint32_t rl = bfi(pm[q], raw.r[q], 0x80008000u);
-      dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(rl)));  // <0 iff kept
+      // positive raw bits order like their values, negative ones (illegal
+      // tokens among them) lie below every positive one
+      dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(raw.r[q])));  // <0 iff kept
     }
     const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
     const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
