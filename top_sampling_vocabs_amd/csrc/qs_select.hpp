@@ -75,11 +75,18 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                            uint4* lut, double* wtab, RedScratch& red,
                                            RowInfo& info) {
   using K = Keys<1>;
-  using PKey = typename PoolLayout<1>::KeyT;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
   constexpr int kMW = NL * (kStep / 32);
   constexpr int kML = (kMW + 63) / 64;
   int par = 0;
+  // the draw's random input (the given uniform, or seed and offset of the
+  // Philox draw), read now by scalar loads so that their latency hides
+  // behind the pass
+  uint64_t u_bits = 0u, seed_in = 0u;
+  if (SAMPLE) {
+    if (a.uniforms) u_bits = (uint64_t)__double_as_longlong(a.uniforms[r]);
+    else { seed_in = a.seed[r]; u_bits = a.offset[r]; }
+  }
 
   // -- requests: the slice's mask words, then every step of the slice ----------------
   const int last_piece = sl.we > sl.wb ? (sl.we - 1) & ~7 : 0;
@@ -207,6 +214,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       (int32_t)uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u)) - 0x8000;
   par ^= 1;
   if (n_legal == 0u) return false;  // the general path reports the empty row
+  if (SAMPLE && !a.uniforms) u_bits = philox_u24(seed_in, u_bits);
 
   // -- runs of 16 values ----------------------------------------------------------------
   // Thread t < kRuns owns ranks 16 t .. 16 t + 15. Its counts are read from LDS
@@ -422,47 +430,75 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t tab_base = sel::kMagLo + sel::kExact - 1u - rho_top;  // wtab[tab_base - raw]
 
   // -- compaction: tokens at or above the boundary, in id order, to the wave's pool ------
-  PKey* const my_pk = reinterpret_cast<PKey*>(pool_raw) + w * kCap;
-  uint16_t* const my_pid =
-      reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap) + w * kCap;
+  // pool entry: raw bits << 16 | token offset in the slice (id order = entry order)
+  uint32_t* const my_pool = reinterpret_cast<uint32_t*>(pool_raw) + w * kCap;
+  // this slice's keep bits, one byte per lane and step: the layout of the mask
+  // words (byte lane & 3 of slice word 16 st + lane / 4)
+  uint8_t* const keep_bytes = reinterpret_cast<uint8_t*>(stage[w]) + lane;
   __syncthreads();  // the histogram (under the pools) is no longer read
   uint32_t pcnt = 0u;
   const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
   static_for<0, NL>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
-    Raw<1> raw;
-    raw.r[0] = xs[st].x; raw.r[1] = xs[st].y; raw.r[2] = xs[st].z; raw.r[3] = xs[st].w;
+    const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
     uint32_t dl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // positive raw bits order like their values, negative ones (illegal
       // tokens among them) lie below every positive one
-      dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(raw.r[q])));  // <0 iff kept
+      dl[q] = bits_of(__builtin_elementwise_sub_sat(as_s2(t2m1), as_s2(r4[q])));  // <0 iff kept
     }
     const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
     const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
-    const uint32_t cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
-                                                __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
-    pcnt = append_pool<1>(cb, raw, (uint32_t)(lane_e + st * kStep - sl.wb), pcnt, my_pk, my_pid);
-  });
-  // per wave: tokens above the boundary and their mass, ties at it
-  const int my_cnt = (int)min(pcnt, kCap);
-  uint32_t gt = 0u, ties = 0u;
-  double mgt = 0.0;
-  walk_pool<1>(my_pk, my_pid, my_cnt, (uint32_t)sl.wb, lane,
-               [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((vm >> j) & 1u) {
-        if (key[j] > pstar) {
-          ++gt;
-          mgt += wtab[tab_base - K::raw(key[j])];
-        } else {
-          ++ties;
+    uint32_t cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
+                                          __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
+    keep_bytes[st * 64] = (uint8_t)cb;
+    const uint32_t c = (uint32_t)__popc(cb);
+    const uint64_t any = ballot(c != 0u);
+    if (any) {
+      uint32_t excl, total;
+      if (!ballot(c > 1u)) {  // at most one per lane: one ballot
+        excl = count_below(any);
+        total = (uint32_t)__popcll(any);
+      } else {
+        const uint32_t incl = scan_incl_u32(c);
+        excl = incl - c;
+        total = readlane_u32(incl, 63);
+      }
+      // a pool that would overflow is not written (the row then declines)
+      if (pcnt + total <= kCap) {
+        uint32_t pos = pcnt + excl;
+        const uint32_t e0 = (uint32_t)(lane_e + st * kStep - sl.wb);
+        while (ballot(cb != 0u)) {
+          if (cb) {
+            const uint32_t j = (uint32_t)__builtin_ctz(cb);
+            cb &= cb - 1u;
+            const uint32_t d = (j & 4u) ? ((j & 2u) ? r4[3] : r4[2]) : ((j & 2u) ? r4[1] : r4[0]);
+            // the token's 16 bits to the top half, the low half cleared
+            const uint32_t hi = __builtin_amdgcn_perm(d, d, (j & 1u) ? 0x03020C0Cu : 0x01000C0Cu);
+            my_pool[pos] = hi + e0 + j;
+            ++pos;
+          }
         }
       }
+      pcnt += total;
     }
   });
+  // per wave: tokens above the boundary and their mass, ties at it (every
+  // entry is at or above the boundary value, which is positive)
+  const int my_cnt = (int)min(pcnt, kCap);
+  const uint32_t e_gt = (raw_star << 16) | 0xFFFFu;  // entries above it compare greater
+  uint32_t gt = 0u, ties = 0u;
+  double mgt = 0.0;
+  for (int i = lane; i < my_cnt; i += 64) {
+    const uint32_t e = my_pool[i];
+    if (e > e_gt) {
+      ++gt;
+      mgt += wtab[tab_base - (e >> 16)];
+    } else {
+      ++ties;
+    }
+  }
   gt = wave_reduce<OpSum>(gt);
   ties = wave_reduce<OpSum>(ties);
   mgt = wave_sum_f64(mgt);
@@ -471,14 +507,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     info.gt[w] = gt;
     info.ties[w] = ties;
     info.mass[w] = mgt;
-  }
-  // the draw's random input (lane-varying address of one element: a vector load)
-  double u_in = 0.0;
-  uint64_t seed_in = 0u, off_in = 0u;
-  if (SAMPLE) {
-    const uint32_t z = __builtin_amdgcn_mbcnt_lo(0u, 0u);  // 0 in every lane
-    if (a.uniforms) u_in = a.uniforms[r + z];
-    else { seed_in = a.seed[r + z]; off_in = a.offset[r + z]; }
   }
   __syncthreads();
   {
@@ -489,8 +517,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // -- tie quota per wave, list offsets, masses, the sampled wave -----------------------
   double u = 0.0;
   if (SAMPLE) {
-    if (a.uniforms) u = u_in;
-    else u = (double)philox_u24(seed_in, off_in) * (1.0 / 16777216.0);
+    if (a.uniforms) u = __longlong_as_double((long long)u_bits);
+    else u = (double)(uint32_t)u_bits * (1.0 / 16777216.0);
   }
   u = uni(u);
   uint32_t my_off, n_p, my_kt, n_z = 0u;
@@ -538,98 +566,59 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t cap = (uint32_t)a.cand_cap;
   // this slice's mask words, gathered in LDS (a resident slice always fits)
   const int sw0 = sl.wb >> 5, sw1 = sl.we > sl.wb ? (sl.we + 31) >> 5 : sw0;
-  uint32_t* const my_stage = stage[w];
-  if (mask_row) {
-    for (int i = lane; i < sw1 - sw0; i += 64) my_stage[i] = 0u;
-  }
+  uint32_t* const my_stage = stage[w];  // the keep bits, written by the compaction
   if (dense_row) {  // zero in memory first (the scatter below lands after these stores)
     for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
   }
+  // walk D, lane-strided: 64 consecutive entries per round, so that the kept
+  // ones take consecutive list positions
   uint32_t pos_base = my_off;
   uint32_t ties_seen = 0u;
   double cbase = my_cumw * inv_wp;
   int my_token = -1;
   int last_pos_id = -1;
-  walk_pool<1>(my_pk, my_pid, my_cnt, (uint32_t)sl.wb, lane,
-               [&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t vm) {
-    uint32_t tb = 0u, gb = 0u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool v = (vm >> j) & 1u;
-      tb |= ((v && key[j] == pstar) ? 1u : 0u) << j;
-      gb |= ((v && key[j] > pstar) ? 1u : 0u) << j;
-    }
-    // the first my_kt ties of this wave (in id order) are kept
-    uint32_t pb = gb;
-    if (ballot(tb != 0u)) {
-      const uint32_t tc = (uint32_t)__popc(tb);
-      const uint32_t tincl = scan_incl_u32(tc);
-      uint32_t trank = ties_seen + tincl - tc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((tb >> j) & 1u) {
-          if (trank < my_kt) pb |= 1u << j;
-          ++trank;
-        }
+  for (int i0 = 0; i0 < my_cnt; i0 += 64) {
+    const int i = i0 + lane;
+    const bool valid = i < my_cnt;
+    const uint32_t e = valid ? my_pool[i] : 0u;
+    const bool g = valid && e > e_gt;
+    const bool t = valid && !g;
+    bool keep = g;
+    const uint64_t tbits = ballot(t);
+    if (tbits) {
+      // ties in id order: the first my_kt of this wave are kept; the bits of
+      // the others are cleared from the keep mask
+      const uint32_t trank = ties_seen + count_below(tbits);
+      if (t) {
+        if (trank < my_kt) keep = true;
+        else if (mask_row)
+          __hip_atomic_fetch_and(my_stage + ((e & 0xFFFFu) >> 5), ~(1u << (e & 31u)),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      ties_seen += readlane_u32(tincl, 63);
+      ties_seen += (uint32_t)__popcll(tbits);
     }
-    const uint32_t pc = (uint32_t)__popc(pb);
-    const uint32_t pincl = scan_incl_u32(pc);
-    const uint32_t total = readlane_u32(pincl, 63);
-    uint32_t pos = pos_base + pincl - pc;
-    double qv[8];
-    double lane_sum = 0.0;
-    int mwi = -1;
-    uint32_t mword = 0u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qv[j] = 0.0;
-      if ((pb >> j) & 1u) {
-        const double q = wtab[tab_base - K::raw(key[j])] * inv_wp;
-        qv[j] = q;
-        lane_sum += q;
-        const float qf = (float)q;
-        if (ids_row && pos < cap) ids_row[pos] = (int32_t)id[j];
-        if (probs_row && pos < cap) probs_row[pos] = qf;
-        if (dense_row) dense_row[id[j]] = qf;
-        if (q > 0.0) last_pos_id = (int)id[j];
-        const int wi = (int)(id[j] >> 5);
-        if (wi != mwi) {
-          if (mwi >= 0 && mask_row)
-            __hip_atomic_fetch_or(my_stage + (mwi - sw0), mword, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-          mwi = wi;
-          mword = 0u;
-        }
-        mword |= 1u << (id[j] & 31u);
-        ++pos;
-      }
+    const uint64_t kbits = ballot(keep);
+    const uint32_t pos = pos_base + count_below(kbits);
+    const int id = (int)(sl.wb + (e & 0xFFFFu));
+    double q = 0.0;
+    if (keep) {
+      q = wtab[tab_base - (e >> 16)] * inv_wp;
+      const float qf = (float)q;
+      if (ids_row && pos < cap) ids_row[pos] = id;
+      if (probs_row && pos < cap) probs_row[pos] = qf;
+      if (dense_row) dense_row[id] = qf;
+      if (q > 0.0) last_pos_id = id;
     }
-    if (mwi >= 0 && mask_row)
-      __hip_atomic_fetch_or(my_stage + (mwi - sw0), mword, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_WORKGROUP);
-    pos_base += total;
+    pos_base += (uint32_t)__popcll(kbits);
     if (SAMPLE && w == sw && my_token < 0) {
-      const double incl = scan_incl_f64(lane_sum);
-      const double wtotal = readlane_f64(incl, 63);
-      double cu = cbase + (incl - lane_sum);
-      int hit = -1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        cu += qv[j];
-        if (hit < 0 && ((pb >> j) & 1u) && u < cu) hit = (int)id[j];
-      }
-      const uint64_t hbits = ballot(hit >= 0);
-      if (hbits) {
-        const int fl = __ffsll((unsigned long long)hbits) - 1;
-        my_token = __shfl(hit, fl, 64);
-      }
-      cbase += wtotal;
+      const double incl = scan_incl_f64(q);
+      const uint64_t hbits = ballot(keep && u < cbase + incl);
+      if (hbits) my_token = __shfl(id, __ffsll((unsigned long long)hbits) - 1, 64);
+      cbase += readlane_f64(incl, 63);
     }
-  });
+  }
   if (mask_row) {
     for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
   }
