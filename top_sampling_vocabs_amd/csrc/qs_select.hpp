@@ -233,10 +233,15 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = pos ? asc[15 - i] : asc[i];
   };
-  // count of rank 16 tid + i (rolled loops below read it from LDS)
-  auto run_count = [&](int i) -> uint32_t {
+  // counts of ranks 16 tid + 4 qd .. + 3, in rank order (one LDS read; the
+  // rolled loops below take a quad per round)
+  auto run_quad = [&](int qd, uint32_t (&c4)[4]) {
     const uint32_t b0 = sel::run_bin0(tid);
-    return hist[tid < (int)(sel::kExact / 16) ? b0 + 15u - (uint32_t)i : b0 + (uint32_t)i];
+    const bool pos = tid < (int)(sel::kExact / 16);
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + (pos ? b0 + 12u - 4u * (uint32_t)qd
+                                                                : b0 + 4u * (uint32_t)qd));
+    c4[0] = pos ? v.w : v.x; c4[1] = pos ? v.z : v.y;
+    c4[2] = pos ? v.y : v.z; c4[3] = pos ? v.x : v.w;
   };
   // the maximum must be a positive exact value (below it: no positive token,
   // or only values below 2^-24; at or above 512: large values, +inf, NaN)
@@ -350,17 +355,22 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       const double rh = run_rh();
       double mb = m_excl, wi = run_w0();
 #pragma unroll 1
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t ci = run_count(i);
-        if (cum < kq && kq <= cum + ci) {
-          info.sel_u[0] = (uint32_t)(16 * tid + i);
-          info.sel_u[1] = kq - cum;
-          info.sel_d[0] = mb + (double)(kq - cum) * wi;
-          info.sel_d[1] = wi;
+      for (int qd = 0; qd < 4; ++qd) {
+        uint32_t c4[4];
+        run_quad(qd, c4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t ci = c4[k];
+          if (cum < kq && kq <= cum + ci) {
+            info.sel_u[0] = (uint32_t)(16 * tid + 4 * qd + k);
+            info.sel_u[1] = kq - cum;
+            info.sel_d[0] = mb + (double)(kq - cum) * wi;
+            info.sel_d[1] = wi;
+          }
+          cum += ci;
+          mb += (double)ci * wi;
+          wi *= rh;
         }
-        cum += ci;
-        mb += (double)ci * wi;
-        wi *= rh;
       }
     }
     __syncthreads();
@@ -382,14 +392,22 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     // with the tiny values' mass only bounded, the cut must be the same for
     // every reference mass in [w_k - err, w_k + err]
     const double target = p * (w_k + w_f_err), target_lo = p * (w_k - w_f_err);
-    if (run_t && ct && m_excl < target) {
+    // runs whose sum reaches the target, with room for rounding: the running
+    // sums below and the prefix sums differ by a few units in the last place
+    // of the target's magnitude, far below the 1e-13 margin
+    if (run_t && ct && m_excl < target && m_excl + mt >= target * (1.0 - 1e-13)) {
       const double rh = run_rh();
       double mb = m_excl, wi = run_w0();
 #pragma unroll 1
-      for (int i = 0; i < 16; ++i) {
+      for (int qd = 0; qd < 4; ++qd) {
+        uint32_t c4[4];
+        run_quad(qd, c4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * qd + k;
         const uint32_t rho = (uint32_t)(16 * tid + i);
         // tokens of this value inside the top-k set
-        const uint32_t ci = !topk_on || rho < rho_k ? run_count(i) : (rho == rho_k ? nk_k : 0u);
+        const uint32_t ci = !topk_on || rho < rho_k ? c4[k] : (rho == rho_k ? nk_k : 0u);
         if (ci && mb < target && mb + (double)ci * wi >= target) {
           const double need = (target - mb) / wi;
           uint32_t nk = need <= 1.0 ? 1u : (need >= (double)ci ? ci : (uint32_t)ceil(need));
@@ -404,6 +422,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         }
         mb += (double)ci * wi;
         wi *= rh;
+      }
       }
     }
     __syncthreads();
