@@ -76,6 +76,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                            RowInfo& info) {
   using K = Keys<1>;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
+  constexpr uint32_t kPool = kCap - 64u;  // entries per wave; 64 dump slots follow
   constexpr int kMW = NL * (kStep / 32);
   constexpr int kML = (kMW + 63) / 64;
   int par = 0;
@@ -485,19 +486,24 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         total = readlane_u32(incl, 63);
       }
       // a pool that would overflow is not written (the row then declines)
-      if (pcnt + total <= kCap) {
-        uint32_t pos = pcnt + excl;
+      if (pcnt + total <= kPool) {
+        uint32_t* slot = my_pool + pcnt + excl;
         const uint32_t e0 = (uint32_t)(lane_e + st * kStep - sl.wb);
-        while (ballot(cb != 0u)) {
-          if (cb) {
-            const uint32_t j = (uint32_t)__builtin_ctz(cb);
-            cb &= cb - 1u;
-            const uint32_t d = (j & 4u) ? ((j & 2u) ? r4[3] : r4[2]) : ((j & 2u) ? r4[1] : r4[0]);
-            // the token's 16 bits to the top half, the low half cleared
-            const uint32_t hi = __builtin_amdgcn_perm(d, d, (j & 1u) ? 0x03020C0Cu : 0x01000C0Cu);
-            my_pool[pos] = hi + e0 + j;
-            ++pos;
-          }
+        // every lane writes each round, lanes without a token left to a slot
+        // of their own past the pool, so the rounds need no branches (a lane
+        // stays idle once it has run out, so its own slot may move on)
+        uint32_t* const dump = my_pool + kPool + lane;
+        for (;;) {
+          const bool on = cb != 0u;
+          if (!ballot(on)) break;
+          const uint32_t j = (uint32_t)__builtin_ctz(cb | 0x100u);
+          cb &= cb - 1u;
+          // token j: bits 16 (j & 3) of the low or the high 64 bits of the chunk
+          const uint64_t h = (j & 4u) ? ((uint64_t)r4[3] << 32 | r4[2])
+                                      : ((uint64_t)r4[1] << 32 | r4[0]);
+          const uint32_t lo = (uint32_t)(h >> ((j & 3u) * 16u));
+          *(on ? slot : dump) = (lo << 16) + (e0 + j);
+          ++slot;
         }
       }
       pcnt += total;
@@ -505,7 +511,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   });
   // per wave: tokens above the boundary and their mass, ties at it (every
   // entry is at or above the boundary value, which is positive)
-  const int my_cnt = (int)min(pcnt, kCap);
+  const int my_cnt = (int)min(pcnt, kPool);
   const uint32_t e_gt = (raw_star << 16) | 0xFFFFu;  // entries above it compare greater
   uint32_t gt = 0u, ties = 0u;
   double mgt = 0.0;
@@ -529,7 +535,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   }
   __syncthreads();
   {
-    const bool over = uni(wave_reduce<OpMax>(act16 && info.cnt[lane] > kCap ? 1u : 0u)) != 0u;
+    const bool over = uni(wave_reduce<OpMax>(act16 && info.cnt[lane] > kPool ? 1u : 0u)) != 0u;
     if (over) return false;
   }
 
