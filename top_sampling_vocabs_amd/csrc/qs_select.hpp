@@ -284,11 +284,17 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint32_t rho0 = 16u * (uint32_t)tid;
     const double w0 = run_w0();
     const double rh = run_rh();
-    uint32_t c[16];
-    load_run(c);
-    double h = (double)c[15];
-#pragma unroll
-    for (int i = 14; i >= 0; --i) h = fma(h, rh, (double)c[i]);
+    // Horner from the last rank down, one quad of counts per round
+    double h = 0.0;
+#pragma unroll 1
+    for (int qd = 3; qd >= 0; --qd) {
+      uint32_t c4[4];
+      run_quad(qd, c4);
+      h = fma(h, rh, (double)c4[3]);
+      h = fma(h, rh, (double)c4[2]);
+      h = fma(h, rh, (double)c4[1]);
+      h = fma(h, rh, (double)c4[0]);
+    }
     mt = w0 * h;
     // the weight table: every rank from the maximum down, as far as it reaches
     if (rho0 + 16u > rho_top && rho0 < rho_top + (uint32_t)sel::kTab) {
@@ -399,31 +405,37 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     if (run_t && ct && m_excl < target && m_excl + mt >= target * (1.0 - 1e-13)) {
       const double rh = run_rh();
       double mb = m_excl, wi = run_w0();
+      // the crossing value of this run (at most one: the sum only grows)
+      uint32_t hit_rho = sel::kNone, hit_c = 0u;
+      double hit_mb = 0.0, hit_w = 0.0;
 #pragma unroll 1
       for (int qd = 0; qd < 4; ++qd) {
         uint32_t c4[4];
         run_quad(qd, c4);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = 4 * qd + k;
-        const uint32_t rho = (uint32_t)(16 * tid + i);
-        // tokens of this value inside the top-k set
-        const uint32_t ci = !topk_on || rho < rho_k ? c4[k] : (rho == rho_k ? nk_k : 0u);
-        if (ci && mb < target && mb + (double)ci * wi >= target) {
-          const double need = (target - mb) / wi;
-          uint32_t nk = need <= 1.0 ? 1u : (need >= (double)ci ? ci : (uint32_t)ceil(need));
-          while (nk > 1u && mb + (double)(nk - 1u) * wi >= target) --nk;
-          while (nk < ci && mb + (double)nk * wi < target) ++nk;
-          // the lower reference must give the same value and count; otherwise
-          // claim 0 (a count of 0 never occurs in a real claim, and it wins)
-          const bool same = mb < target_lo && mb + (double)nk * wi >= target_lo &&
-                            (nk == 1u || mb + (double)(nk - 1u) * wi < target_lo);
-          __hip_atomic_fetch_min(&info.claim, same ? ((uint64_t)rho << 32) | nk : 0ull,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t rho = (uint32_t)(16 * tid + 4 * qd + k);
+          // tokens of this value inside the top-k set
+          const uint32_t ci = !topk_on || rho < rho_k ? c4[k] : (rho == rho_k ? nk_k : 0u);
+          const double nb = mb + (double)ci * wi;
+          if (ci && mb < target && nb >= target) {
+            hit_rho = rho; hit_c = ci; hit_mb = mb; hit_w = wi;
+          }
+          mb = nb;
+          wi *= rh;
         }
-        mb += (double)ci * wi;
-        wi *= rh;
       }
+      if (hit_rho != sel::kNone) {
+        const double need = (target - hit_mb) / hit_w;
+        uint32_t nk = need <= 1.0 ? 1u : (need >= (double)hit_c ? hit_c : (uint32_t)ceil(need));
+        while (nk > 1u && hit_mb + (double)(nk - 1u) * hit_w >= target) --nk;
+        while (nk < hit_c && hit_mb + (double)nk * hit_w < target) ++nk;
+        // the lower reference must give the same value and count; otherwise
+        // claim 0 (a count of 0 never occurs in a real claim, and it wins)
+        const bool same = hit_mb < target_lo && hit_mb + (double)nk * hit_w >= target_lo &&
+                          (nk == 1u || hit_mb + (double)(nk - 1u) * hit_w < target_lo);
+        __hip_atomic_fetch_min(&info.claim, same ? ((uint64_t)hit_rho << 32) | nk : 0ull,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     __syncthreads();
