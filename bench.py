@@ -201,13 +201,13 @@ def time_graph(preps, K, flags=None):
 # (its runs C, I and J drop duplicate handling, sort the candidates, or sort
 # the full row: not paths of this library).
 ABLATION_RUNS = [
-    ("A", "full path: truncation hit, histogram scan (bf16) / quaternary search (fp32)", 0),
+    ("A", "normal path: value histogram (bf16 in registers) / truncation hit + quaternary search (fp32)", 0),
     ("B", "single streamed tier instead of the register tiers", 8),
     ("D", "forced fallback: quaternary searches over the full row", 1),
     ("E", "no truncation: quaternary searches over the full row", 2),
     ("F", "truncation hit, binary pivot (one pivot per round)", 16 | 4),
     ("G", "forced fallback, binary pivot", 16 | 1),
-    ("Q", "truncation hit, quaternary search on bf16 pools instead of the histogram scan", 4),
+    ("Q", "truncation hit, quaternary search on bf16 pools (the page's design)", 4),
 ]
 
 

@@ -76,11 +76,13 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
 
 /* Path switches for ablations and path-invariance tests; outputs are identical
  * with or without them (page "Qrita", ablation table: forced fallback and no
- * truncation). 0 is the normal path. */
+ * truncation). 0 is the normal path, in which bf16 rows held in registers are
+ * settled by a value histogram of the whole row; any switch sends every row
+ * through the truncation-and-search path, which the switches then vary. */
 #define QS_FLAG_FORCE_MISS     1u  /* run every search over the full row        */
 #define QS_FLAG_NO_TRUNCATION  2u  /* skip the sigma-truncation compaction      */
 #define QS_FLAG_PIVOT_SEARCH   4u  /* quaternary pivot search also on bf16 pools
-                                      (instead of the histogram scan)           */
+                                      (instead of their key-histogram scan)     */
 #define QS_FLAG_STREAM         8u  /* stream the row even when it fits in
                                       registers                                 */
 #define QS_FLAG_BINARY_PIVOT  16u  /* one pivot per search round (the interval's
