@@ -159,9 +159,36 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   uint16_t* const pool_id = reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap);
 
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int w = uni(tid >> 6);  // wave index, kept in a scalar register
-  const int lane = tid & 63;
+  const int w = uni((int)threadIdx.x >> 6);  // wave index, kept in a scalar register
+
+  // -- bf16 rows held in registers: the value-histogram path ---------------------
+  // (rows it cannot settle exactly, and the path switches, take the general
+  // path below, which derives its per-lane values again so that none of them
+  // is held across this path)
+  if constexpr (DT == 1 && kResident) {
+    if (a.flags == 0u) {
+      const int tid = threadIdx.x;
+      const int lane = tid & 63;
+      Slice sl;
+      sl.row = a.logits + (size_t)r * a.row_bytes;
+      sl.mrow = nullptr;
+      sl.V = a.V;
+      sl.wb = uni(min(a.V, w * a.seg));
+      sl.we = uni(min(a.V, (w + 1) * a.seg));
+      const int W = (a.V + 31) >> 5;
+      const uint32_t* const bmrow = a.bitmask ? a.bitmask + (size_t)r * a.bm_stride : nullptr;
+      uint32_t* const mask_row = a.keep_mask ? a.keep_mask + (size_t)r * W : nullptr;
+      float* const dense_row = a.dense ? a.dense + (size_t)r * a.V : nullptr;
+      if (select_row<SAMPLE, NL>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
+                                 pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
+                                 info))
+        return;
+      __syncthreads();  // the general path reuses the LDS
+    }
+  }
+
+  const int lane = (int)lane_id();
+  const int tid = w * 64 + lane;
   int par = 0;
 
   const int V = a.V;
@@ -207,19 +234,6 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       }
     }
   };
-
-  // -- bf16 rows held in registers: the value-histogram path ---------------------
-  // (rows it cannot settle exactly, and the path switches, take the general
-  // path below)
-  if constexpr (DT == 1 && kResident) {
-    if (a.flags == 0u) {
-      if (select_row<SAMPLE, NL>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
-                                 pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
-                                 info))
-        return;
-      __syncthreads();  // the general path reuses the LDS
-    }
-  }
 
   // -- the sample: step 0 of every slice ----------------------------------------
   // The first 512 tokens of each of the 16 slices (8192 tokens) are the only

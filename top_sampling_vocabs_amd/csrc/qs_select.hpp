@@ -90,7 +90,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   }
 
   // -- requests: the slice's mask words, then every step of the slice ----------------
-  const int last_piece = sl.we > sl.wb ? (sl.we - 1) & ~7 : 0;
   const int lane_e = sl.wb + lane * kChunk;
   uint32_t mw[kML];
   {
@@ -112,12 +111,18 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   constexpr int kLook = NL < 10 ? NL : 10;
   constexpr int kEarly = kLook < 4 ? kLook : 4;
   uint4 xs[NL];
+  // the row through a buffer resource whose range ends at the row's last
+  // 16-byte chunk: requests past it read zeros (masked as padding below), so
+  // the address of a step is the lane's constant offset plus a scalar one
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(sl.row), (short)0, (int)(((uint32_t)sl.V * 2u + 15u) & ~15u),
+      0x00020000);
+  const int voff = lane_e * 2;
   auto issue = [&](auto stc) {
     constexpr int st = decltype(stc)::value;
-    if constexpr (st < NL) {
-      const int ep = min(lane_e + st * kStep, last_piece);
-      xs[st] = *reinterpret_cast<const uint4*>(chunk_ptr<1>(sl.row, ep));
-    }
+    if constexpr (st < NL)
+      xs[st] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc, voff, st * kStep * 2, 0));
   };
   static_for<0, kEarly>(issue);
 
@@ -144,11 +149,14 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // -- the pass: count every legal token in its value bin ------------------------------
   // legal bits of step st: byte (lane & 3) of slice word 16 st + lane / 4, held
   // by lane (st & 3) * 16 + lane / 4 in mw[st / 4]
+  const int bp_addr = (lane >> 2) * 4;               // byte address of lane lane / 4
+  const uint32_t bsh = (uint32_t)(lane & 3) * 8u;     // this lane's byte of that word
   auto legal_bits = [&](int st) -> uint32_t {
     uint32_t m8 = 0xFFu;
     if (bmrow) {
-      const uint32_t wd = (uint32_t)__shfl((int)mw[st >> 2], (st & 3) * 16 + (lane >> 2), 64);
-      m8 = (wd >> ((lane & 3) * 8)) & 0xFFu;
+      const uint32_t wd =
+          (uint32_t)__builtin_amdgcn_ds_bpermute(bp_addr + (st & 3) * 64, (int)mw[st >> 2]);
+      m8 = __builtin_amdgcn_ubfe(wd, bsh, 8u);
     }
     if (sl.wb + (st + 1) * kStep > sl.we) {  // a step that ends past the slice
       const int rem = sl.we - (lane_e + st * kStep);
@@ -181,7 +189,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       uint32_t bi = bits_of(__builtin_elementwise_sub_sat(
           as_u2(d & 0x7FFF7FFFu), as_u2((sel::kMagLo - 16u) * 0x10001u)));
       bi = bits_of(__builtin_elementwise_min(as_u2(bi), as_u2(sel::kTop * 0x10001u)));
-      bi = bits_of((as_u2(d) >> 15) * (unsigned short)sel::kSide + as_u2(bi));
+      {  // the sign's side: bin + sign * kSide, one packed multiply-add
+        const uint32_t sg = bits_of(as_u2(d) >> 15);
+        __asm__("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(bi) : "v"(sg), "s"(sel::kSide * 0x10001u), "v"(bi));
+      }
       bi = bfi(nb[q], bi, dump2);
       __asm__ volatile("" : "+v"(bi));  // two plain 16-bit extracts for the addresses
       __hip_atomic_fetch_add(hist + (bi & 0xFFFFu), 1u, __ATOMIC_RELAXED,
