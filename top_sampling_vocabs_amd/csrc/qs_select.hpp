@@ -478,7 +478,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // this slice's keep bits, one byte per lane and step: the layout of the mask
   // words (byte lane & 3 of slice word 16 st + lane / 4)
   uint8_t* const keep_bytes = reinterpret_cast<uint8_t*>(stage[w]) + lane;
-  __syncthreads();  // the histogram (under the pools) is no longer read
+  // (the pools overwrite the histogram: its last reads, in the searches above,
+  // all precede the search barriers)
   uint32_t pcnt = 0u;
   const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
   static_for<0, NL>([&](auto stc) {
