@@ -76,7 +76,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                            RowInfo& info) {
   using K = Keys<1>;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
-  constexpr uint32_t kPool = kCap - 64u;  // entries per wave; 64 dump slots follow
+  // entries per wave; 64 dump slots and one step of the slice (64 lanes x 16 B) follow
+  constexpr uint32_t kPool = kCap - 64u - 256u;
   constexpr int kMW = NL * (kStep / 32);
   constexpr int kML = (kMW + 63) / 64;
   int par = 0;
@@ -482,6 +483,11 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // all precede the search barriers)
   uint32_t pcnt = 0u;
   const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
+  uint32_t* const dump = my_pool + kPool + lane;
+  // this lane's chunk of the current step, staged in LDS so that a round
+  // reads its token's bits by index
+  uint4* const my_chunk = reinterpret_cast<uint4*>(my_pool + kPool + 64u) + lane;
+  const uint16_t* const chunk_bits = reinterpret_cast<const uint16_t*>(my_chunk);
   static_for<0, NL>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
     const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
@@ -513,24 +519,21 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       if (pcnt + total <= kPool) {
         uint32_t* slot = my_pool + pcnt + excl;
         const uint32_t e0 = (uint32_t)(lane_e + st * kStep - sl.wb);
+        if (c) *my_chunk = xs[st];
         // every lane writes each round, lanes without a token left to a slot
         // of their own past the pool, so the rounds need no branches (a lane
         // stays idle once it has run out, so its own slot may move on)
-        uint32_t* const dump = my_pool + kPool + lane;
         for (;;) {
           const bool on = cb != 0u;
           if (!ballot(on)) break;
           const uint32_t j = (uint32_t)__builtin_ctz(cb | 0x100u);
           cb &= cb - 1u;
-          // token j: bits 16 (j & 3) of the low or the high 64 bits of the chunk
-          const uint64_t h = (j & 4u) ? ((uint64_t)r4[3] << 32 | r4[2])
-                                      : ((uint64_t)r4[1] << 32 | r4[0]);
-          const uint32_t lo = (uint32_t)(h >> ((j & 3u) * 16u));
-          *(on ? slot : dump) = (lo << 16) + (e0 + j);
+          const uint32_t key = chunk_bits[j & 7u];
+          *(on ? slot : dump) = (key << 16) + (e0 + j);
           ++slot;
         }
       }
-      pcnt += total;
+      pcnt = uni(pcnt + total);
     }
   });
   // per wave: tokens above the boundary and their mass, ties at it (every
