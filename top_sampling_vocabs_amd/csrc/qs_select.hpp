@@ -542,15 +542,40 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t e_gt = (raw_star << 16) | 0xFFFFu;  // entries above it compare greater
   uint32_t gt = 0u, ties = 0u;
   double mgt = 0.0;
-  for (int i = lane; i < my_cnt; i += 64) {
-    const uint32_t e = my_pool[i];
-    if (e > e_gt) {
-      ++gt;
-      mgt += wtab[tab_base - (e >> 16)];
+  // KP consecutive entries per lane and round: one for short pools, four for
+  // long ones (reads past my_cnt stay in this wave's pool region and are not
+  // counted)
+  auto load_entries = [&](auto kpc, int ib, uint32_t (&e)[4]) {
+    constexpr int KP = decltype(kpc)::value;
+    if constexpr (KP == 4) {
+      const uint4 e4 = *reinterpret_cast<const uint4*>(my_pool + ib);
+      e[0] = e4.x; e[1] = e4.y; e[2] = e4.z; e[3] = e4.w;
     } else {
-      ++ties;
+      e[0] = my_pool[ib];
     }
-  }
+  };
+  const bool long_pool = uni(my_cnt) > 192;
+  auto walk_a = [&](auto kpc) {
+    constexpr int KP = decltype(kpc)::value;
+    for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
+      const int ib = i0 + KP * lane;
+      uint32_t e[4];
+      load_entries(kpc, ib, e);
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        if (ib + k < my_cnt) {
+          if (e[k] > e_gt) {
+            ++gt;
+            mgt += wtab[tab_base - (e[k] >> 16)];
+          } else {
+            ++ties;
+          }
+        }
+      }
+    }
+  };
+  if (long_pool) walk_a(std::integral_constant<int, 4>{});
+  else walk_a(std::integral_constant<int, 1>{});
   gt = wave_reduce<OpSum>(gt);
   ties = wave_reduce<OpSum>(ties);
   mgt = wave_sum_f64(mgt);
@@ -624,53 +649,84 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
   }
-  // walk D, lane-strided: 64 consecutive entries per round, so that the kept
-  // ones take consecutive list positions
+  // walk D: 64 KP consecutive entries per round, KP per lane, so that the
+  // kept ones of a lane take consecutive list positions and the prefix sums
+  // of a round serve KP entries
   uint32_t pos_base = my_off;
   uint32_t ties_seen = 0u;
   double cbase = my_cumw * inv_wp;
   int my_token = -1;
   int last_pos_id = -1;
-  for (int i0 = 0; i0 < my_cnt; i0 += 64) {
-    const int i = i0 + lane;
-    const bool valid = i < my_cnt;
-    const uint32_t e = valid ? my_pool[i] : 0u;
-    const bool g = valid && e > e_gt;
-    const bool t = valid && !g;
-    bool keep = g;
-    const uint64_t tbits = ballot(t);
-    if (tbits) {
+  auto walk_d = [&](auto kpc) {
+   constexpr int KP = decltype(kpc)::value;
+   for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
+    const int ib = i0 + KP * lane;
+    uint32_t e[4];
+    load_entries(kpc, ib, e);
+    uint32_t kb = 0u, tb = 0u;  // kept (above the boundary) and tie bits of the KP
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const bool valid = ib + k < my_cnt;
+      kb |= (valid && e[k] > e_gt ? 1u : 0u) << k;
+      tb |= (valid && e[k] <= e_gt ? 1u : 0u) << k;
+    }
+    const uint32_t tc = (uint32_t)__popc(tb);
+    if (ballot(tc != 0u)) {
       // ties in id order: the first my_kt of this wave are kept; the bits of
       // the others are cleared from the keep mask
-      const uint32_t trank = ties_seen + count_below(tbits);
-      if (t) {
-        if (trank < my_kt) keep = true;
-        else if (mask_row)
-          __hip_atomic_fetch_and(my_stage + ((e & 0xFFFFu) >> 5), ~(1u << (e & 31u)),
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t tincl = KP == 1 ? count_below(ballot(tc != 0u)) + tc : scan_incl_u32(tc);
+      uint32_t trank = ties_seen + tincl - tc;
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        if ((tb >> k) & 1u) {
+          if (trank < my_kt) kb |= 1u << k;
+          else if (mask_row)
+            __hip_atomic_fetch_and(my_stage + ((e[k] & 0xFFFFu) >> 5), ~(1u << (e[k] & 31u)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          ++trank;
+        }
       }
-      ties_seen += (uint32_t)__popcll(tbits);
+      ties_seen += KP == 1 ? (uint32_t)__popcll(ballot(tc != 0u)) : readlane_u32(tincl, 63);
     }
-    const uint64_t kbits = ballot(keep);
-    const uint32_t pos = pos_base + count_below(kbits);
-    const int id = (int)(sl.wb + (e & 0xFFFFu));
-    double q = 0.0;
-    if (keep) {
-      q = wtab[tab_base - (e >> 16)] * inv_wp;
-      const float qf = (float)q;
-      if (ids_row && pos < cap) ids_row[pos] = id;
-      if (probs_row && pos < cap) probs_row[pos] = qf;
-      if (dense_row) dense_row[id] = qf;
-      if (q > 0.0) last_pos_id = id;
+    const uint32_t kc = (uint32_t)__popc(kb);
+    const uint32_t kincl = KP == 1 ? count_below(ballot(kc != 0u)) + kc : scan_incl_u32(kc);
+    uint32_t pos = pos_base + kincl - kc;
+    double qv[4];
+    double lane_sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      qv[k] = 0.0;
+      if ((kb >> k) & 1u) {
+        const int id = (int)(sl.wb + (e[k] & 0xFFFFu));
+        const double q = wtab[tab_base - (e[k] >> 16)] * inv_wp;
+        qv[k] = q;
+        lane_sum += q;
+        const float qf = (float)q;
+        if (ids_row && pos < cap) ids_row[pos] = id;
+        if (probs_row && pos < cap) probs_row[pos] = qf;
+        if (dense_row) dense_row[id] = qf;
+        if (q > 0.0) last_pos_id = id;
+        ++pos;
+      }
     }
-    pos_base += (uint32_t)__popcll(kbits);
+    pos_base += KP == 1 ? (uint32_t)__popcll(ballot(kc != 0u)) : readlane_u32(kincl, 63);
     if (SAMPLE && w == sw && my_token < 0) {
-      const double incl = scan_incl_f64(q);
-      const uint64_t hbits = ballot(keep && u < cbase + incl);
-      if (hbits) my_token = __shfl(id, __ffsll((unsigned long long)hbits) - 1, 64);
+      const double incl = scan_incl_f64(lane_sum);
+      double cu = cbase + (incl - lane_sum);
+      int hit = -1;
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        cu += qv[k];
+        if (hit < 0 && ((kb >> k) & 1u) && u < cu) hit = (int)(sl.wb + (e[k] & 0xFFFFu));
+      }
+      const uint64_t hbits = ballot(hit >= 0);
+      if (hbits) my_token = __shfl(hit, __ffsll((unsigned long long)hbits) - 1, 64);
       cbase += readlane_f64(incl, 63);
     }
   }
+  };
+  if (long_pool) walk_d(std::integral_constant<int, 4>{});
+  else walk_d(std::integral_constant<int, 1>{});
   if (mask_row) {
     for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
   }
