@@ -399,3 +399,30 @@ def test_topp_background_extremes(qs):
     # candidate keys spanning more than the 1024-key histogram: some rows are
     # settled by pivot rounds on the pool (more rounds than the two scans)
     assert (dbg[:, 1] >= 3).any(), dbg.tolist()
+
+
+@pytest.mark.gpu
+def test_small_temperature_large_logits(qs):
+    """bf16 rows with logits in the upper exact binades (spacing 1 and 2) and
+    temperatures down to 0.001: the weights (v - m) / T of values above the
+    maximum would overflow, so the value-histogram path must start the run
+    that holds the maximum at the maximum. Every row is settled by that path
+    (no search rounds) and must match the oracle."""
+    rng = np.random.default_rng(91)
+    B, V = 12, 9000
+    z = (300.0 + 20.0 * rng.standard_normal((B, V))).astype(np.float32)
+    z[6:] = (450.0 + 15.0 * rng.standard_normal((6, V))).astype(np.float32)
+    z = np.minimum(z, 510.0)
+    T = np.array([0.001, 0.005, 0.02, 0.1, 0.001, 0.02] * 2, np.float32)
+    k = np.array([0, 5, 50, 0, 3, 0, 0, 7, 0, 100, 1, 0], np.int32)
+    p = np.array([0.9, 1.0, 0.5, 0.99, 0.7, 0.3, 0.95, 1.0, 0.6, 0.8, 1.0, 0.999],
+                 np.float32)
+    bits = workloads._random_bitmask(rng, B, V, 0.5)
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rep, out = check_workload(qs, w, seed=6)
+    assert (out["status"].cpu().numpy() == 0).all()
+    dbg = out["debug"].cpu().numpy()
+    assert (dbg[:, 1] == 0).all(), dbg.tolist()

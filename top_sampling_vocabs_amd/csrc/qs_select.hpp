@@ -276,36 +276,35 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // -- fp64 masses relative to the maximum, block prefix sums in rank order -------------
   const double m = sel::rho_value(rho_top);
   // this run's 16 values are one spacing d apart, descending: their weights
-  // are w0, w0 rh, ..., w0 rh^15 with w0 = exp((v0 - m) / T), rh = exp(-d / T)
-  auto run_w0 = [&]() { return exp64((sel::rho_value(16u * (uint32_t)tid) - m) * invT); };
+  // are w0, w0 rh, ..., w0 rh^15 with w0 = exp((v0 - m) / T), rh = exp(-d / T).
+  // Ranks above the maximum hold no token; the run holding the maximum starts
+  // its weights there (w = 1), so no weight above 1 is ever formed (it could
+  // overflow at a small T)
+  auto run_w0 = [&]() {
+    const uint32_t b = max(16u * (uint32_t)tid, rho_top);
+    return exp64((sel::rho_value(b) - m) * invT);
+  };
   auto run_rh = [&]() {
     const uint32_t mag0 = sel::rho_mag(16u * (uint32_t)tid);
     return exp64(-ldexp(1.0, (int)(mag0 >> 7) - 134) * invT);
   };
   double mt = 0.0;
   if (run_t) {
-    const uint4* const h4 = reinterpret_cast<const uint4*>(hist + sel::run_bin0(tid));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = h4[q];
-      ct += (v.x + v.y) + (v.z + v.w);
-    }
-  }
-  __asm__ volatile("" ::: "memory");  // the counts are read again below, not held
-  if (run_t && ct) {
     const uint32_t rho0 = 16u * (uint32_t)tid;
     const double w0 = run_w0();
     const double rh = run_rh();
-    // Horner from the last rank down, one quad of counts per round
+    // the run's counts (four quads, read at once) and their Horner sum from
+    // the last rank down
+    uint32_t c4[4][4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) run_quad(qd, c4[qd]);
     double h = 0.0;
-#pragma unroll 1
+#pragma unroll
     for (int qd = 3; qd >= 0; --qd) {
-      uint32_t c4[4];
-      run_quad(qd, c4);
-      h = fma(h, rh, (double)c4[3]);
-      h = fma(h, rh, (double)c4[2]);
-      h = fma(h, rh, (double)c4[1]);
-      h = fma(h, rh, (double)c4[0]);
+      ct += (c4[qd][0] + c4[qd][1]) + (c4[qd][2] + c4[qd][3]);
+#pragma unroll
+      for (int k = 3; k >= 0; --k)
+        if (rho0 + (uint32_t)(4 * qd + k) >= rho_top) h = fma(h, rh, (double)c4[qd][k]);
     }
     mt = w0 * h;
     // the weight table: every rank from the maximum down, as far as it reaches
@@ -314,8 +313,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
 #pragma unroll 1
       for (int i = 0; i < 16; ++i) {
         const uint32_t rho = rho0 + (uint32_t)i;
-        if (rho >= rho_top && rho < rho_top + (uint32_t)sel::kTab) wtab[rho - rho_top] = wi;
-        wi *= rh;
+        if (rho >= rho_top) {
+          if (rho < rho_top + (uint32_t)sel::kTab) wtab[rho - rho_top] = wi;
+          wi *= rh;
+        }
       }
     }
   }
@@ -386,9 +387,11 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
             info.sel_d[0] = mb + (double)(kq - cum) * wi;
             info.sel_d[1] = wi;
           }
-          cum += ci;
-          mb += (double)ci * wi;
-          wi *= rh;
+          if ((uint32_t)(16 * tid + 4 * qd + k) >= rho_top) {  // (no token above)
+            cum += ci;
+            mb += (double)ci * wi;
+            wi *= rh;
+          }
         }
       }
     }
@@ -429,12 +432,14 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
           const uint32_t rho = (uint32_t)(16 * tid + 4 * qd + k);
           // tokens of this value inside the top-k set
           const uint32_t ci = !topk_on || rho < rho_k ? c4[k] : (rho == rho_k ? nk_k : 0u);
-          const double nb = mb + (double)ci * wi;
-          if (ci && mb < target && nb >= target) {
-            hit_rho = rho; hit_c = ci; hit_mb = mb; hit_w = wi;
+          if (rho >= rho_top) {  // (no token above)
+            const double nb = mb + (double)ci * wi;
+            if (ci && mb < target && nb >= target) {
+              hit_rho = rho; hit_c = ci; hit_mb = mb; hit_w = wi;
+            }
+            mb = nb;
+            wi *= rh;
           }
-          mb = nb;
-          wi *= rh;
         }
       }
       if (hit_rho != sel::kNone) {
