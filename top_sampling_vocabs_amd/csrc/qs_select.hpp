@@ -707,8 +707,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         qv[k] = q;
         lane_sum += q;
         const float qf = (float)q;
-        if (ids_row && pos < cap) ids_row[pos] = id;
-        if (probs_row && pos < cap) probs_row[pos] = qf;
+        // (streaming stores: the outputs go straight on to memory instead of
+        // waiting in L2 for the end of the kernel)
+        if (ids_row && pos < cap) __builtin_nontemporal_store(id, ids_row + pos);
+        if (probs_row && pos < cap) __builtin_nontemporal_store(qf, probs_row + pos);
         if (dense_row) dense_row[id] = qf;
         if (q > 0.0) last_pos_id = id;
         ++pos;
@@ -733,7 +735,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   if (long_pool) walk_d(std::integral_constant<int, 4>{});
   else walk_d(std::integral_constant<int, 1>{});
   if (mask_row) {
-    for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
+    for (int i = lane; i < sw1 - sw0; i += 64)
+      __builtin_nontemporal_store(my_stage[i], mask_row + sw0 + i);
   }
   // the token: from wave sw; if rounding left u at or above wave sw's last
   // cumulative sum, that wave's last kept id with q > 0; if u lies past every
