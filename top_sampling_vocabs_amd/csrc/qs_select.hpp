@@ -374,7 +374,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       uint32_t cum = c_excl;
       const double rh = run_rh();
       double mb = m_excl, wi = run_w0();
-#pragma unroll 1
+#pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         uint32_t c4[4];
         run_quad(qd, c4);
@@ -423,7 +423,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       // the crossing value of this run (at most one: the sum only grows)
       uint32_t hit_rho = sel::kNone, hit_c = 0u;
       double hit_mb = 0.0, hit_w = 0.0;
-#pragma unroll 1
+#pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         uint32_t c4[4];
         run_quad(qd, c4);
