@@ -1532,8 +1532,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     }
   });
   // this wave's mask words
-  if (mask_row && stage_ok) {
-    for (int i = lane; i < sw1 - sw0; i += 64) mask_row[sw0 + i] = my_stage[i];
+  if (mask_row && stage_ok) {  // streaming stores: on to memory, not held in L2
+    for (int i = lane; i < sw1 - sw0; i += 64)
+      __builtin_nontemporal_store(my_stage[i], mask_row + sw0 + i);
   }
   // the token: from wave sw; if rounding left u at or above wave sw's last
   // cumulative sum, that wave's last kept id with q > 0; if u lies past every
