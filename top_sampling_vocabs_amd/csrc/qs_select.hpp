@@ -531,9 +531,12 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         for (;;) {
           const bool on = cb != 0u;
           if (!ballot(on)) break;
-          const uint32_t j = (uint32_t)__builtin_ctz(cb | 0x100u);
+          // lowest set bit (all ones for an idle lane: its reads land in the
+          // LDS next to its chunk and its entry goes to its dump slot)
+          uint32_t j;
+          __asm__("v_ffbl_b32 %0, %1" : "=v"(j) : "v"(cb));
           cb &= cb - 1u;
-          const uint32_t key = chunk_bits[j & 7u];
+          const uint32_t key = chunk_bits[j];
           *(on ? slot : dump) = (key << 16) + (e0 + j);
           ++slot;
         }
