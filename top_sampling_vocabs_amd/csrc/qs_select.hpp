@@ -646,9 +646,23 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const double inv_wp = 1.0 / w_p;
 
   // -- outputs --------------------------------------------------------------------------
-  int32_t* ids_row = a.cand_ids ? a.cand_ids + (size_t)r * a.cand_cap : nullptr;
-  float* probs_row = a.cand_probs ? a.cand_probs + (size_t)r * a.cand_cap : nullptr;
-  const uint32_t cap = (uint32_t)a.cand_cap;
+  // the output rows and the list capacity are held in VGPRs for the walk
+  // below (scalar registers are scarce there)
+  auto to_vgpr = [](uint32_t x) {
+    uint32_t v;
+    __asm__("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+    return v;
+  };
+  auto ptr_vgpr = [&](auto* ptr) {
+    const uint64_t b = (uint64_t)(uintptr_t)ptr;
+    return reinterpret_cast<decltype(ptr)>(
+        (uintptr_t)(((uint64_t)to_vgpr((uint32_t)(b >> 32)) << 32) | to_vgpr((uint32_t)b)));
+  };
+  int32_t* const ids_row =
+      a.cand_ids ? ptr_vgpr(a.cand_ids + (size_t)r * a.cand_cap) : nullptr;
+  float* const probs_row =
+      a.cand_probs ? ptr_vgpr(a.cand_probs + (size_t)r * a.cand_cap) : nullptr;
+  const uint32_t cap = to_vgpr((uint32_t)a.cand_cap);
   // this slice's mask words, gathered in LDS (a resident slice always fits)
   const int sw0 = sl.wb >> 5, sw1 = sl.we > sl.wb ? (sl.we + 31) >> 5 : sw0;
   uint32_t* const my_stage = stage[w];  // the keep bits, written by the compaction
