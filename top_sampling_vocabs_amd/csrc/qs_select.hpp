@@ -658,10 +658,13 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     return reinterpret_cast<decltype(ptr)>(
         (uintptr_t)(((uint64_t)to_vgpr((uint32_t)(b >> 32)) << 32) | to_vgpr((uint32_t)b)));
   };
-  int32_t* const ids_row =
-      a.cand_ids ? ptr_vgpr(a.cand_ids + (size_t)r * a.cand_cap) : nullptr;
-  float* const probs_row =
-      a.cand_probs ? ptr_vgpr(a.cand_probs + (size_t)r * a.cand_cap) : nullptr;
+  // (global address space: the stores stay global, not flat, instructions)
+  using gi32 = __attribute__((address_space(1))) int32_t;
+  using gf32 = __attribute__((address_space(1))) float;
+  gi32* const ids_row =
+      a.cand_ids ? (gi32*)ptr_vgpr(a.cand_ids + (size_t)r * a.cand_cap) : nullptr;
+  gf32* const probs_row =
+      a.cand_probs ? (gf32*)ptr_vgpr(a.cand_probs + (size_t)r * a.cand_cap) : nullptr;
   const uint32_t cap = to_vgpr((uint32_t)a.cand_cap);
   // this slice's mask words, gathered in LDS (a resident slice always fits)
   const int sw0 = sl.wb >> 5, sw1 = sl.we > sl.wb ? (sl.we + 31) >> 5 : sw0;
