@@ -129,6 +129,9 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
 
   // -- tables: legal pair masks, the cleared histogram, this slice's mask words ------
   uint32_t* const hist = reinterpret_cast<uint32_t*>(pool_raw);  // kBins + 64 dump bins
+  // the pair-mask table right after the histogram, at a small LDS offset that
+  // fits a load's immediate field (the pools overwrite both after the pass)
+  lut = reinterpret_cast<uint4*>(pool_raw + (sel::kBins + 64) * 4);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const uint32_t e = (uint32_t)(lane + 64 * q4);
