@@ -76,8 +76,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                            RowInfo& info) {
   using K = Keys<1>;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
-  // entries per wave; 64 dump slots and one step of the slice (64 lanes x 16 B) follow
-  constexpr uint32_t kPool = kCap - 64u - 256u;
+  // entries per wave; 64 dump slots and two steps of the slice (64 lanes x 32 B) follow
+  constexpr uint32_t kPool = kCap - 64u - 512u;
   constexpr int kMW = NL * (kStep / 32);
   constexpr int kML = (kMW + 63) / 64;
   int par = 0;
@@ -492,13 +492,12 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   uint32_t pcnt = 0u;
   const uint32_t t2m1 = ((raw_star - 1u) & 0xFFFFu) * 0x10001u;
   uint32_t* const dump = my_pool + kPool + lane;
-  // this lane's chunk of the current step, staged in LDS so that a round
-  // reads its token's bits by index
-  uint4* const my_chunk = reinterpret_cast<uint4*>(my_pool + kPool + 64u) + lane;
-  const uint16_t* const chunk_bits = reinterpret_cast<const uint16_t*>(my_chunk);
-  static_for<0, NL>([&](auto stc) {
-    constexpr int st = decltype(stc)::value;
-    const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+  // this lane's chunks of the current two steps, staged in LDS so that a
+  // round reads its token's bits by index (0..15 over both chunks)
+  uint4* const my_chunks = reinterpret_cast<uint4*>(my_pool + kPool + 64u) + 2 * lane;
+  const uint16_t* const chunk_bits = reinterpret_cast<const uint16_t*>(my_chunks);
+  auto keep_bits = [&](const uint4& x) -> uint32_t {
+    const uint32_t r4[4] = {x.x, x.y, x.z, x.w};
     uint32_t dl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -508,26 +507,41 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     }
     const uint32_t cA = __builtin_amdgcn_perm(dl[1], dl[0], 0x0B0A0908u);
     const uint32_t cB = __builtin_amdgcn_perm(dl[3], dl[2], 0x0B0A0908u);
-    uint32_t cb = __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
-                                          __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
-    keep_bytes[st * 64] = (uint8_t)cb;
-    const uint32_t c = (uint32_t)__popc(cb);
-    const uint64_t any = ballot(c != 0u);
-    if (any) {
-      uint32_t excl, total;
-      if (!ballot(c > 1u)) {  // at most one per lane: one ballot
-        excl = count_below(any);
-        total = (uint32_t)__popcll(any);
-      } else {
-        const uint32_t incl = scan_incl_u32(c);
-        excl = incl - c;
-        total = readlane_u32(incl, 63);
-      }
+    return __builtin_amdgcn_sad_u8(cB & 0x80402010u, 0u,
+                                   __builtin_amdgcn_sad_u8(cA & 0x08040201u, 0u, 0u));
+  };
+  // two steps per group: one prefix sum and one set of rounds for both, so
+  // the rounds follow the fuller lane of the pair rather than of each step
+  static_for<0, (NL + 1) / 2>([&](auto gc) {
+    constexpr int s0 = 2 * decltype(gc)::value;
+    constexpr bool two = s0 + 1 < NL;
+    const uint32_t cb0 = keep_bits(xs[s0]);
+    keep_bytes[s0 * 64] = (uint8_t)cb0;
+    uint32_t cb1 = 0u;
+    if constexpr (two) {
+      cb1 = keep_bits(xs[s0 + 1]);
+      keep_bytes[(s0 + 1) * 64] = (uint8_t)cb1;
+    }
+    const uint32_t c0 = (uint32_t)__popc(cb0), c1 = (uint32_t)__popc(cb1);
+    if (ballot((cb0 | cb1) != 0u)) {
+      // both counts in one prefix sum (16-bit fields: each total is at most 512)
+      const uint32_t cc = c0 | (c1 << 16);
+      const uint32_t incl = scan_incl_u32(cc);
+      const uint32_t excl = incl - cc;
+      const uint32_t tot = readlane_u32(incl, 63);
+      const uint32_t t0 = tot & 0xFFFFu, t1 = tot >> 16;
       // a pool that would overflow is not written (the row then declines)
-      if (pcnt + total <= kPool) {
-        uint32_t* slot = my_pool + pcnt + excl;
-        const uint32_t e0 = (uint32_t)(lane_e + st * kStep - sl.wb);
-        if (c) *my_chunk = xs[st];
+      if (pcnt + t0 + t1 <= kPool) {
+        if (c0) my_chunks[0] = xs[s0];
+        if constexpr (two) {
+          if (c1) my_chunks[1] = xs[s0 + 1];
+        }
+        // round r writes the lane's r-th token: of step s0 at base0 + r while
+        // r < c0, of step s0 + 1 at base1 + (r - c0) after
+        uint32_t* slot = my_pool + pcnt + (excl & 0xFFFFu);
+        const int32_t jump = (int32_t)(t0 + (excl >> 16)) - (int32_t)((excl & 0xFFFFu) + c0);
+        const uint32_t e0 = (uint32_t)(lane_e + s0 * kStep - sl.wb);
+        uint32_t cb = cb0 | (cb1 << 8);
         // every lane writes each round, lanes without a token left to a slot
         // of their own past the pool, so the rounds need no branches (a lane
         // stays idle once it has run out, so its own slot may move on)
@@ -535,16 +549,18 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
           const bool on = cb != 0u;
           if (!ballot(on)) break;
           // lowest set bit (all ones for an idle lane: its reads land in the
-          // LDS next to its chunk and its entry goes to its dump slot)
+          // LDS next to its chunks and its entry goes to its dump slot)
           uint32_t j;
           __asm__("v_ffbl_b32 %0, %1" : "=v"(j) : "v"(cb));
           cb &= cb - 1u;
           const uint32_t key = chunk_bits[j];
-          *(on ? slot : dump) = (key << 16) + (e0 + j);
+          const uint32_t hi = (j >> 3) & 1u;  // token of the second step
+          const uint32_t off = e0 + j + hi * (uint32_t)(kStep - 8);
+          *(on ? slot + (hi ? jump : 0) : dump) = (key << 16) + off;
           ++slot;
         }
       }
-      pcnt = uni(pcnt + total);
+      pcnt = uni(pcnt + t0 + t1);
     }
   });
   // per wave: tokens above the boundary and their mass, ties at it (every
