@@ -155,19 +155,29 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // by lane (st & 3) * 16 + lane / 4 in mw[st / 4]
   const int bp_addr = (lane >> 2) * 4;               // byte address of lane lane / 4
   const uint32_t bsh = (uint32_t)(lane & 3) * 8u;     // this lane's byte of that word
-  auto legal_bits = [&](int st) -> uint32_t {
-    uint32_t m8 = 0xFFu;
-    if (bmrow) {
-      const uint32_t wd =
-          (uint32_t)__builtin_amdgcn_ds_bpermute(bp_addr + (st & 3) * 64, (int)mw[st >> 2]);
-      m8 = __builtin_amdgcn_ubfe(wd, bsh, 8u);
-    }
+  auto legal_word = [&](int st) -> uint32_t {
+    return bmrow ? (uint32_t)__builtin_amdgcn_ds_bpermute(bp_addr + (st & 3) * 64,
+                                                         (int)mw[st >> 2])
+                 : 0xFFFFFFFFu;
+  };
+  auto legal_bits = [&](int st, uint32_t wd) -> uint32_t {
+    uint32_t m8 = __builtin_amdgcn_ubfe(wd, bsh, 8u);
     if (sl.wb + (st + 1) * kStep > sl.we) {  // a step that ends past the slice
       const int rem = sl.we - (lane_e + st * kStep);
       m8 &= rem >= 8 ? 0xFFu : (rem > 0 ? (1u << rem) - 1u : 0u);
     }
     return m8;
   };
+  // the legal words run two steps ahead and the pair masks one step ahead of
+  // the counting, so no wait for them also waits for the step's LDS atomics
+  // (LDS requests complete in order)
+  uint32_t wdv[NL];
+  uint32_t mbv[NL];
+  uint4 nbv[NL];
+  wdv[0] = legal_word(0);
+  if constexpr (NL > 1) wdv[1] = legal_word(1);
+  mbv[0] = legal_bits(0, wdv[0]);
+  nbv[0] = lut[mbv[0]];
   uint32_t n_legal = 0u;
   // the largest legal raw bits read as signed 16-bit: positive values order
   // like their bits, negative ones lie below every positive one
@@ -175,10 +185,14 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const uint32_t dump2 = (uint32_t)(sel::kBins + lane) * 0x10001u;
   static_for<0, NL>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
-    const uint32_t mb = legal_bits(st);
-    n_legal += (uint32_t)__popc(mb);
+    if constexpr (st + 2 < NL) wdv[st + 2] = legal_word(st + 2);
+    if constexpr (st + 1 < NL) {
+      mbv[st + 1] = legal_bits(st + 1, wdv[st + 1]);
+      nbv[st + 1] = lut[mbv[st + 1]];
+    }
+    n_legal += (uint32_t)__popc(mbv[st]);
     issue(std::integral_constant<int, st + kLook>{});
-    const uint4 nb4 = lut[mb];
+    const uint4 nb4 = nbv[st];
     const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
     const uint32_t d4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
     uint32_t dm[4];
