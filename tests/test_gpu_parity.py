@@ -426,3 +426,28 @@ def test_small_temperature_large_logits(qs):
     assert (out["status"].cpu().numpy() == 0).all()
     dbg = out["debug"].cpu().numpy()
     assert (dbg[:, 1] == 0).all(), dbg.tolist()
+
+
+@pytest.mark.gpu
+def test_histogram_pool_overflow_declines(qs):
+    """bf16 rows whose kept set is larger than the value-histogram path's
+    pools (flat logits, p close to 1, every token legal): the path declines
+    and the truncation path settles the row (search rounds are reported);
+    rows with a small kept set stay on the histogram path (no rounds). Both
+    must match the oracle."""
+    rng = np.random.default_rng(123)
+    B, V = 6, 40000
+    z = (0.05 * rng.standard_normal((B, V))).astype(np.float32)
+    z[3:] = (3.0 * rng.standard_normal((3, V))).astype(np.float32)
+    T = np.ones(B, np.float32)
+    k = np.zeros(B, np.int32)
+    p = np.array([0.999, 0.99, 0.995, 0.5, 0.9, 0.7], np.float32)
+    bits = np.ones((B, V), bool)
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rep, out = check_workload(qs, w, seed=8, cand_cap=65536)
+    dbg = out["debug"].cpu().numpy()
+    assert (dbg[:3, 1] >= 1).all(), dbg.tolist()   # declined: truncation path rounds
+    assert (dbg[3:, 1] == 0).all(), dbg.tolist()   # settled by the value histogram
