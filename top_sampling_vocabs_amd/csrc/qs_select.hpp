@@ -762,8 +762,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         const float qf = (float)q;
         // (streaming stores: the outputs go straight on to memory instead of
         // waiting in L2 for the end of the kernel)
-        if (ids_row && pos < cap) __builtin_nontemporal_store(id, ids_row + pos);
-        if (probs_row && pos < cap) __builtin_nontemporal_store(qf, probs_row + pos);
+        if (pos < cap) {
+          if (ids_row) __builtin_nontemporal_store(id, ids_row + pos);
+          if (probs_row) __builtin_nontemporal_store(qf, probs_row + pos);
+        }
         if (dense_row) dense_row[id] = qf;
         if (q > 0.0) last_pos_id = id;
         ++pos;
