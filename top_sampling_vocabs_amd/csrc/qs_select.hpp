@@ -4,9 +4,9 @@
 // The kept set is the one a full stable sort by (-z, id) gives (page "Qrita",
 // key design 3). Here it is found without a sort, a truncation threshold or a
 // pivot search:
-//  1. the whole slice is requested at once and stays in VGPRs; every legal
-//     token is counted, as its step arrives, in an LDS histogram with one bin
-//     per bf16 value of magnitude in [2^-24, 512) and sign;
+//  1. the slice is held in VGPRs as it arrives; every legal token is counted
+//     in an LDS histogram with one bin per bf16 value of magnitude in
+//     [2^-24, 512) and sign (smaller and larger magnitudes in lumps);
 //  2. block-wide prefix sums over the bins, in descending value order, of the
 //     counts and of the fp64 masses exp((v - m) / T) give the k-th largest
 //     value with its tie quota (the page's stop test, evaluated at every value
@@ -16,9 +16,11 @@
 //     the wave's id-ordered pool; the tie walk, the 16-wave prefix and the
 //     output walk then write the mask, the id-ordered lists and the token.
 // A row this path cannot settle exactly returns false and takes the general
-// path: greedy rows, legal values outside the bins (magnitude >= 512 or below
-// 2^-24, infinities, NaN), a boundary at or below zero, a weight table or a
-// pool that would not fit.
+// path: greedy rows, invalid parameters, empty rows, legal magnitudes >= 512,
+// infinities or NaN, a maximum that is not a positive value of the bins, a
+// boundary at or below zero or past the weight table, a top-p cut that the
+// bound on the lumped small values leaves open, every token kept, and a pool
+// that would overflow.
 // Included by the kernels' translation unit inside namespace qs, after its
 // packed 16-bit helpers.
 #pragma once
@@ -250,21 +252,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // Thread t < kRuns owns ranks 16 t .. 16 t + 15. Its counts are read from LDS
   // again in every phase (the row is still held in VGPRs).
   const bool run_t = tid < sel::kRuns;
-  auto load_run = [&](uint32_t (&c)[16]) {
-    const uint4* const h4 = reinterpret_cast<const uint4*>(hist + sel::run_bin0(tid));
-    uint32_t asc[16];  // bin order
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = h4[q];
-      asc[4 * q] = v.x; asc[4 * q + 1] = v.y; asc[4 * q + 2] = v.z; asc[4 * q + 3] = v.w;
-    }
-    // rank order: positive runs descend through their bins, negative runs ascend
-    const bool pos = tid < (int)(sel::kExact / 16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = pos ? asc[15 - i] : asc[i];
-  };
-  // counts of ranks 16 tid + 4 qd .. + 3, in rank order (one LDS read; the
-  // rolled loops below take a quad per round)
+  // counts of ranks 16 tid + 4 qd .. + 3, in rank order (one LDS read)
   auto run_quad = [&](int qd, uint32_t (&c4)[4]) {
     const uint32_t b0 = sel::run_bin0(tid);
     const bool pos = tid < (int)(sel::kExact / 16);
