@@ -294,10 +294,12 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     return exp64(-ldexp(1.0, (int)(mag0 >> 7) - 134) * invT);
   };
   double mt = 0.0;
+  // the run's first weight and ratio, kept for the boundary searches
+  double w0 = 0.0, rh = 0.0;
   if (run_t) {
     const uint32_t rho0 = 16u * (uint32_t)tid;
-    const double w0 = run_w0();
-    const double rh = run_rh();
+    w0 = run_w0();
+    rh = run_rh();
     // the run's counts (four quads, read at once) and their Horner sum from
     // the last rank down
     uint32_t c4[4][4];
@@ -377,8 +379,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint32_t kq = (uint32_t)kk;
     if (run_t && c_excl < kq && kq <= c_excl + ct) {
       uint32_t cum = c_excl;
-      const double rh = run_rh();
-      double mb = m_excl, wi = run_w0();
+      double mb = m_excl, wi = w0;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         uint32_t c4[4];
@@ -423,8 +424,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     // sums below and the prefix sums differ by a few units in the last place
     // of the target's magnitude, far below the 1e-13 margin
     if (run_t && ct && m_excl < target && m_excl + mt >= target * (1.0 - 1e-13)) {
-      const double rh = run_rh();
-      double mb = m_excl, wi = run_w0();
+      double mb = m_excl, wi = w0;
       // the crossing value of this run (at most one: the sum only grows)
       uint32_t hit_rho = sel::kNone, hit_c = 0u;
       double hit_mb = 0.0, hit_w = 0.0;
