@@ -556,9 +556,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
           __asm__("v_ffbl_b32 %0, %1" : "=v"(j) : "v"(cb));
           cb &= cb - 1u;
           const uint32_t key = chunk_bits[j];
-          const uint32_t hi = (j >> 3) & 1u;  // token of the second step
-          const uint32_t off = e0 + j + hi * (uint32_t)(kStep - 8);
-          *(on ? slot + (hi ? jump : 0) : dump) = (key << 16) + off;
+          // all ones for a token of the second step, else zero
+          const int32_t hm = __builtin_amdgcn_sbfe((int32_t)j, 3, 1);
+          const uint32_t off = e0 + j + ((uint32_t)hm & (uint32_t)(kStep - 8));
+          *(on ? slot + (hm & jump) : dump) = (key << 16) | off;
           ++slot;
         }
       }
