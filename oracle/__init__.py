@@ -9,7 +9,8 @@ never imports it.
 
 Modules:
 * ``sampling`` — fp64 definition: stable full-row sort, top-k, top-p, greedy,
-  statuses, inverse-CDF walk in token-id order, keep-mask packing.
+  statuses, inverse-CDF walk in token-id order, the drawn token's
+  log-probability, keep-mask packing.
 * ``exact``    — rational-arithmetic mode for the pages' worked examples and a
   brute-force subset enumerator for tiny vocabularies.
 * ``philox``   — Philox4x32-10 from its published definition (parity unpinned:
@@ -21,8 +22,8 @@ Modules:
 from .sampling import (  # noqa: F401
     ROW_OK, ROW_EMPTY, ROW_ALL_NEG_INF, ROW_NONFINITE, ROW_BAD_PARAM,
     ROW_CAND_OVERFLOW, TOP_P_BAND, RowResult, bf16_bits_to_float64,
-    legal_from_bitmask, filter_row, sample_from, keep_mask_words, argmax_row,
-    params_valid)
+    legal_from_bitmask, filter_row, sample_from, token_logprob, keep_mask_words,
+    argmax_row, params_valid)
 from .exact import exact_filter, brute_force_filter  # noqa: F401
 from .philox import philox4x32, uniform  # noqa: F401
 from .batch import decode_logits, filter_batch, sample_batch, argmax_batch  # noqa: F401

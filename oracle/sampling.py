@@ -222,6 +222,23 @@ def sample_from(kept, q, u):
     return int(kept[last_pos]), dist
 
 
+def token_logprob(res, token):
+    """Log-probability of the drawn token under the distribution it was drawn
+    from: after temperature, mask, top-k, top-p and renormalisation (page
+    "Sampling 系统设计：从 logits 到可控生成", section on logprobs: a sampler may
+    return the chosen token's log-probability and must say which distribution
+    it refers to; this is that reading). Greedy rows draw from a point mass,
+    so 0; error rows have no token, so NaN.
+    """
+    if res.status != ROW_OK or token < 0:
+        return float("nan")
+    if res.greedy:
+        return 0.0
+    i = int(np.searchsorted(res.kept, token))
+    assert i < len(res.kept) and int(res.kept[i]) == token, "token outside P"
+    return float(np.log(res.q[i]))
+
+
 def keep_mask_words(kept, V):
     """Packed keep mask for one row: uint32[ceil(V/32)], LSB-first."""
     W = (V + 31) // 32

@@ -414,3 +414,52 @@ def test_signed_zeros_tie():
     assert list(filter_row(z, 1.0, 1, 1.0).kept) == [1]
     assert list(filter_row(z, 1.0, 2, 1.0).kept) == [1, 2]
     assert oracle.argmax_row(z) == (oracle.ROW_OK, 1)
+
+
+# --- the drawn token's log-probability ---------------------------------------
+
+@pytest.mark.parametrize("ex", EXAMPLES, ids=[e["name"] for e in EXAMPLES])
+def test_token_logprob_worked_examples(ex):
+    """For every kept token of the pages' worked examples the log-probability
+    is the log of the page's exact renormalised fraction."""
+    probs = np.array([float(Fraction(x)) for x in ex["probs"]])
+    legal = None if ex["legal"] is None else np.array(ex["legal"])
+    res = filter_row(np.log(probs), 1.0 / ex["inv_t"], ex["k"], float(Fraction(ex["p"])), legal)
+    for tok, qf in zip(ex["kept"], ex["q"]):
+        want = np.log(float(Fraction(qf)))
+        assert abs(oracle.token_logprob(res, tok) - want) < 1e-6
+
+
+def test_token_logprob_log_softmax_without_truncation():
+    """With top-k and top-p off the final distribution is the softmax of z/T
+    over the legal tokens, so the log-probability is scipy's log-softmax."""
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(11)
+    z = rng.normal(0, 3, 300)
+    legal = rng.random(300) < 0.6
+    T = float(np.float32(0.7))  # the contract passes T as float32
+    res = filter_row(z, T, 0, 1.0, legal)
+    ls = log_softmax(z[legal] / T)
+    ids = np.flatnonzero(legal)
+    for j in (0, 17, 101, len(ids) - 1):
+        assert abs(oracle.token_logprob(res, int(ids[j])) - ls[j]) < 1e-12
+
+
+def test_token_logprob_uniform_and_degenerate():
+    # k equal logits kept by top-k: each has probability 1/k
+    res = filter_row(np.zeros(40), 1.0, 8, 1.0)
+    assert abs(oracle.token_logprob(res, 3) + np.log(8)) < 1e-15
+    # a single kept token: probability 1
+    z = np.arange(20, dtype=np.float64)
+    res = filter_row(z, 1.0, 1, 1.0)
+    assert oracle.token_logprob(res, 19) == 0.0
+    # greedy: a point mass
+    res = filter_row(z, 0.0, 0, 1.0)
+    assert res.greedy and oracle.token_logprob(res, 19) == 0.0
+    # error rows: no token
+    res = filter_row(np.full(20, np.nan), 1.0, 0, 1.0)
+    assert np.isnan(oracle.token_logprob(res, -1))
+    # the kept probabilities exponentiate back to one
+    res = filter_row(np.random.default_rng(3).normal(0, 2, 500), 1.3, 60, 0.8)
+    tot = sum(np.exp(oracle.token_logprob(res, int(t))) for t in res.kept)
+    assert abs(tot - 1.0) < 1e-12
