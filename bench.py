@@ -98,7 +98,7 @@ class Prepared:
             None if self.bm is None else P(self.bm.data_ptr()),
             0 if self.bm is None else self.bm.stride(0),
             P(self.seed.data_ptr()), P(self.offset.data_ptr()), None,
-            P(self.tokens.data_ptr()), P(self.keep.data_ptr()), P(self.cids.data_ptr()),
+            P(self.tokens.data_ptr()), None, P(self.keep.data_ptr()), P(self.cids.data_ptr()),
             P(self.cprobs.data_ptr()), P(self.ccount.data_ptr()), cand_cap, None,
             P(self.status.data_ptr()), None, flags, stream)
         self.lib = lib

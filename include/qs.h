@@ -138,13 +138,19 @@ QS_API int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V,
  * uniforms     [B] float64 in [0,1), optional: when given, row r uses
  *              u = uniforms[r] and offsets are neither read nor written.
  * tokens       [B] int32 out, required: the token, -1 on an error row.
+ * logprobs     [B] float32 out, optional: natural log of the drawn token's
+ *              probability under the distribution it was drawn from (after
+ *              temperature, mask, top-k, top-p and renormalisation; page
+ *              "Sampling 系统设计：从 logits 到可控生成", logprobs section: the
+ *              sampler may return it and must state which distribution it
+ *              refers to). 0 on greedy rows (a point mass), NaN on error rows.
  */
 QS_API int qs_sample(const void* logits, int dtype, int64_t B, int64_t V,
               int64_t row_stride, const float* temperature,
               const int32_t* top_k, const float* top_p,
               const uint32_t* bitmask, int64_t bitmask_stride,
               const uint64_t* seed, uint64_t* offset, const double* uniforms,
-              int32_t* tokens, uint32_t* keep_mask, int32_t* cand_ids,
+              int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
               float* cand_probs, int32_t* cand_count, int64_t cand_cap,
               float* dense_probs, int32_t* row_status, int32_t* debug_stats,
               uint32_t flags, void* stream);

@@ -155,3 +155,27 @@ def compare_tokens(res, tokens, rows, rep, uniforms=None, offsets_in=None,
                 rep.cdf_band += 1
             else:
                 rep.fail(f"row {r}: token {tokens[r]} != oracle (u={u}, dist={dmin:.3g})")
+
+
+LOGPROB_ATOL = 1e-6  # the probabilities' 1e-6 relative tolerance, on the log scale
+
+
+def compare_logprobs(res, tokens, logprobs, cand_count, rows, rep):
+    """The drawn token's log-probability against the oracle's, for the token the
+    GPU drew: NaN on error rows, 0 on greedy rows, else log q of that token
+    within LOGPROB_ATOL plus the float32 rounding of the result. Rows that kept
+    an adjacent top-p prefix (a different set, so different q) are skipped."""
+    tokens = tokens.cpu().numpy()
+    lp = logprobs.cpu().numpy().astype(np.float64)
+    cc = cand_count.cpu().numpy()
+    for r in rows:
+        rr = res[r]
+        want = oracle.token_logprob(rr, int(tokens[r]))
+        if rr.status != oracle.ROW_OK:
+            if not np.isnan(lp[r]):
+                rep.fail(f"row {r}: error row logprob {lp[r]}")
+            continue
+        if not rr.greedy and cc[r] != len(rr.kept):
+            continue
+        if not abs(lp[r] - want) <= LOGPROB_ATOL + 1.2e-7 * abs(want):
+            rep.fail(f"row {r}: logprob {lp[r]} != {want}")

@@ -80,14 +80,14 @@ def test_empty_batch_is_a_no_op(lib):
 
 def smp(lib, **kw):
     args = dict(logits=A16, dtype=1, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
-                bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16,
+                bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16, lp=None,
                 keep=None, cids=None, cprobs=None, ccount=None, cap=0, dense=None,
                 status=A16, dbg=None, flags=0, stream=None)
     args.update(kw)
     return lib.qs_sample(args["logits"], args["dtype"], args["B"], args["V"], args["stride"],
                          args["T"], args["k"], args["p"], args["bitmask"], args["bms"],
                          args["seed"], args["offset"], args["uni"], args["tokens"],
-                         args["keep"], args["cids"], args["cprobs"], args["ccount"],
+                         args["lp"], args["keep"], args["cids"], args["cprobs"], args["ccount"],
                          args["cap"], args["dense"], args["status"], args["dbg"],
                          args["flags"], args["stream"])
 
@@ -95,6 +95,7 @@ def smp(lib, **kw):
 @pytest.mark.parametrize("kw", [
     dict(tokens=None), dict(seed=None), dict(offset=None), dict(seed=None, offset=None),
     dict(offset=ctypes.c_void_p(0x200004)), dict(uni=ctypes.c_void_p(0x200004)),
+    dict(lp=ctypes.c_void_p(0x200002)),
     dict(stride=60), dict(V=-5),
 ])
 def test_sample_rejects_bad_arguments(lib, kw):

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import workloads
-from _harness import Report, compare_filter, compare_tokens, to_device, words_u32
+from _harness import (Report, compare_filter, compare_logprobs, compare_tokens, to_device,
+                      words_u32)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,8 @@ def run_all(qs, d, uniforms=None, flags=0, cand_cap=None, V=None):
     cap = cand_cap if cand_cap is not None else V
     out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
                     seed=d["seed"], offset=d["offset"], uniforms=uniforms,
-                    keep_mask=True, cand_cap=cap, dense=True, debug=True, flags=flags)
+                    keep_mask=True, cand_cap=cap, dense=True, debug=True, logprobs=True,
+                    flags=flags)
     torch.cuda.synchronize()
     return out
 
@@ -46,6 +48,7 @@ def check_workload(qs, w, rows=None, seed=0, flags=0, cand_cap=None, dense=True)
     rep = Report()
     compare_filter(w, res, out, rows, rep, check_dense=dense)
     compare_tokens(res, out["tokens"], rows, rep, uniforms=uni)
+    compare_logprobs(res, out["tokens"], out["logprobs"], out["cand_count"], rows, rep)
     # filter_mask gives the same mask and lists
     fm = qs.filter_mask(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
                         cand_cap=cand_cap or w.V, flags=flags)
@@ -110,6 +113,7 @@ def test_parity_ragged(qs, dtype, V, stream):
     rep = Report()
     compare_filter(w, res, out, range(B), rep)
     compare_tokens(res, out["tokens"], range(B), rep, uniforms=uni)
+    compare_logprobs(res, out["tokens"], out["logprobs"], out["cand_count"], range(B), rep)
     rep.check()
 
 
@@ -136,6 +140,9 @@ def test_path_invariance(qs):
             for key in ("keep_mask", "cand_count", "dense", "tokens", "status"):
                 assert torch.equal(base[key], alt[key]), (cfg, flags, key)
             assert lists_equal(base, alt), (cfg, flags)
+            # log q in fp64 from either path's weights, rounded to float32
+            assert np.allclose(base["logprobs"].cpu().numpy(), alt["logprobs"].cpu().numpy(),
+                               rtol=2.4e-7, atol=1e-9, equal_nan=True), (cfg, flags)
             dbg = alt["debug"].cpu().numpy()
             ok = base["status"].cpu().numpy() == 0
             if flags in (qs.FLAG_FORCE_MISS, qs.FLAG_NO_TRUNCATION,

@@ -64,7 +64,7 @@ def load(path=LIB_PATH):
         _p, _i32, _i64, _i64, _i64,
         _p, _p, _p,
         _p, _i64,
-        _p, _p, _p, _p,                      # seed, offset, uniforms, tokens
+        _p, _p, _p, _p, _p,                  # seed, offset, uniforms, tokens, logprobs
         _p, _p, _p, _p, _i64,
         _p, _p, _p, _u32, _p]
     lib.qs_argmax.restype = _i32
@@ -160,13 +160,16 @@ def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
 
 
 def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset=None,
-           uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False, flags=0):
+           uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False,
+           logprobs=False, flags=0):
     """Filter and draw one token per row.
 
     seed, offset: int64 [B] CUDA tensors holding the uint64 RNG state; offset is
     advanced in place by the randomness actually consumed. uniforms: float64
-    [B] to use fixed u values instead (offsets untouched). Returns a dict with
-    tokens [B], status [B] and the optional outputs of filter_mask.
+    [B] to use fixed u values instead (offsets untouched). logprobs: also
+    return the log-probability of each drawn token under the distribution it
+    was drawn from (float32 [B]). Returns a dict with tokens [B], status [B]
+    and the optional outputs of filter_mask.
     """
     import torch
     lib = load()
@@ -183,6 +186,8 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
     W = (V + 31) // 32
     out = {"tokens": torch.empty(B, dtype=torch.int32, device=dev),
            "status": torch.empty(B, dtype=torch.int32, device=dev)}
+    if logprobs:
+        out["logprobs"] = torch.empty(B, dtype=torch.float32, device=dev)
     if keep_mask:
         out["keep_mask"] = torch.empty((B, W), dtype=torch.int32, device=dev)
     if cand_cap:
@@ -199,7 +204,7 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
         _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
         _ptr(seed) if uniforms is None else None,
         _ptr(offset) if uniforms is None else None, _ptr(uniforms), _ptr(out["tokens"]),
-        _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
+        _ptr(out.get("logprobs")), _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
         _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
         _ptr(out["status"]), _ptr(out.get("debug")), int(flags), _stream(dev))
     _status(rc, "qs_sample")

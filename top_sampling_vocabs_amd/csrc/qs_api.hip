@@ -36,7 +36,8 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
                   int64_t row_stride, const float* temperature, const int32_t* top_k,
                   const float* top_p, const uint32_t* bitmask, int64_t bitmask_stride,
                   const uint64_t* seed, uint64_t* offset, const double* uniforms,
-                  int32_t* tokens, uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
+                  int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+                  float* cand_probs,
                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
                   int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* stream) {
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
@@ -57,8 +58,8 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   if (!aligned(temperature, 4) || !aligned(top_k, 4) || !aligned(top_p, 4) ||
       !aligned(row_status, 4) || !aligned(keep_mask, 4) || !aligned(cand_ids, 4) ||
       !aligned(cand_probs, 4) || !aligned(cand_count, 4) || !aligned(dense_probs, 4) ||
-      !aligned(debug_stats, 4) || !aligned(tokens, 4) || !aligned(seed, 8) ||
-      !aligned(offset, 8) || !aligned(uniforms, 8))
+      !aligned(debug_stats, 4) || !aligned(tokens, 4) || !aligned(logprobs, 4) ||
+      !aligned(seed, 8) || !aligned(offset, 8) || !aligned(uniforms, 8))
     return QS_ERR_INVALID_ARG;
 
   qs::FilterArgs a;
@@ -75,6 +76,7 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.offset = offset;
   a.uniforms = uniforms;
   a.tokens = tokens;
+  a.logprobs = logprobs;
   a.keep_mask = keep_mask;
   a.cand_ids = cand_ids;
   a.cand_probs = cand_probs;
@@ -99,7 +101,7 @@ int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V, int64_t 
                    float* dense_probs, int32_t* row_status, int32_t* debug_stats,
                    uint32_t flags, void* stream) {
   return filter_common(false, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
-                       bitmask, bitmask_stride, nullptr, nullptr, nullptr, nullptr, keep_mask,
+                       bitmask, bitmask_stride, nullptr, nullptr, nullptr, nullptr, nullptr, keep_mask,
                        cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
                        debug_stats, flags, stream);
 }
@@ -107,13 +109,13 @@ int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V, int64_t 
 int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
               const float* temperature, const int32_t* top_k, const float* top_p,
               const uint32_t* bitmask, int64_t bitmask_stride, const uint64_t* seed,
-              uint64_t* offset, const double* uniforms, int32_t* tokens, uint32_t* keep_mask,
-              int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              uint64_t* offset, const double* uniforms, int32_t* tokens, float* logprobs,
+              uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
               float* dense_probs, int32_t* row_status, int32_t* debug_stats, uint32_t flags,
               void* stream) {
   return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
-                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, keep_mask,
-                       cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
+                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
+                       keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
                        debug_stats, flags, stream);
 }
 

@@ -73,6 +73,20 @@ constexpr int kRingDepth[2] = {5, 10};
 constexpr int kStageWords = 320;      // packed-mask words of one slice held in LDS
 static_assert(kResidentMaxSteps * (kStep / 32) <= kStageWords, "stage holds a resident slice");
 
+// The drawn token of row r and, when asked for, the log of its probability
+// under the final (renormalised) distribution, the one it was drawn from.
+__device__ __forceinline__ void put_token(const FilterArgs& a, int r, int tok, double q) {
+  a.tokens[r] = tok;
+  if (a.logprobs) a.logprobs[r] = (float)log(q);
+}
+
+// Probability of the wave's last kept id with q > 0 (`last_id`, the wave-wide
+// maximum of each lane's last such id), read from the lane that holds it.
+__device__ __forceinline__ double last_token_q(int my_last_id, double my_last_q, int last_id) {
+  const uint64_t at = ballot(last_id >= 0 && my_last_id == last_id);
+  return at ? readlane_f64(my_last_q, __ffsll((unsigned long long)at) - 1) : 0.0;
+}
+
 #include "qs_select.hpp"
 
 // Relative error bound of one hardware exp2 (v_exp_f32), taken as 4 ulp.
@@ -226,7 +240,10 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     zero_outputs();
     if (tid == 0) {
       a.status[r] = code;
-      if (SAMPLE) a.tokens[r] = -1;
+      if (SAMPLE) {
+        a.tokens[r] = -1;
+        if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
+      }
       if (a.cand_count) a.cand_count[r] = 0;
       if (a.dbg) {
         a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
@@ -1457,7 +1474,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   uint32_t ties_seen = 0u;
   double cbase = my_cumw * inv_wp;
   int my_token = -1;       // set in wave sw
+  double my_q = 0.0;       // its probability
   int last_pos_id = -1;    // last kept id with q > 0 in this wave
+  double last_pos_q = 0.0;
   walk([&](const uint32_t (&key)[8], const uint32_t (&id)[8], uint32_t vm) {
     uint32_t tb = 0u, gb = 0u;
 #pragma unroll
@@ -1500,7 +1519,10 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         if (ids_row && pos < cap) ids_row[pos] = (int32_t)id[j];
         if (probs_row && pos < cap) probs_row[pos] = qf;
         if (dense_row) dense_row[id[j]] = qf;
-        if (q > 0.0) last_pos_id = (int)id[j];
+        if (q > 0.0) {
+          last_pos_id = (int)id[j];
+          last_pos_q = q;
+        }
         const int wi = (int)(id[j] >> 5);
         if (wi != mwi) {
           if (mwi >= 0 && mask_row) or_mask_word(mwi, mword);
@@ -1518,15 +1540,20 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       const double wtotal = readlane_f64(incl, 63);
       double c = cbase + (incl - lane_sum);
       int hit = -1;
+      double hq = 0.0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         c += qv[j];
-        if (hit < 0 && ((pb >> j) & 1u) && u < c) hit = (int)id[j];
+        if (hit < 0 && ((pb >> j) & 1u) && u < c) {
+          hit = (int)id[j];
+          hq = qv[j];
+        }
       }
       const uint64_t hbits = ballot(hit >= 0);
       if (hbits) {
         const int fl = __ffsll((unsigned long long)hbits) - 1;
         my_token = __shfl(hit, fl, 64);
+        my_q = readlane_f64(hq, fl);
       }
       cbase += wtotal;
     }
@@ -1540,13 +1567,17 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // cumulative sum, that wave's last kept id with q > 0; if u lies past every
   // wave, the last kept id with q > 0 of the row
   const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
-  if (SAMPLE && lane == 0) {
-    if (greedy) {
-      if (my_kt > 0u) a.tokens[r] = last_id;  // the one kept token lies in this wave
-    } else if (w == sw) {
-      a.tokens[r] = my_token >= 0 ? my_token : last_id;
-    } else if (sw < 0 && w == last_w) {
-      a.tokens[r] = last_id;
+  if (SAMPLE) {
+    const double last_q = last_token_q(last_pos_id, last_pos_q, last_id);
+    if (lane == 0) {
+      if (greedy) {
+        if (my_kt > 0u) put_token(a, r, last_id, 1.0);  // the one kept token is in this wave
+      } else if (w == sw) {
+        if (my_token >= 0) put_token(a, r, my_token, my_q);
+        else put_token(a, r, last_id, last_q);
+      } else if (sw < 0 && w == last_w) {
+        put_token(a, r, last_id, last_q);
+      }
     }
   }
 

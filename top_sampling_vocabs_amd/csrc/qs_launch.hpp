@@ -21,6 +21,7 @@ struct FilterArgs {
   uint64_t* offset;
   const double* uniforms;
   int32_t* tokens;
+  float* logprobs;        // optional: log q of the drawn token
   uint32_t* keep_mask;
   int32_t* cand_ids;
   float* cand_probs;

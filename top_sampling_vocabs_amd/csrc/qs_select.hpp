@@ -703,7 +703,10 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   uint32_t ties_seen = 0u;
   double cbase = my_cumw * inv_wp;
   int my_token = -1;
-  int last_pos_id = -1;
+  double my_q = 0.0;
+  // this lane's last kept entry with q > 0; entries never equal ~0u (their
+  // offset field stays below the slice length)
+  uint32_t last_e = ~0u;
   auto walk_d = [&](auto kpc) {
    constexpr int KP = decltype(kpc)::value;
    for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
@@ -756,7 +759,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
           if (probs_row) __builtin_nontemporal_store(qf, probs_row + pos);
         }
         if (dense_row) dense_row[id] = qf;
-        if (q > 0.0) last_pos_id = id;
+        if (q > 0.0) last_e = e[k];
         ++pos;
       }
     }
@@ -765,13 +768,21 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       const double incl = scan_incl_f64(lane_sum);
       double cu = cbase + (incl - lane_sum);
       int hit = -1;
+      double hq = 0.0;
 #pragma unroll
       for (int k = 0; k < KP; ++k) {
         cu += qv[k];
-        if (hit < 0 && ((kb >> k) & 1u) && u < cu) hit = (int)(sl.wb + (e[k] & 0xFFFFu));
+        if (hit < 0 && ((kb >> k) & 1u) && u < cu) {
+          hit = (int)(sl.wb + (e[k] & 0xFFFFu));
+          hq = qv[k];
+        }
       }
       const uint64_t hbits = ballot(hit >= 0);
-      if (hbits) my_token = __shfl(hit, __ffsll((unsigned long long)hbits) - 1, 64);
+      if (hbits) {
+        const int fl = __ffsll((unsigned long long)hbits) - 1;
+        my_token = __shfl(hit, fl, 64);
+        my_q = readlane_f64(hq, fl);
+      }
       cbase += readlane_f64(incl, 63);
     }
   }
@@ -785,10 +796,19 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // the token: from wave sw; if rounding left u at or above wave sw's last
   // cumulative sum, that wave's last kept id with q > 0; if u lies past every
   // wave, the last kept id with q > 0 of the row
+  const int last_pos_id = last_e == ~0u ? -1 : (int)(sl.wb + (last_e & 0xFFFFu));
   const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
-  if (SAMPLE && lane == 0) {
-    if (w == sw) a.tokens[r] = my_token >= 0 ? my_token : last_id;
-    else if (sw < 0 && w == last_w) a.tokens[r] = last_id;
+  if (SAMPLE) {
+    const double last_pos_q = last_e == ~0u ? 0.0 : wtab[tab_base - (last_e >> 16)] * inv_wp;
+    const double last_q = last_token_q(last_pos_id, last_pos_q, last_id);
+    if (lane == 0) {
+      if (w == sw) {
+        if (my_token >= 0) put_token(a, r, my_token, my_q);
+        else put_token(a, r, last_id, last_q);
+      } else if (sw < 0 && w == last_w) {
+        put_token(a, r, last_id, last_q);
+      }
+    }
   }
   if (tid == 0) {
     const bool over = (a.cand_ids || a.cand_probs) ? n_p > cap : false;
