@@ -463,3 +463,87 @@ def test_token_logprob_uniform_and_degenerate():
     res = filter_row(np.random.default_rng(3).normal(0, 2, 500), 1.3, 60, 0.8)
     tot = sum(np.exp(oracle.token_logprob(res, int(t))) for t in res.kept)
     assert abs(tot - 1.0) < 1e-12
+
+
+# --- exact speculative verification ------------------------------------------
+
+def _dyadic_dist(rng, n, den=64):
+    """n probabilities that are multiples of 1/den, summing to exactly 1, some 0."""
+    cuts = np.sort(rng.choice(np.arange(1, den), n - 1, replace=True))
+    w = np.diff(np.concatenate([[0], cuts, [den]])).astype(np.float64)
+    return (w / den).astype(np.float32)
+
+
+def _out_distribution(t_ids, t_p, d_ids, d_p, n_grid=512):
+    """Output distribution of the verifier when x ~ q, u_accept and u_resample
+    uniform: every x in the draft list weighted by q(x), both uniforms on a
+    midpoint grid. Also returns the acceptance rate."""
+    grid = (np.arange(n_grid) + 0.5) / n_grid
+    out = {}
+    acc_rate = 0.0
+    for x, qx in zip(d_ids, d_p):
+        if qx == 0.0:
+            continue
+        acc = 0
+        for u1 in grid:
+            st, tok, a, _ = oracle.spec_verify_row(t_ids, t_p, len(t_ids), len(t_ids), d_ids, d_p,
+                                                   len(d_ids), len(d_ids), int(x), u1, 0.5)
+            acc += a
+        pa = acc / n_grid
+        acc_rate += float(qx) * pa
+        out[int(x)] = out.get(int(x), 0.0) + float(qx) * pa
+        if pa < 1.0:
+            for u2 in grid:
+                st, tok, a, _ = oracle.spec_verify_row(t_ids, t_p, len(t_ids), len(t_ids), d_ids,
+                                                       d_p, len(d_ids), len(d_ids), int(x), 0.999999,
+                                                       u2)
+                if a == 0:
+                    out[tok] = out.get(tok, 0.0) + float(qx) * (1.0 - pa) / n_grid
+    return out, acc_rate
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_spec_verify_output_is_target(seed):
+    """The page's claim: accept-or-resample outputs exactly the target p, and the
+    acceptance rate is sum(min(p, q)) = 1 - TV(p, q) (grid resolution 1/512)."""
+    rng = np.random.default_rng(seed)
+    V = 9
+    ids = np.arange(V)
+    p = _dyadic_dist(rng, V)
+    q = _dyadic_dist(rng, V)
+    t_keep = p > 0
+    d_keep = q > 0
+    out, acc = _out_distribution(ids[t_keep], p[t_keep], ids[d_keep], q[d_keep])
+    for y in range(V):
+        assert abs(out.get(y, 0.0) - float(p[y])) < 4.0 / 512, (y, out.get(y), p[y])
+    assert abs(acc - float(np.minimum(p, q).sum())) < 2.0 / 512
+    assert abs(acc - (1.0 - 0.5 * float(np.abs(p - q).sum()))) < 2.0 / 512
+
+
+def test_spec_verify_special_cases():
+    ids = np.array([3, 7, 11, 20])
+    p = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    # identical distributions: every draft token is accepted
+    for x in ids:
+        for u1 in (0.0, 0.5, 0.999):
+            st, tok, a, _ = oracle.spec_verify_row(ids, p, 4, 4, ids, p, 4, 4, int(x), u1, 0.3)
+            assert st == oracle.ROW_OK and a == 1 and tok == x
+    # a draft token the target excludes is always rejected; the residual is
+    # p - q where positive: here only id 3 (p 0.5 > q 0.25) and id 11
+    q = np.array([0.25, 0.25, 0.0, 0.5], np.float32)   # id 11 has q 0 but is listed
+    d_ids = ids
+    t_ids = np.array([3, 7, 11])
+    tp = np.array([0.5, 0.25, 0.25], np.float32)
+    for u2, want in ((0.0, 3), (0.49, 3), (0.51, 11), (0.99, 11)):
+        st, tok, a, _ = oracle.spec_verify_row(t_ids, tp, 3, 3, d_ids, q, 4, 4, 20, 0.0, u2)
+        assert st == oracle.ROW_OK and a == 0 and tok == want, (u2, tok)
+    # accept iff u * q(x) < p(x): x = 7, p = q = 0.25 always; x = 3 (p > q) always
+    assert oracle.spec_verify_row(t_ids, tp, 3, 3, d_ids, q, 4, 4, 3, 0.999, 0.5)[2] == 1
+    # errors
+    assert oracle.spec_verify_row(t_ids, tp, 0, 3, d_ids, q, 4, 4, 3, 0.1, 0.1)[0] == oracle.ROW_EMPTY
+    assert oracle.spec_verify_row(t_ids, tp, 3, 2, d_ids, q, 4, 4, 3, 0.1, 0.1)[0] == \
+        oracle.ROW_CAND_OVERFLOW
+    assert oracle.spec_verify_row(t_ids, tp, 3, 3, d_ids, q, 4, 4, 5, 0.1, 0.1)[0] == \
+        oracle.ROW_BAD_PARAM
+    assert oracle.spec_verify_row(t_ids, tp, 3, 3, d_ids, q, 4, 4, 3, 1.0, 0.1)[0] == \
+        oracle.ROW_BAD_PARAM
