@@ -165,6 +165,44 @@ QS_API int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V,
               int64_t bitmask_stride, int32_t* tokens, int32_t* row_status,
               void* stream);
 
+/* Exact speculative-decoding verification of one draft token per row
+ * (page "第 9 讲 · 生成与推测解码", section 5.2: accept the draft token x with
+ * probability min(1, p(x)/q(x)); on rejection draw from max(0, p - q)
+ * renormalised, so that the output is distributed exactly as p).
+ *
+ * p (target) and q (draft) are candidate lists as qs_filter_mask / qs_sample
+ * write them: ids ascending and unique, float32 probabilities; a token outside
+ * a list has probability 0 in it. A row may be one position of a draft run;
+ * the caller keeps the accepted prefix.
+ *
+ * target_ids, target_probs [B][target_cap]; target_count [B] int32
+ * draft_ids, draft_probs   [B][draft_cap];  draft_count [B] int32
+ * draft_tokens [B] int32: x, drawn from the draft list
+ * u_accept, u_resample [B] float64 in [0,1): the row's two uniforms.
+ *              Accept iff u_accept * q(x) < p(x) (float64 on the widened list
+ *              values). Else the residual r(y) = max(0, p(y) - q(y)) over the
+ *              target list, R its sum, and the first y in id order whose
+ *              cumulative residual exceeds u_resample * R (the last y with
+ *              r(y) > 0 if rounding leaves none). If R == 0 (only through
+ *              the lists' rounding) the draw uses p itself.
+ * tokens, accepted, row_status [B] int32 out: the output token, 1 if it is
+ *              the accepted draft token else 0, and the row status:
+ *              QS_ROW_BAD_PARAM for a negative count, x missing from the
+ *              draft list or a uniform outside [0,1); QS_ROW_EMPTY for an
+ *              empty list (or a target list of zero mass); QS_ROW_CAND_OVERFLOW
+ *              when a count exceeds its capacity (the list is truncated). An
+ *              error row gets token -1 and accepted 0.
+ * Every pointer is required. Lists that are not ascending give unspecified
+ * tokens (every read stays within the counts and capacities). One kernel
+ * launch on `stream`; nothing is allocated. */
+QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* target_probs,
+                   const int32_t* target_count, int64_t target_cap,
+                   const int32_t* draft_ids, const float* draft_probs,
+                   const int32_t* draft_count, int64_t draft_cap,
+                   const int32_t* draft_tokens, const double* u_accept,
+                   const double* u_resample, int32_t* tokens, int32_t* accepted,
+                   int32_t* row_status, void* stream);
+
 /* Library version string (static storage). */
 QS_API const char* qs_version(void);
 

@@ -18,7 +18,8 @@ Decisions, in float64 on the float32 list values widened exactly:
             rounding leaves none, the last y with r(y) > 0
   R == 0    (rounding only: p <= q everywhere although p(x) < q(x)) draw from
             p itself the same way
-Row errors: EMPTY when either list is empty, CAND_OVERFLOW when either count
+Row errors: BAD_PARAM for a negative count; EMPTY when either list is empty
+(or the target list holds no positive probability); CAND_OVERFLOW when either count
 exceeds its list's capacity (the list is truncated, so p or q is unknown),
 BAD_PARAM when x is not in the draft list or a uniform lies outside [0, 1).
 """
@@ -55,6 +56,8 @@ def spec_verify_row(t_ids, t_probs, t_count, t_cap, d_ids, d_probs, d_count, d_c
                     x, u_accept, u_resample):
     """Returns (status, token, accepted, distance); distance is how close the
     resampling target came to a CDF step (inf when nothing was resampled)."""
+    if t_count < 0 or d_count < 0:
+        return ROW_BAD_PARAM, -1, 0, np.inf
     if t_count == 0 or d_count == 0:
         return ROW_EMPTY, -1, 0, np.inf
     if t_count > t_cap or d_count > d_cap:
@@ -80,6 +83,8 @@ def spec_verify_row(t_ids, t_probs, t_count, t_cap, d_ids, d_probs, d_count, d_c
         P = 0.0
         for v in t_p:
             P += float(v)
+        if not P > 0.0:  # every listed target probability underflowed
+            return ROW_EMPTY, -1, 0, np.inf
         tok, dist = _inverse_cdf(t_ids, t_p, u_resample * P)
     return ROW_OK, tok, 0, dist
 

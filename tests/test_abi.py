@@ -114,3 +114,18 @@ def test_argmax_rejects_bad_arguments(lib):
     assert am(stride=10) == _lib.QS_ERR_INVALID_ARG  # 40 bytes is not a multiple of 16
     assert am(V=0) == _lib.QS_ERR_INVALID_ARG
     assert am(B=0) == _lib.QS_OK
+
+
+def test_spec_verify_rejects_bad_arguments(lib):
+    def sv(**kw):
+        a = dict(B=2, tids=A16, tp=A16, tc=A16, tcap=8, dids=A16, dp=A16, dc=A16, dcap=8,
+                 x=A16, u1=A8, u2=A8, tok=A16, acc=A16, status=A16, stream=None)
+        a.update(kw)
+        return lib.qs_spec_verify(a["B"], a["tids"], a["tp"], a["tc"], a["tcap"], a["dids"],
+                                  a["dp"], a["dc"], a["dcap"], a["x"], a["u1"], a["u2"],
+                                  a["tok"], a["acc"], a["status"], a["stream"])
+    for kw in (dict(B=-1), dict(tcap=0), dict(dcap=0), dict(tids=None), dict(dp=None),
+               dict(x=None), dict(u1=None), dict(u2=ctypes.c_void_p(0x200004)),
+               dict(acc=ctypes.c_void_p(0x200002)), dict(status=None)):
+        assert sv(**kw) == _lib.QS_ERR_INVALID_ARG, kw
+    assert sv(B=0) == _lib.QS_OK

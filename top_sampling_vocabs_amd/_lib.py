@@ -33,7 +33,7 @@ FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
-EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_version")
+EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_version")
 
 _lib = None
 
@@ -69,6 +69,12 @@ def load(path=LIB_PATH):
         _p, _p, _p, _u32, _p]
     lib.qs_argmax.restype = _i32
     lib.qs_argmax.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
+    lib.qs_spec_verify.restype = _i32
+    lib.qs_spec_verify.argtypes = [
+        _i64, _p, _p, _p, _i64,              # B, target ids, probs, count, cap
+        _p, _p, _p, _i64,                    # draft ids, probs, count, cap
+        _p, _p, _p,                          # draft tokens, u_accept, u_resample
+        _p, _p, _p, _p]                      # tokens, accepted, row_status, stream
     lib.qs_version.restype = ctypes.c_char_p
     lib.qs_version.argtypes = []
     if path == LIB_PATH:
@@ -224,3 +230,37 @@ def argmax(logits, bitmask=None):
                        _ptr(tokens), _ptr(status), _stream(dev))
     _status(rc, "qs_argmax")
     return tokens, status
+
+
+def spec_verify(target_ids, target_probs, target_count, draft_ids, draft_probs, draft_count,
+                draft_tokens, u_accept, u_resample):
+    """Exact speculative verification of one draft token per row over candidate
+    lists (as filter_mask / sample return them). Returns a dict with tokens,
+    accepted and status, int32 [B] each."""
+    import torch
+    lib = load()
+    B = int(draft_tokens.shape[0])
+    dev = draft_tokens.device
+    for t, dt, name in ((target_ids, torch.int32, "target_ids"),
+                        (target_probs, torch.float32, "target_probs"),
+                        (draft_ids, torch.int32, "draft_ids"),
+                        (draft_probs, torch.float32, "draft_probs")):
+        if t.dim() != 2 or t.shape[0] != B or t.dtype != dt or not t.is_contiguous() \
+                or t.device != dev:
+            raise ValueError(f"{name}: need a contiguous [B, cap] {dt} tensor on {dev}")
+    if target_ids.shape != target_probs.shape or draft_ids.shape != draft_probs.shape:
+        raise ValueError("ids and probs of a list must have the same shape")
+    _check_rowvec(target_count, B, torch.int32, "target_count")
+    _check_rowvec(draft_count, B, torch.int32, "draft_count")
+    _check_rowvec(draft_tokens, B, torch.int32, "draft_tokens")
+    _check_rowvec(u_accept, B, torch.float64, "u_accept")
+    _check_rowvec(u_resample, B, torch.float64, "u_resample")
+    out = {k: torch.empty(B, dtype=torch.int32, device=dev)
+           for k in ("tokens", "accepted", "status")}
+    rc = lib.qs_spec_verify(
+        B, _ptr(target_ids), _ptr(target_probs), _ptr(target_count), target_ids.shape[1],
+        _ptr(draft_ids), _ptr(draft_probs), _ptr(draft_count), draft_ids.shape[1],
+        _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
+        _ptr(out["tokens"]), _ptr(out["accepted"]), _ptr(out["status"]), _stream(dev))
+    _status(rc, "qs_spec_verify")
+    return out

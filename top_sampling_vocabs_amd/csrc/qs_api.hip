@@ -140,6 +140,41 @@ int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_s
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;
 }
 
+int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* target_probs,
+                   const int32_t* target_count, int64_t target_cap, const int32_t* draft_ids,
+                   const float* draft_probs, const int32_t* draft_count, int64_t draft_cap,
+                   const int32_t* draft_tokens, const double* u_accept,
+                   const double* u_resample, int32_t* tokens, int32_t* accepted,
+                   int32_t* row_status, void* stream) {
+  if (B < 0 || B > kMaxB) return QS_ERR_INVALID_ARG;
+  if (B == 0) return QS_OK;
+  if (target_cap < 1 || target_cap > kMaxV || draft_cap < 1 || draft_cap > kMaxV)
+    return QS_ERR_INVALID_ARG;
+  const void* req4[] = {target_ids, target_probs, target_count, draft_ids, draft_probs,
+                        draft_count, draft_tokens, tokens, accepted, row_status};
+  for (const void* p : req4)
+    if (!p || !aligned(p, 4)) return QS_ERR_INVALID_ARG;
+  if (!u_accept || !u_resample || !aligned(u_accept, 8) || !aligned(u_resample, 8))
+    return QS_ERR_INVALID_ARG;
+  qs::SpecArgs a;
+  a.t_ids = target_ids;
+  a.t_probs = target_probs;
+  a.t_count = target_count;
+  a.t_cap = target_cap;
+  a.d_ids = draft_ids;
+  a.d_probs = draft_probs;
+  a.d_count = draft_count;
+  a.d_cap = draft_cap;
+  a.x = draft_tokens;
+  a.u_accept = u_accept;
+  a.u_resample = u_resample;
+  a.tokens = tokens;
+  a.accepted = accepted;
+  a.status = row_status;
+  hipError_t e = qs::launch_spec(a, (int)B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
 const char* qs_version(void) { return "qs 0.1.0 gfx950"; }
 
 }  // extern "C"

@@ -44,8 +44,26 @@ struct ArgmaxArgs {
   int32_t* status;
 };
 
+struct SpecArgs {
+  const int32_t* t_ids;    // [B][t_cap] target list ids, ascending
+  const float* t_probs;
+  const int32_t* t_count;
+  int64_t t_cap;
+  const int32_t* d_ids;    // [B][d_cap] draft list
+  const float* d_probs;
+  const int32_t* d_count;
+  int64_t d_cap;
+  const int32_t* x;        // [B] draft tokens
+  const double* u_accept;
+  const double* u_resample;
+  int32_t* tokens;
+  int32_t* accepted;
+  int32_t* status;
+};
+
 int seg_for(int V);
 hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st);
 hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st);
+hipError_t launch_spec(const SpecArgs& a, int B, hipStream_t st);
 
 }  // namespace qs
