@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time K eager launches instead of one replay of a HIP graph "
                          "holding the K launches")
+    ap.add_argument("--spec", action="store_true",
+                    help="instead of the headline line, time the speculative verifier "
+                         "(qs_spec_verify) on candidate lists of the headline workload")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the headline line, print one line timing the path "
                          "switches (the Qrita page's ablation runs) on the headline "
@@ -212,6 +215,92 @@ ABLATION_RUNS = [
 ]
 
 
+class SpecPrepared:
+    """Target and draft candidate lists of one input set, made on the device by
+    the filter (draft logits = target logits + N(0, 0.5^2) noise, same T, k, p),
+    draft tokens drawn from the draft lists, and the ctypes argument tuple of
+    qs_spec_verify."""
+
+    def __init__(self, lib, w, cap, stream, seed):
+        import torch
+        import top_sampling_vocabs_amd as qs
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        z = torch.from_numpy(w.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        zd = (z.float() + 0.5 * torch.randn(z.shape, device=dev, generator=g)).to(torch.bfloat16)
+        T = torch.from_numpy(w.T).to(dev)
+        k = torch.from_numpy(w.k).to(dev)
+        p = torch.from_numpy(w.p).to(dev)
+        # sampled rows only (greedy rows have no draft distribution to verify)
+        T = torch.where(T > 0, T, torch.ones_like(T))
+        bm = None if w.bitmask is None else torch.from_numpy(w.bitmask.view(np.int32)).to(dev)
+        self.t = qs.filter_mask(z, T, k, p, bm, cand_cap=cap)
+        uni = torch.rand(w.B, dtype=torch.float64, device=dev, generator=g)
+        self.d = qs.sample(zd, T, k, p, bm, uniforms=uni, cand_cap=cap)
+        self.x = self.d["tokens"]
+        self.u1 = torch.rand(w.B, dtype=torch.float64, device=dev, generator=g)
+        self.u2 = torch.rand(w.B, dtype=torch.float64, device=dev, generator=g)
+        self.out = {n: torch.empty(w.B, dtype=torch.int32, device=dev)
+                    for n in ("tokens", "accepted", "status")}
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.args = (w.B, P(self.t["cand_ids"]), P(self.t["cand_probs"]), P(self.t["cand_count"]),
+                     cap, P(self.d["cand_ids"]), P(self.d["cand_probs"]), P(self.d["cand_count"]),
+                     cap, P(self.x), P(self.u1), P(self.u2), P(self.out["tokens"]),
+                     P(self.out["accepted"]), P(self.out["status"]), stream)
+        self.lib = lib
+
+    def call(self, stream=None, flags=None):
+        args = self.args if stream is None else self.args[:-1] + (stream,)
+        rc = self.lib.qs_spec_verify(*args)
+        if rc != 0:
+            raise RuntimeError(f"qs_spec_verify returned {rc}")
+
+    def bytes_read(self):
+        """Algorithmic bytes: every row reads its counts, token and uniforms; a
+        rejected row also reads the target list twice (mass, then draw) and the
+        draft list once (8 bytes an entry)."""
+        acc = self.out["accepted"].cpu().numpy()
+        ok = self.out["status"].cpu().numpy() == 0
+        tc = self.t["cand_count"].cpu().numpy().astype(np.int64)
+        dc = self.d["cand_count"].cpu().numpy().astype(np.int64)
+        rej = ok & (acc == 0)
+        return int(len(acc) * 28 + (16 * tc[rej] + 8 * dc[rej]).sum()), float(acc[ok].mean()), \
+            int(rej.sum()), int((~ok).sum())
+
+
+def spec_bench(args, lib, stream):
+    import torch
+    cap = 16384
+    preps = [SpecPrepared(lib, workloads.make(args.workload, seed=workloads.BASE_SEED +
+                                              args.workload + 1000 * i), cap, stream, 77 + i)
+             for i in range(args.sets)]
+    for i in range(args.warmup):
+        preps[i % len(preps)].call()
+    torch.cuda.synchronize()
+    ms, graph, cs = time_graph(preps, args.steps)
+    per = ms / args.steps
+    stats = [pr.bytes_read() for pr in preps]
+    nbytes = sum(s[0] for s in stats) / len(stats)
+    B = preps[0].args[0]
+    line = {
+        "metric": "speculative verification rows/sec over candidate lists, B=256 V=151936",
+        "value": round(B / (per * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "candidate lists (cap 16384) of the B=256 V=151936 bf16 batch as "
+                               "target, of the same logits + N(0, 0.5^2) as draft",
+                   "accept_rate": round(float(np.mean([s[1] for s in stats])), 4),
+                   "rejected_rows": [s[2] for s in stats], "error_rows": [s[3] for s in stats]},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,
+                     "bytes_per_launch": int(nbytes)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def ablation(args, lib, stream):
     """Time every path switch on the headline workload and at the page's
     ablation shape; every switch gives identical outputs (the path-invariance
@@ -289,6 +378,9 @@ def main():
     import top_sampling_vocabs_amd as qs
     lib = qs.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.spec:
+        spec_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        return
     if args.ablation:
         ablation(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         return

@@ -11,12 +11,14 @@
 // One workgroup of 16 waves per row:
 //   1. wave 0 finds x in the draft list and wave 1 in the target list, each by
 //      a 64-ary search (one load per lane per level, 2-3 levels at list
-//      lengths in the thousands);
+//      lengths in the thousands), while the other 14 waves stage the draft
+//      list in LDS (when it fits; an accepted row spends only bandwidth on
+//      it, a rejected one finds it there);
 //   2. accept iff u_accept * q(x) < p(x) in float64 on the widened list
 //      values; an accepted row is finished;
-//   3. a rejected row stages the draft list in LDS (when it fits), and each
-//      wave takes a contiguous sixteenth of the target list, 4 entries per
-//      lane per round, looks up q of each id by binary search and sums the
+//   3. for a rejected row each wave takes a contiguous sixteenth of the
+//      target list, 4 entries per lane per round with the entries of 4 rounds
+//      loaded together, looks up q of each id by binary search and sums the
 //      residual max(0, p - q) with the same wave scans the draw uses;
 //   4. the wave holding u_resample * R (R = the residual mass, summed in wave
 //      order) walks its range again and returns the first id whose
@@ -60,65 +62,54 @@ __device__ int wave_find(const int32_t* ids, int n, int x) {
   return eq ? lo + __ffsll((unsigned long long)eq) - 1 : -1;
 }
 
-struct SpecRow {
-  const int32_t* t_ids;
-  const float* t_p;
-  const int32_t* q_ids;  // the draft list, in LDS or in memory
-  const float* q_p;
-  int tc, dc;
-};
+constexpr int kSpecNR = 4;        // rounds whose entries are loaded together
 
-// Weights of the KP entries i0 + KP*lane + k (0 past `end`): the residual
-// max(0, p - q), or p itself when `use_p`. Returns the lane's sum in k order.
-__device__ double entry_weights(const SpecRow& s, int i0, int end, bool use_p,
-                                int (&id)[kSpecKP], double (&wv)[kSpecKP]) {
-  const int lane = lane_id();
-  int lo[kSpecKP], len[kSpecKP];
-  double p[kSpecKP];
-#pragma unroll
-  for (int k = 0; k < kSpecKP; ++k) {
-    const int i = i0 + kSpecKP * lane + k;
-    const bool v = i < end;
-    id[k] = v ? s.t_ids[i] : -1;
-    p[k] = v ? (double)s.t_p[i] : 0.0;
-    lo[k] = 0;
-    len[k] = v && !use_p ? s.dc : 0;
-  }
-  // lower bounds of the ids in the draft list, the KP searches interleaved
-  bool more = true;
-  while (more) {
-    more = false;
+// The draft list staged in LDS (when it fits).
+__shared__ int32_t s_ids[kSpecTile];
+__shared__ float s_p[kSpecTile];
+
+// Residual weights max(0, p - q) of one round's KP entries per lane (p itself
+// when `use_p`; 0 for absent entries, id < 0), q looked up in the draft list:
+// in LDS when STAGED, else in memory. The binary searches take the same
+// number of steps in every lane (it depends on the list length only), so the
+// KP searches of a lane run interleaved without divergence. Returns the
+// lane's sum in k order.
+template <bool STAGED>
+__device__ double round_weights(const int (&id)[kSpecKP], const float (&p)[kSpecKP], bool use_p,
+                                const int32_t* g_ids, const float* g_p, int dc,
+                                double (&wv)[kSpecKP]) {
+  const int32_t* q_ids = STAGED ? s_ids : g_ids;
+  const float* q_p = STAGED ? s_p : g_p;
+  double sum = 0.0;
+  if (use_p) {
 #pragma unroll
     for (int k = 0; k < kSpecKP; ++k) {
-      if (len[k] > 0) {
-        const int half = len[k] >> 1;
-        if (s.q_ids[lo[k] + half] < id[k]) {
-          lo[k] += half + 1;
-          len[k] -= half + 1;
-        } else {
-          len[k] = half;
-        }
-        more = more || len[k] > 0;
-      }
+      wv[k] = id[k] >= 0 ? (double)p[k] : 0.0;
+      sum += wv[k];
     }
+    return sum;
   }
-  double sum = 0.0;
+  int base[kSpecKP];
+#pragma unroll
+  for (int k = 0; k < kSpecKP; ++k) base[k] = 0;
+  for (int len = dc; len > 1;) {  // reads stay below base + len <= dc
+    const int half = len >> 1;
+#pragma unroll
+    for (int k = 0; k < kSpecKP; ++k) base[k] += q_ids[base[k] + half] < id[k] ? half : 0;
+    len -= half;
+  }
 #pragma unroll
   for (int k = 0; k < kSpecKP; ++k) {
-    double w = p[k];
-    if (!use_p && id[k] >= 0) {
-      const double q = (lo[k] < s.dc && s.q_ids[lo[k]] == id[k]) ? (double)s.q_p[lo[k]] : 0.0;
-      w = p[k] > q ? p[k] - q : 0.0;
-    }
-    wv[k] = w;
-    sum += w;
+    const int pos = base[k] + (q_ids[base[k]] < id[k] ? 1 : 0);  // lower bound
+    const double q = (pos < dc && q_ids[pos] == id[k]) ? (double)q_p[pos] : 0.0;
+    const double pk = (double)p[k];
+    wv[k] = id[k] >= 0 && pk > q ? pk - q : 0.0;
+    sum += wv[k];
   }
   return sum;
 }
 
 __global__ void __launch_bounds__(kSpecThreads) spec_verify_kernel(SpecArgs a) {
-  __shared__ int32_t s_ids[kSpecTile];
-  __shared__ float s_p[kSpecTile];
   __shared__ double s_wsum[kSpecWaves];
   __shared__ double s_px, s_qx;
   __shared__ int s_in_draft;
@@ -152,7 +143,30 @@ __global__ void __launch_bounds__(kSpecThreads) spec_verify_kernel(SpecArgs a) {
   const int32_t* d_ids = a.d_ids + (size_t)r * a.d_cap;
   const float* d_p = a.d_probs + (size_t)r * a.d_cap;
 
-  // -- p(x) and q(x) -------------------------------------------------------------------
+  // -- p(x) and q(x); meanwhile waves 2-15 stage the draft list (before the
+  // decision is known: an accepted row spends only bandwidth on it) ---------------
+  const bool staged = dc <= kSpecTile;
+  if (w >= 2 && staged) {
+    constexpr int kStagers = kSpecThreads - 128;
+    for (int i0 = tid - 128; i0 < dc; i0 += 4 * kStagers) {
+      int32_t iv[4];
+      float pv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // the four loads first, then the stores
+        const int i = i0 + k * kStagers;
+        iv[k] = i < dc ? d_ids[i] : 0;
+        pv[k] = i < dc ? d_p[i] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * kStagers;
+        if (i < dc) {
+          s_ids[i] = iv[k];
+          s_p[i] = pv[k];
+        }
+      }
+    }
+  }
   if (w == 0) {
     const int i = wave_find(d_ids, dc, x);
     if (lane == 0) {
@@ -174,25 +188,41 @@ __global__ void __launch_bounds__(kSpecThreads) spec_verify_kernel(SpecArgs a) {
   }
 
   // -- rejected: the residual mass, per wave ------------------------------------------
-  const bool staged = dc <= kSpecTile;
-  if (staged) {
-    for (int i = tid; i < dc; i += kSpecThreads) {
-      s_ids[i] = d_ids[i];
-      s_p[i] = d_p[i];
-    }
-  }
-  __syncthreads();
-  const SpecRow s{t_ids, t_p, staged ? s_ids : d_ids, staged ? s_p : d_p, tc, dc};
   const int per = (tc + kSpecWaves - 1) / kSpecWaves;
   const int b0 = min(w * per, tc), b1 = min(b0 + per, tc);
 
+  // the NR rounds' entries i0 + g*64*KP + KP*lane + k of this wave's range,
+  // loaded together (one memory latency per NR rounds)
+  constexpr int kRound = 64 * kSpecKP;
+  auto load_rounds = [&](int i0, int (&id)[kSpecNR][kSpecKP], float (&pv)[kSpecNR][kSpecKP]) {
+#pragma unroll
+    for (int g = 0; g < kSpecNR; ++g)
+#pragma unroll
+      for (int k = 0; k < kSpecKP; ++k) {
+        const int i = i0 + g * kRound + kSpecKP * lane + k;
+        id[g][k] = i < b1 ? t_ids[i] : -1;
+        pv[g][k] = i < b1 ? t_p[i] : 0.0f;
+      }
+  };
+  auto weights = [&](const int (&id)[kSpecKP], const float (&pv)[kSpecKP], bool use_p,
+                     double (&wv)[kSpecKP]) {
+    return staged ? round_weights<true>(id, pv, use_p, d_ids, d_p, dc, wv)
+                  : round_weights<false>(id, pv, use_p, d_ids, d_p, dc, wv);
+  };
   auto wave_mass = [&](bool use_p) {
     double cb = 0.0;
-    for (int i0 = b0; i0 < b1; i0 += 64 * kSpecKP) {
-      int id[kSpecKP];
-      double wv[kSpecKP];
-      const double ls = entry_weights(s, i0, b1, use_p, id, wv);
-      cb += readlane_f64(scan_incl_f64(ls), 63);
+    for (int i0 = b0; i0 < b1; i0 += kSpecNR * kRound) {
+      int id[kSpecNR][kSpecKP];
+      float pv[kSpecNR][kSpecKP];
+      load_rounds(i0, id, pv);
+#pragma unroll
+      for (int g = 0; g < kSpecNR; ++g) {
+        if (i0 + g * kRound < b1) {
+          double wv[kSpecKP];
+          const double ls = weights(id[g], pv[g], use_p, wv);
+          cb += readlane_f64(scan_incl_f64(ls), 63);
+        }
+      }
     }
     return cb;
   };
@@ -238,25 +268,29 @@ __global__ void __launch_bounds__(kSpecThreads) spec_verify_kernel(SpecArgs a) {
 
   int tok = -1, last_pos = -1;
   double cb = cbase;
-  for (int i0 = b0; i0 < b1; i0 += 64 * kSpecKP) {
-    int id[kSpecKP];
-    double wv[kSpecKP];
-    const double ls = entry_weights(s, i0, b1, use_p, id, wv);
-    const double incl = scan_incl_f64(ls);
-    double cu = cb + (incl - ls);
-    int hit = -1;
+  for (int i0 = b0; i0 < b1 && tok < 0; i0 += kSpecNR * kRound) {
+    int id[kSpecNR][kSpecKP];
+    float pv[kSpecNR][kSpecKP];
+    load_rounds(i0, id, pv);
 #pragma unroll
-    for (int k = 0; k < kSpecKP; ++k) {
-      cu += wv[k];
-      if (wv[k] > 0.0) last_pos = id[k];
-      if (hit < 0 && id[k] >= 0 && target < cu) hit = id[k];
+    for (int g = 0; g < kSpecNR; ++g) {
+      if (tok < 0 && i0 + g * kRound < b1) {
+        double wv[kSpecKP];
+        const double ls = weights(id[g], pv[g], use_p, wv);
+        const double incl = scan_incl_f64(ls);
+        double cu = cb + (incl - ls);
+        int hit = -1;
+#pragma unroll
+        for (int k = 0; k < kSpecKP; ++k) {
+          cu += wv[k];
+          if (wv[k] > 0.0) last_pos = id[g][k];
+          if (hit < 0 && id[g][k] >= 0 && target < cu) hit = id[g][k];
+        }
+        const uint64_t hb = ballot(hit >= 0);
+        if (hb) tok = __shfl(hit, __ffsll((unsigned long long)hb) - 1, 64);
+        cb += readlane_f64(incl, 63);
+      }
     }
-    const uint64_t hb = ballot(hit >= 0);
-    if (hb) {
-      tok = __shfl(hit, __ffsll((unsigned long long)hb) - 1, 64);
-      break;
-    }
-    cb += readlane_f64(incl, 63);
   }
   if (tok < 0) tok = (int)wave_reduce<OpMax>((uint32_t)(last_pos + 1)) - 1;
   if (lane == 0) {
