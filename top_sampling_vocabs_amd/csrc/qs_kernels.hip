@@ -73,11 +73,21 @@ constexpr int kRingDepth[2] = {5, 10};
 constexpr int kStageWords = 320;      // packed-mask words of one slice held in LDS
 static_assert(kResidentMaxSteps * (kStep / 32) <= kStageWords, "stage holds a resident slice");
 
+// Natural log of q >= 0 for a float32 output: q = m 2^e with m in [0.5, 1),
+// log2 m by the hardware single-precision log2 (about 1e-7 absolute on that
+// interval), the sum scaled by ln 2 in float64. A few instructions, where a
+// full float64 log would weigh on the code of the kernel it sits in.
+__device__ __forceinline__ float log_prob(double q) {
+  int e;
+  const double m = frexp(q, &e);
+  return (float)(((double)e + (double)__log2f((float)m)) * 0.6931471805599453);
+}
+
 // The drawn token of row r and, when asked for, the log of its probability
 // under the final (renormalised) distribution, the one it was drawn from.
 __device__ __forceinline__ void put_token(const FilterArgs& a, int r, int tok, double q) {
   a.tokens[r] = tok;
-  if (a.logprobs) a.logprobs[r] = (float)log(q);
+  if (a.logprobs) a.logprobs[r] = log_prob(q);
 }
 
 // Probability of the wave's last kept id with q > 0 (`last_id`, the wave-wide
@@ -1568,7 +1578,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // wave, the last kept id with q > 0 of the row
   const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
   if (SAMPLE) {
-    const double last_q = last_token_q(last_pos_id, last_pos_q, last_id);
+    const double last_q = a.logprobs ? last_token_q(last_pos_id, last_pos_q, last_id) : 0.0;
     if (lane == 0) {
       if (greedy) {
         if (my_kt > 0u) put_token(a, r, last_id, 1.0);  // the one kept token is in this wave

@@ -799,8 +799,11 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const int last_pos_id = last_e == ~0u ? -1 : (int)(sl.wb + (last_e & 0xFFFFu));
   const int last_id = (int)wave_reduce<OpMax>((uint32_t)(last_pos_id + 1)) - 1;
   if (SAMPLE) {
-    const double last_pos_q = last_e == ~0u ? 0.0 : wtab[tab_base - (last_e >> 16)] * inv_wp;
-    const double last_q = last_token_q(last_pos_id, last_pos_q, last_id);
+    double last_q = 0.0;
+    if (a.logprobs) {
+      const double last_pos_q = last_e == ~0u ? 0.0 : wtab[tab_base - (last_e >> 16)] * inv_wp;
+      last_q = last_token_q(last_pos_id, last_pos_q, last_id);
+    }
     if (lane == 0) {
       if (w == sw) {
         if (my_token >= 0) put_token(a, r, my_token, my_q);
