@@ -1,0 +1,71 @@
+"""History-dependent logit processors applied before the sampling contract.
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module.
+
+Page "Sampling 系统设计：从 logits 到可控生成", repetition-penalty section: a
+repetition penalty needs the sequence's earlier tokens and lowers the chance
+that a token seen before is picked again; the page leaves the exact formula
+open (frameworks differ in how they treat positive and negative logits) and
+asks for a simple version in the right place, as a logits processor fed by
+the sequence's history. The reading taken here, for each distinct token t in
+the row's history with 0 <= t < V:
+    z_t <- (z_t / r if z_t > 0 else z_t * r) - a
+with r the repetition penalty (> 0; 1 disables it) and a the presence
+penalty (0 disables it), each operation in float32 and rounded, the result
+stored in the logits' dtype (bfloat16 round-to-nearest-even). A token repeated
+in the history is penalised once. Other tokens are untouched. A row with r not
+finite or <= 0, a not finite, or a history count outside [0, capacity] is
+left unchanged and reported as BAD_PARAM. Applied to the raw logits, before
+temperature and the rest of the contract.
+"""
+
+import numpy as np
+
+from .sampling import ROW_BAD_PARAM, ROW_OK
+
+
+def _to_bf16_bits(x32):
+    """float32 -> bfloat16 bits, round to nearest even (NaN kept quiet)."""
+    b = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x32, np.float32))
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = ((b[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+def apply_penalties_row(z, dtype, history, count, cap, rep, pres):
+    """z: one row as stored (float32, or bfloat16 bits as uint16). Returns
+    (status, new row as stored)."""
+    rep = np.float32(rep)
+    pres = np.float32(pres)
+    if not (np.isfinite(rep) and rep > 0 and np.isfinite(pres)) or count < 0 or count > cap:
+        return ROW_BAD_PARAM, z.copy()
+    out = z.copy()
+    V = len(z)
+    seen = set()
+    for t in history[:count]:
+        t = int(t)
+        if t < 0 or t >= V or t in seen:
+            continue
+        seen.add(t)
+        if dtype == "bf16":
+            v = (np.uint32(z[t]) << np.uint32(16)).astype(np.uint32).view(np.float32)
+        else:
+            v = np.float32(z[t])
+        v = np.float32(v / rep) if v > 0 else np.float32(v * rep)
+        v = np.float32(v - pres)
+        out[t] = _to_bf16_bits(np.array([v]))[0] if dtype == "bf16" else v
+    return ROW_OK, out
+
+
+def apply_penalties_batch(logits, dtype, history, count, rep, pres):
+    """Row loop: (status [B] int32, new logits) in the input layout."""
+    B = logits.shape[0]
+    cap = history.shape[1]
+    out = logits.copy()
+    st = np.zeros(B, np.int32)
+    for r in range(B):
+        st[r], out[r] = apply_penalties_row(logits[r], dtype, history[r], int(count[r]), cap,
+                                            rep[r], pres[r])
+    return st, out

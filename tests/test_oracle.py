@@ -547,3 +547,38 @@ def test_spec_verify_special_cases():
         oracle.ROW_BAD_PARAM
     assert oracle.spec_verify_row(t_ids, tp, 3, 3, d_ids, q, 4, 4, 3, 1.0, 0.1)[0] == \
         oracle.ROW_BAD_PARAM
+
+
+# --- repetition / presence penalties ------------------------------------------
+
+def test_penalties_hand_example():
+    """Positive logits divide, negative multiply, then the presence penalty is
+    subtracted; a repeated history token is penalised once; ids outside [0, V)
+    are ignored; untouched tokens keep their bits."""
+    z = np.array([2.0, -2.0, 1.0, 0.5, -0.0], np.float32)
+    st, out = oracle.apply_penalties_row(z, "f32", np.array([0, 1, 0, 7, -1]), 5, 5, 2.0, 0.5)
+    assert st == oracle.ROW_OK
+    assert out.tolist() == [0.5, -4.5, 1.0, 0.5, -0.0]
+    # the identity parameters change nothing
+    st, out = oracle.apply_penalties_row(z, "f32", np.array([0, 1, 2, 3, 4]), 5, 5, 1.0, 0.0)
+    assert np.array_equal(out.view(np.uint32), z.view(np.uint32))
+    # count 0: nothing; bad parameters: unchanged and flagged
+    assert np.array_equal(oracle.apply_penalties_row(z, "f32", np.array([0]), 0, 1, 2.0, 1.0)[1], z)
+    for rep, pres, cnt in ((0.0, 0.0, 1), (-1.0, 0.0, 1), (np.nan, 0.0, 1), (1.0, np.inf, 1),
+                           (1.0, 0.0, 2), (1.0, 0.0, -1)):
+        st, out = oracle.apply_penalties_row(z, "f32", np.array([0]), cnt, 1, rep, pres)
+        assert st == oracle.ROW_BAD_PARAM and np.array_equal(out, z)
+
+
+def test_penalties_bf16_rounding():
+    """bf16 rows: the float32 result is rounded to nearest even. 1.0 / 3 =
+    0.33333334 lies between bf16 0.33203125 and 0.333984375, nearer the
+    latter; -1.0 * 1.5 - 0.0 = -1.5 is exact."""
+    z = np.array([0x3F80, 0xBF80], np.uint16)  # 1.0, -1.0
+    st, out = oracle.apply_penalties_row(z, "bf16", np.array([0]), 1, 1, 3.0, 0.0)
+    assert out[0] == 0x3EAB and out[1] == 0xBF80  # 0.333984375
+    st, out = oracle.apply_penalties_row(z, "bf16", np.array([1]), 1, 1, 1.5, 0.0)
+    assert out[1] == 0xBFC0  # -1.5
+    # ties round to even: 1 + 2^-8 (bits 0x3F808000) -> 1.0, 1 + 3*2^-8 -> 1 + 2^-6
+    assert oracle.penalties._to_bf16_bits(np.array([1 + 2**-8], np.float32))[0] == 0x3F80
+    assert oracle.penalties._to_bf16_bits(np.array([1 + 3 * 2**-8], np.float32))[0] == 0x3F82
