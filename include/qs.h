@@ -203,6 +203,31 @@ QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* tar
                    const double* u_resample, int32_t* tokens, int32_t* accepted,
                    int32_t* row_status, void* stream);
 
+/* Repetition and presence penalties over each row's history, applied in place
+ * to the logits before qs_filter_mask / qs_sample (page "Sampling 系统设计：从
+ * logits 到可控生成", repetition-penalty section: a history-dependent logits
+ * processor; the page leaves the formula open). For each distinct token t of
+ * row r's history with 0 <= t < V:
+ *   z[r][t] <- (z > 0 ? z / rep[r] : z * rep[r]) - pres[r]
+ * in float32, each operation rounded, stored in the logits' dtype (bfloat16:
+ * round to nearest even). A token repeated in the history is penalised once;
+ * ids outside [0, V) are ignored; every other logit is untouched (the work is
+ * proportional to the history, not to V). rep = 1 and pres = 0 change nothing.
+ *
+ * logits            [B][row_stride] float32 or bfloat16 (dtype), modified in
+ *                   place; aligned to its element size; V <= 2^20
+ * history           [B][history_cap] int32 token ids; history_count [B] int32
+ * repetition_penalty, presence_penalty [B] float32
+ * row_status        [B] int32 out: QS_ROW_OK, or QS_ROW_BAD_PARAM (row left
+ *                   unchanged) when rep is not finite or <= 0, pres is not
+ *                   finite, or the count lies outside [0, history_cap].
+ * Every pointer is required. One kernel launch on `stream`; nothing is
+ * allocated. */
+QS_API int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                       const int32_t* history, int64_t history_cap,
+                       const int32_t* history_count, const float* repetition_penalty,
+                       const float* presence_penalty, int32_t* row_status, void* stream);
+
 /* Library version string (static storage). */
 QS_API const char* qs_version(void);
 

@@ -33,7 +33,8 @@ FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
-EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_version")
+EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_apply_penalties",
+           "qs_version")
 
 _lib = None
 
@@ -75,6 +76,11 @@ def load(path=LIB_PATH):
         _p, _p, _p, _i64,                    # draft ids, probs, count, cap
         _p, _p, _p,                          # draft tokens, u_accept, u_resample
         _p, _p, _p, _p]                      # tokens, accepted, row_status, stream
+    lib.qs_apply_penalties.restype = _i32
+    lib.qs_apply_penalties.argtypes = [
+        _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
+        _p, _i64, _p,                        # history, history_cap, history_count
+        _p, _p, _p, _p]                      # repetition, presence, row_status, stream
     lib.qs_version.restype = ctypes.c_char_p
     lib.qs_version.argtypes = []
     if path == LIB_PATH:
@@ -264,3 +270,27 @@ def spec_verify(target_ids, target_probs, target_count, draft_ids, draft_probs, 
         _ptr(out["tokens"]), _ptr(out["accepted"]), _ptr(out["status"]), _stream(dev))
     _status(rc, "qs_spec_verify")
     return out
+
+
+def apply_penalties(logits, history, history_count, repetition, presence):
+    """Repetition and presence penalties over each row's history, applied to
+    logits in place. history: int32 [B, cap]; history_count: int32 [B];
+    repetition, presence: float32 [B]. Returns the row status (int32 [B])."""
+    import torch
+    lib = load()
+    if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a CUDA tensor [B, V] with unit column stride")
+    B, V = logits.shape
+    if history.dim() != 2 or history.shape[0] != B or history.dtype != torch.int32 \
+            or not history.is_contiguous() or history.device != logits.device:
+        raise ValueError("history must be a contiguous int32 [B, cap] tensor on the logits' device")
+    _check_rowvec(history_count, B, torch.int32, "history_count")
+    _check_rowvec(repetition, B, torch.float32, "repetition")
+    _check_rowvec(presence, B, torch.float32, "presence")
+    status = torch.empty(B, dtype=torch.int32, device=logits.device)
+    rc = lib.qs_apply_penalties(_ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+                                _ptr(history), history.shape[1], _ptr(history_count),
+                                _ptr(repetition), _ptr(presence), _ptr(status),
+                                _stream(logits.device))
+    _status(rc, "qs_apply_penalties")
+    return status

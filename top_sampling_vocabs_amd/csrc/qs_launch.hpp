@@ -61,9 +61,25 @@ struct SpecArgs {
   int32_t* status;
 };
 
+constexpr int kPenaltyMaxV = 1 << 20;  // vocabulary bitmap held in LDS
+
+struct PenaltyArgs {
+  uint8_t* logits;         // modified in place
+  int64_t row_bytes;
+  int V;
+  int dtype;
+  const int32_t* hist;     // [B][hist_cap] token ids
+  int64_t hist_cap;
+  const int32_t* count;
+  const float* rep;
+  const float* pres;
+  int32_t* status;
+};
+
 int seg_for(int V);
 hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st);
 hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st);
 hipError_t launch_spec(const SpecArgs& a, int B, hipStream_t st);
+hipError_t launch_penalty(const PenaltyArgs& a, int B, hipStream_t st);
 
 }  // namespace qs

@@ -1,0 +1,80 @@
+// Repetition and presence penalties over each row's history, in place.
+//
+// Page "Sampling 系统设计：从 logits 到可控生成", repetition-penalty section: the
+// penalty depends on the tokens the sequence produced before and belongs in a
+// logits processor fed by that history; the page leaves the formula open.
+// Taken here: for each distinct token t of the row's history (0 <= t < V),
+//   z_t <- (z_t > 0 ? z_t / r : z_t * r) - a
+// in float32, each operation rounded, stored back in the logits' dtype
+// (bfloat16 round to nearest even). Every other logit is untouched, so the
+// work is O(history), not O(V): the sampling kernels then read the modified
+// row as they read any other.
+//
+// One workgroup per row. A token repeated in the history is penalised once:
+// every history entry clears its token's bit in an LDS bitmap of the
+// vocabulary, then sets it with an atomic OR; the entry that finds the bit
+// clear owns the token and alone rewrites its logit, so no two threads write
+// the same element.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qs.h"
+#include "qs_launch.hpp"
+
+namespace qs {
+namespace {
+
+constexpr int kPenThreads = 256;
+__shared__ uint32_t s_seen[kPenaltyMaxV / 32];  // 128 KB
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (v != v) return (uint16_t)((b >> 16) | 0x40u);  // NaN stays NaN (quiet)
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cnt = a.count[r];
+  const float rep = a.rep[r], pres = a.pres[r];
+  const bool ok = isfinite(rep) && rep > 0.0f && isfinite(pres) && cnt >= 0 &&
+                  (int64_t)cnt <= a.hist_cap;
+  if (!ok) {
+    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    return;
+  }
+  const int32_t* h = a.hist + (size_t)r * a.hist_cap;
+  uint8_t* row = a.logits + (size_t)r * a.row_bytes;
+  for (int i = tid; i < cnt; i += kPenThreads) {
+    const int t = h[i];
+    if (t >= 0 && t < a.V) s_seen[t >> 5] = 0u;
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt; i += kPenThreads) {
+    const int t = h[i];
+    if (t < 0 || t >= a.V) continue;
+    const uint32_t bit = 1u << (t & 31);
+    const uint32_t old = __hip_atomic_fetch_or(&s_seen[t >> 5], bit, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (old & bit) continue;  // an earlier entry of the same token owns it
+    float v;
+    if (a.dtype == QS_F32) v = reinterpret_cast<float*>(row)[t];
+    else v = __uint_as_float((uint32_t)reinterpret_cast<uint16_t*>(row)[t] << 16);
+    v = v > 0.0f ? v / rep : v * rep;
+    v = v - pres;
+    if (a.dtype == QS_F32) reinterpret_cast<float*>(row)[t] = v;
+    else reinterpret_cast<uint16_t*>(row)[t] = to_bf16_rne(v);
+  }
+  if (tid == 0) a.status[r] = QS_ROW_OK;
+}
+
+}  // namespace
+
+hipError_t launch_penalty(const PenaltyArgs& a, int B, hipStream_t st) {
+  hipLaunchKernelGGL(penalty_kernel, dim3((unsigned)B), dim3(kPenThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qs
