@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--spec", action="store_true",
                     help="instead of the headline line, time the speculative verifier "
                          "(qs_spec_verify) on candidate lists of the headline workload")
+    ap.add_argument("--penalties", action="store_true",
+                    help="instead of the headline line, time qs_apply_penalties (2048-token "
+                         "histories) on the headline batch, alone and followed by qs_sample")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the headline line, print one line timing the path "
                          "switches (the Qrita page's ablation runs) on the headline "
@@ -301,6 +304,83 @@ def spec_bench(args, lib, stream):
     print(json.dumps(line), flush=True)
 
 
+class PenaltyPrepared:
+    """A 2048-token history per row (uniform ids, so about 2,030 distinct),
+    repetition 1.2 and presence 0.3, and the ctypes tuple of qs_apply_penalties
+    on the same device logits a Prepared set samples from."""
+
+    H = 2048
+
+    def __init__(self, lib, prep, seed):
+        import torch
+        w = prep.w
+        rng = np.random.default_rng(seed)
+        self.hist = torch.from_numpy(rng.integers(0, w.V, (w.B, self.H)).astype(np.int32)).cuda()
+        self.cnt = torch.full((w.B,), self.H, dtype=torch.int32, device="cuda")
+        self.rep = torch.full((w.B,), 1.2, dtype=torch.float32, device="cuda")
+        self.pres = torch.full((w.B,), 0.3, dtype=torch.float32, device="cuda")
+        self.status = torch.empty(w.B, dtype=torch.int32, device="cuda")
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.args = (P(prep.logits), 1 if w.dtype == "bf16" else 0, w.B, w.V, w.V, P(self.hist),
+                     self.H, P(self.cnt), P(self.rep), P(self.pres), P(self.status), None)
+        self.lib, self.prep, self.with_sample = lib, prep, False
+
+    def call(self, stream=None, flags=None):
+        rc = self.lib.qs_apply_penalties(*(self.args[:-1] + (stream,)))
+        if rc != 0:
+            raise RuntimeError(f"qs_apply_penalties returned {rc}")
+        if self.with_sample:
+            self.prep.call(stream)
+
+
+def penalties_bench(args, lib, stream):
+    """Penalties alone, then penalties + sample per step. Each set is
+    penalised once for real (repetition 1.2, presence 0.3); the timed steps
+    then apply repetition 1 and presence 0 to the same histories, which does
+    the same loads, arithmetic and stores but leaves the rows as one real
+    application made them (applying 1.2 over and over would drive the
+    penalised logits to huge negative values no real row holds)."""
+    import torch
+    sets = [workloads.make(args.workload, seed=workloads.BASE_SEED + args.workload + 1000 * i)
+            for i in range(args.sets)]
+    preps = [Prepared(lib, w, args.cand_cap, args.flags, stream) for w in sets]
+    pens = [PenaltyPrepared(lib, pr, 500 + i) for i, pr in enumerate(preps)]
+    for pn in pens:
+        pn.call(stream)
+        pn.rep.fill_(1.0)
+        pn.pres.fill_(0.0)
+    torch.cuda.synchronize()
+    out = {}
+    for mode in ("penalties", "penalties+sample"):
+        for pn in pens:
+            pn.with_sample = mode != "penalties"
+        for i in range(args.warmup):
+            pens[i % len(pens)].call(stream)
+        torch.cuda.synchronize()
+        ms, graph, cs = time_graph(pens, args.steps)
+        out[mode] = ms / args.steps
+        del graph
+    B = preps[0].w.B
+    H = PenaltyPrepared.H
+    nbytes = B * (4 * H + 12 + 2 * 2 * H)  # ids, params, read + write of each penalised logit
+    per = out["penalties"]
+    line = {
+        "metric": "rows/sec of penalties + sample, B=256 V=151936",
+        "value": round(B / (out["penalties+sample"] * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(out["penalties+sample"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "B=256 V=151936 bf16 batch, 2048-token history per row, "
+                               "repetition 1.2, presence 0.3",
+                   "penalties_ms": round(per, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,
+                     "bytes_per_launch": nbytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def ablation(args, lib, stream):
     """Time every path switch on the headline workload and at the page's
     ablation shape; every switch gives identical outputs (the path-invariance
@@ -378,6 +458,9 @@ def main():
     import top_sampling_vocabs_amd as qs
     lib = qs.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.penalties:
+        penalties_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        return
     if args.spec:
         spec_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         return

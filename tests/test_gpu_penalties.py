@@ -31,11 +31,12 @@ def _history(rng, B, V, cap):
     return hist, cnt
 
 
+@pytest.mark.parametrize("cap", [600, 9000])  # one round held in registers; several rounds
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_penalties_bitwise(qs, dtype):
+def test_penalties_bitwise(qs, dtype, cap):
     import torch
-    rng = np.random.default_rng(31 + (dtype == "bf16"))
-    B, V, cap = 40, 20011, 600
+    rng = np.random.default_rng(31 + (dtype == "bf16") + cap)
+    B, V = 40, 20011
     z = rng.normal(0, 3, (B, V)).astype(np.float32)
     z[0, :50] = 0.0
     z[1, :50] = -0.0
@@ -56,7 +57,9 @@ def test_penalties_bitwise(qs, dtype):
     pres = rng.choice([0.0, 0.5, -0.3], B).astype(np.float32)
     rep[5], pres[6], cnt[7] = 0.0, np.inf, cap + 1  # invalid rows
     rep[8] = np.nan
-    print(f"penalties {dtype} B={B} V={V}", flush=True)
+    if cap > 4096:
+        cnt[8:] = rng.integers(4097, cap + 1, B - 8)
+    print(f"penalties {dtype} B={B} V={V} cap={cap}", flush=True)
     st = qs.apply_penalties(dev, torch.from_numpy(hist).cuda(), torch.from_numpy(cnt).cuda(),
                             torch.from_numpy(rep).cuda(), torch.from_numpy(pres).cuda())
     torch.cuda.synchronize()

@@ -10,11 +10,13 @@
 // work is O(history), not O(V): the sampling kernels then read the modified
 // row as they read any other.
 //
-// One workgroup per row. A token repeated in the history is penalised once:
-// every history entry clears its token's bit in an LDS bitmap of the
-// vocabulary, then sets it with an atomic OR; the entry that finds the bit
-// clear owns the token and alone rewrites its logit, so no two threads write
-// the same element.
+// One workgroup of 1024 threads per row, 4 history entries per thread per
+// round with their loads issued together (a history of up to 4096 ids is
+// read once and held in registers). A token repeated in the history is
+// penalised once: every history entry clears its token's bit in an LDS bitmap
+// of the vocabulary, then sets it with an atomic OR; the entry that finds the
+// bit clear owns the token and alone rewrites its logit, so no two threads
+// write the same element.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,7 +27,8 @@
 namespace qs {
 namespace {
 
-constexpr int kPenThreads = 256;
+constexpr int kPenThreads = 1024;
+constexpr int kPenU = 4;  // history entries per thread per round, their loads issued together
 __shared__ uint32_t s_seen[kPenaltyMaxV / 32];  // 128 KB
 
 __device__ __forceinline__ uint16_t to_bf16_rne(float v) {
@@ -47,25 +50,67 @@ __global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
   }
   const int32_t* h = a.hist + (size_t)r * a.hist_cap;
   uint8_t* row = a.logits + (size_t)r * a.row_bytes;
-  for (int i = tid; i < cnt; i += kPenThreads) {
-    const int t = h[i];
-    if (t >= 0 && t < a.V) s_seen[t >> 5] = 0u;
-  }
-  __syncthreads();
-  for (int i = tid; i < cnt; i += kPenThreads) {
-    const int t = h[i];
-    if (t < 0 || t >= a.V) continue;
-    const uint32_t bit = 1u << (t & 31);
-    const uint32_t old = __hip_atomic_fetch_or(&s_seen[t >> 5], bit, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (old & bit) continue;  // an earlier entry of the same token owns it
-    float v;
-    if (a.dtype == QS_F32) v = reinterpret_cast<float*>(row)[t];
-    else v = __uint_as_float((uint32_t)reinterpret_cast<uint16_t*>(row)[t] << 16);
-    v = v > 0.0f ? v / rep : v * rep;
-    v = v - pres;
-    if (a.dtype == QS_F32) reinterpret_cast<float*>(row)[t] = v;
-    else reinterpret_cast<uint16_t*>(row)[t] = to_bf16_rne(v);
+  auto load_ids = [&](int i0, int (&t)[kPenU]) {
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      const int i = i0 + u * kPenThreads;
+      const int x = i < cnt ? h[i] : -1;
+      t[u] = x >= 0 && x < a.V ? x : -1;  // -1: nothing to do
+    }
+  };
+  auto clear_bits = [&](const int (&t)[kPenU]) {
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u)
+      if (t[u] >= 0) s_seen[t[u] >> 5] = 0u;
+  };
+  // claim each id's bit; the owners read, penalise and write back their logits
+  auto penalise = [&](int (&t)[kPenU]) {
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      if (t[u] >= 0) {
+        const uint32_t bit = 1u << (t[u] & 31);
+        const uint32_t old = __hip_atomic_fetch_or(&s_seen[t[u] >> 5], bit, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (old & bit) t[u] = -1;  // an earlier entry of the same token owns it
+      }
+    }
+    float v[kPenU];
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      v[u] = 0.0f;
+      if (t[u] >= 0) {
+        if (a.dtype == QS_F32) v[u] = reinterpret_cast<float*>(row)[t[u]];
+        else v[u] = __uint_as_float((uint32_t)reinterpret_cast<uint16_t*>(row)[t[u]] << 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      if (t[u] >= 0) {
+        float x = v[u] > 0.0f ? v[u] / rep : v[u] * rep;
+        x = x - pres;
+        if (a.dtype == QS_F32) reinterpret_cast<float*>(row)[t[u]] = x;
+        else reinterpret_cast<uint16_t*>(row)[t[u]] = to_bf16_rne(x);
+      }
+    }
+  };
+  if (cnt <= kPenU * kPenThreads) {  // one round: the ids stay in registers
+    int t[kPenU];
+    load_ids(tid, t);
+    clear_bits(t);
+    __syncthreads();
+    penalise(t);
+  } else {
+    for (int i0 = tid; i0 < cnt; i0 += kPenU * kPenThreads) {
+      int t[kPenU];
+      load_ids(i0, t);
+      clear_bits(t);
+    }
+    __syncthreads();
+    for (int i0 = tid; i0 < cnt; i0 += kPenU * kPenThreads) {
+      int t[kPenU];
+      load_ids(i0, t);
+      penalise(t);
+    }
   }
   if (tid == 0) a.status[r] = QS_ROW_OK;
 }
