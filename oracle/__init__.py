@@ -17,7 +17,8 @@ Modules:
   the pages give no test vectors; pinned statistically only).
 * ``spec``     — exact speculative-decoding verification (accept with
   min(1, p/q), else resample from max(0, p - q)) over candidate lists.
-* ``penalties`` — repetition and presence penalties over each row's history.
+* ``penalties`` — repetition and presence penalties over each row's history,
+  and an additive logit bias list per row.
 * ``batch``    — row loops over a whole [B, V] batch with the exact input layout
   the C-ABI uses (fp32 or bf16 bit patterns, packed uint32 bitmask).
 """
@@ -31,4 +32,5 @@ from .exact import exact_filter, brute_force_filter  # noqa: F401
 from .philox import philox4x32, uniform  # noqa: F401
 from .batch import decode_logits, filter_batch, sample_batch, argmax_batch  # noqa: F401
 from .spec import spec_verify_row, spec_verify_batch  # noqa: F401
-from .penalties import apply_penalties_row, apply_penalties_batch  # noqa: F401
+from .penalties import (apply_penalties_row, apply_penalties_batch,  # noqa: F401
+                        apply_logit_bias_row, apply_logit_bias_batch)

@@ -69,3 +69,44 @@ def apply_penalties_batch(logits, dtype, history, count, rep, pres):
         st[r], out[r] = apply_penalties_row(logits[r], dtype, history[r], int(count[r]), cap,
                                             rep[r], pres[r])
     return st, out
+
+
+def apply_logit_bias_row(z, dtype, ids, vals, count, cap):
+    """Additive logit bias (the processors list of page "Sampling 系统设计：从
+    logits 到可控生成" ends with such per-token edits; a bias list is the plain
+    reading): z_t <- z_t + b for each (t, b) of the row's first `count` entries
+    with 0 <= t < V, in float32, stored in the logits' dtype. A row whose count
+    lies outside [0, cap], whose values are not all finite, or that lists one
+    token twice is left unchanged and reported as BAD_PARAM."""
+    if count < 0 or count > cap:
+        return ROW_BAD_PARAM, z.copy()
+    V = len(z)
+    vals = np.asarray(vals[:count], np.float32)
+    if not np.isfinite(vals).all():
+        return ROW_BAD_PARAM, z.copy()
+    inside = [int(t) for t in ids[:count] if 0 <= int(t) < V]
+    if len(set(inside)) != len(inside):
+        return ROW_BAD_PARAM, z.copy()
+    out = z.copy()
+    for t, b in zip(ids[:count], vals):
+        t = int(t)
+        if t < 0 or t >= V:
+            continue
+        if dtype == "bf16":
+            v = (np.uint32(z[t]) << np.uint32(16)).astype(np.uint32).view(np.float32)
+        else:
+            v = np.float32(z[t])
+        v = np.float32(v + b)
+        out[t] = _to_bf16_bits(np.array([v]))[0] if dtype == "bf16" else v
+    return ROW_OK, out
+
+
+def apply_logit_bias_batch(logits, dtype, ids, vals, count):
+    """Row loop: (status [B] int32, new logits) in the input layout."""
+    B = logits.shape[0]
+    cap = ids.shape[1]
+    out = logits.copy()
+    st = np.zeros(B, np.int32)
+    for r in range(B):
+        st[r], out[r] = apply_logit_bias_row(logits[r], dtype, ids[r], vals[r], int(count[r]), cap)
+    return st, out

@@ -582,3 +582,25 @@ def test_penalties_bf16_rounding():
     # ties round to even: 1 + 2^-8 (bits 0x3F808000) -> 1.0, 1 + 3*2^-8 -> 1 + 2^-6
     assert oracle.penalties._to_bf16_bits(np.array([1 + 2**-8], np.float32))[0] == 0x3F80
     assert oracle.penalties._to_bf16_bits(np.array([1 + 3 * 2**-8], np.float32))[0] == 0x3F82
+
+
+def test_logit_bias_hand_example():
+    z = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    st, out = oracle.apply_logit_bias_row(z, "f32", np.array([2, 0, 9, -1]),
+                                          np.array([-0.25, 4.0, 7.0, 1.0], np.float32), 4, 4)
+    assert st == oracle.ROW_OK and out.tolist() == [5.0, -2.0, 0.25, 3.0]
+    # only the first `count` entries apply
+    st, out = oracle.apply_logit_bias_row(z, "f32", np.array([3, 1]), np.array([1.0, 1.0],
+                                          np.float32), 1, 2)
+    assert out.tolist() == [1.0, -2.0, 0.5, 4.0]
+    # a token listed twice, a non-finite value, a bad count: unchanged and flagged
+    for ids, vals, cnt in (([1, 1], [1.0, 2.0], 2), ([1, 2], [np.inf, 0.0], 2),
+                           ([1, 2], [1.0, 1.0], 3), ([1, 2], [1.0, 1.0], -1)):
+        st, out = oracle.apply_logit_bias_row(z, "f32", np.array(ids), np.array(vals, np.float32),
+                                              cnt, 2)
+        assert st == oracle.ROW_BAD_PARAM and np.array_equal(out, z)
+    # bf16: 1.0 + 2^-9 rounds back to 1.0 (below half an ulp), 1.0 + 2^-7 is exact
+    zb = np.array([0x3F80, 0x3F80], np.uint16)
+    st, out = oracle.apply_logit_bias_row(zb, "bf16", np.array([0, 1]),
+                                          np.array([2**-9, 2**-7], np.float32), 2, 2)
+    assert out.tolist() == [0x3F80, 0x3F81]
