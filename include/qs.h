@@ -228,6 +228,28 @@ QS_API int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int
                        const int32_t* history_count, const float* repetition_penalty,
                        const float* presence_penalty, int32_t* row_status, void* stream);
 
+/* Additive logit bias, applied in place to the logits before qs_filter_mask /
+ * qs_sample (page "Sampling 系统设计：从 logits 到可控生成", logits-processor
+ * section: processors edit the logits before the softmax; a per-row list of
+ * token biases is the plain additive one). For each (t, b) of row r's first
+ * bias_count[r] entries with 0 <= t < V:  z[r][t] <- z[r][t] + b  in float32,
+ * stored in the logits' dtype (bfloat16: round to nearest even); ids outside
+ * [0, V) are ignored. A bias of -inf is not accepted: use the legal-token
+ * bitmask to exclude tokens.
+ *
+ * logits       [B][row_stride] float32 or bfloat16 (dtype), modified in place;
+ *              aligned to its element size; V <= 2^20
+ * bias_ids     [B][bias_cap] int32; bias_values [B][bias_cap] float32;
+ *              bias_count [B] int32
+ * row_status   [B] int32 out: QS_ROW_OK, or QS_ROW_BAD_PARAM (row left
+ *              unchanged) when the count lies outside [0, bias_cap], a value
+ *              is not finite, or a token in [0, V) is listed twice.
+ * Every pointer is required. One kernel launch on `stream`; nothing is
+ * allocated. */
+QS_API int qs_apply_logit_bias(void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                        const int32_t* bias_ids, const float* bias_values, int64_t bias_cap,
+                        const int32_t* bias_count, int32_t* row_status, void* stream);
+
 /* Library version string (static storage). */
 QS_API const char* qs_version(void);
 

@@ -146,3 +146,19 @@ def test_apply_penalties_rejects_bad_arguments(lib):
                dict(status=None)):
         assert ap(**kw) == _lib.QS_ERR_INVALID_ARG, kw
     assert ap(B=0) == _lib.QS_OK
+
+
+def test_apply_logit_bias_rejects_bad_arguments(lib):
+    def ab(**kw):
+        a = dict(logits=A16, dtype=0, B=2, V=64, stride=64, ids=A16, vals=A16, cap=8, cnt=A16,
+                 status=A16, stream=None)
+        a.update(kw)
+        return lib.qs_apply_logit_bias(a["logits"], a["dtype"], a["B"], a["V"], a["stride"],
+                                       a["ids"], a["vals"], a["cap"], a["cnt"], a["status"],
+                                       a["stream"])
+    for kw in (dict(dtype=5), dict(B=-1), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
+               dict(stride=10), dict(logits=ctypes.c_void_p(0x100002)), dict(cap=0),
+               dict(ids=None), dict(vals=ctypes.c_void_p(0x100001)), dict(cnt=None),
+               dict(status=None)):
+        assert ab(**kw) == _lib.QS_ERR_INVALID_ARG, kw
+    assert ab(B=0) == _lib.QS_OK

@@ -99,3 +99,40 @@ def test_penalties_then_sample(qs):
     compare_filter(w, res, out, range(w.B), rep_)
     compare_tokens(res, out["tokens"], range(w.B), rep_, uniforms=uni)
     rep_.check()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_logit_bias_bitwise(qs, dtype):
+    """Additive bias lists: every logit bit for bit against the oracle, with ids
+    outside [0, V), rows listing a token twice, a non-finite value or a bad
+    count (left unchanged and flagged)."""
+    import torch
+    rng = np.random.default_rng(41 + (dtype == "bf16"))
+    B, V, cap = 24, 30011, 700
+    z = rng.normal(0, 3, (B, V)).astype(np.float32)
+    if dtype == "bf16":
+        host = (z.view(np.uint32) >> 16).astype(np.uint16)
+        dev = torch.from_numpy(host.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        host = z
+        dev = torch.from_numpy(z).cuda()
+    ids = np.stack([rng.permutation(V + 50)[:cap] - 25 for _ in range(B)]).astype(np.int32)
+    vals = rng.normal(0, 5, (B, cap)).astype(np.float32)
+    cnt = rng.integers(0, cap + 1, B).astype(np.int32)
+    cnt[:4] = cap
+    ids[0, 7] = ids[0, 3] = 11          # a token listed twice
+    vals[1, 5] = np.nan                 # a non-finite value
+    cnt[2] = cap + 1                    # count beyond capacity
+    ids[3, 9] = ids[3, 2] = V + 3       # a repeated id outside [0, V) is ignored
+    print(f"logit bias {dtype} B={B} V={V}", flush=True)
+    st = qs.apply_logit_bias(dev, torch.from_numpy(ids).cuda(), torch.from_numpy(vals).cuda(),
+                             torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    want_st, want = oracle.apply_logit_bias_batch(host, dtype, ids, vals, cnt)
+    assert np.array_equal(st.cpu().numpy(), want_st)
+    assert (want_st[:3] == oracle.ROW_BAD_PARAM).all() and want_st[3] == oracle.ROW_OK
+    got = dev.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else \
+        dev.cpu().numpy().view(np.uint32)
+    ref = want.view(np.uint16) if dtype == "bf16" else want.view(np.uint32)
+    diff = np.argwhere(got != ref)
+    assert len(diff) == 0, diff[:10]

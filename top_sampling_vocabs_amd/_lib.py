@@ -34,7 +34,7 @@ FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
 EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_apply_penalties",
-           "qs_version")
+           "qs_apply_logit_bias", "qs_version")
 
 _lib = None
 
@@ -81,6 +81,11 @@ def load(path=LIB_PATH):
         _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
         _p, _i64, _p,                        # history, history_cap, history_count
         _p, _p, _p, _p]                      # repetition, presence, row_status, stream
+    lib.qs_apply_logit_bias.restype = _i32
+    lib.qs_apply_logit_bias.argtypes = [
+        _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
+        _p, _p, _i64, _p,                    # bias ids, values, cap, count
+        _p, _p]                              # row_status, stream
     lib.qs_version.restype = ctypes.c_char_p
     lib.qs_version.argtypes = []
     if path == LIB_PATH:
@@ -293,4 +298,29 @@ def apply_penalties(logits, history, history_count, repetition, presence):
                                 _ptr(repetition), _ptr(presence), _ptr(status),
                                 _stream(logits.device))
     _status(rc, "qs_apply_penalties")
+    return status
+
+
+def apply_logit_bias(logits, bias_ids, bias_values, bias_count):
+    """Additive logit bias per row, applied to logits in place. bias_ids: int32
+    [B, cap]; bias_values: float32 [B, cap]; bias_count: int32 [B]. Returns the
+    row status (int32 [B])."""
+    import torch
+    lib = load()
+    if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a CUDA tensor [B, V] with unit column stride")
+    B, V = logits.shape
+    for t, dt, name in ((bias_ids, torch.int32, "bias_ids"), (bias_values, torch.float32,
+                                                              "bias_values")):
+        if t.dim() != 2 or t.shape[0] != B or t.dtype != dt or not t.is_contiguous() \
+                or t.device != logits.device:
+            raise ValueError(f"{name}: need a contiguous [B, cap] {dt} tensor on the logits' device")
+    if bias_ids.shape != bias_values.shape:
+        raise ValueError("bias_ids and bias_values must have the same shape")
+    _check_rowvec(bias_count, B, torch.int32, "bias_count")
+    status = torch.empty(B, dtype=torch.int32, device=logits.device)
+    rc = lib.qs_apply_logit_bias(_ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+                                 _ptr(bias_ids), _ptr(bias_values), bias_ids.shape[1],
+                                 _ptr(bias_count), _ptr(status), _stream(logits.device))
+    _status(rc, "qs_apply_logit_bias")
     return status

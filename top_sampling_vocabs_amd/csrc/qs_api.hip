@@ -203,6 +203,32 @@ int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t ro
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;
 }
 
+int qs_apply_logit_bias(void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                        const int32_t* bias_ids, const float* bias_values, int64_t bias_cap,
+                        const int32_t* bias_count, int32_t* row_status, void* stream) {
+  if (dtype != QS_F32 && dtype != QS_BF16) return QS_ERR_INVALID_ARG;
+  if (B < 0 || B > kMaxB || V < 1 || V > qs::kPenaltyMaxV) return QS_ERR_INVALID_ARG;
+  if (B == 0) return QS_OK;
+  const int64_t es = dtype == QS_F32 ? 4 : 2;
+  if (!logits || !aligned(logits, (uintptr_t)es) || row_stride < V) return QS_ERR_INVALID_ARG;
+  if (bias_cap < 1 || bias_cap > kMaxV) return QS_ERR_INVALID_ARG;
+  const void* req4[] = {bias_ids, bias_values, bias_count, row_status};
+  for (const void* p : req4)
+    if (!p || !aligned(p, 4)) return QS_ERR_INVALID_ARG;
+  qs::BiasArgs a;
+  a.logits = static_cast<uint8_t*>(logits);
+  a.row_bytes = row_stride * es;
+  a.V = (int)V;
+  a.dtype = dtype;
+  a.ids = bias_ids;
+  a.vals = bias_values;
+  a.cap = bias_cap;
+  a.count = bias_count;
+  a.status = row_status;
+  hipError_t e = qs::launch_bias(a, (int)B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
 const char* qs_version(void) { return "qs 0.1.0 gfx950"; }
 
 }  // extern "C"

@@ -79,10 +79,23 @@ struct PenaltyArgs {
   int32_t* status;
 };
 
+struct BiasArgs {
+  uint8_t* logits;         // modified in place
+  int64_t row_bytes;
+  int V;
+  int dtype;
+  const int32_t* ids;      // [B][cap] token ids
+  const float* vals;       // [B][cap] biases
+  int64_t cap;
+  const int32_t* count;
+  int32_t* status;
+};
+
 int seg_for(int V);
 hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st);
 hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st);
 hipError_t launch_spec(const SpecArgs& a, int B, hipStream_t st);
 hipError_t launch_penalty(const PenaltyArgs& a, int B, hipStream_t st);
+hipError_t launch_bias(const BiasArgs& a, int B, hipStream_t st);
 
 }  // namespace qs

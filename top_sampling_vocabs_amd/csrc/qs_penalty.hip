@@ -115,7 +115,66 @@ __global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
   if (tid == 0) a.status[r] = QS_ROW_OK;
 }
 
+// Additive logit bias: z_t <- z_t + b for each (t, b) of the row's list with
+// 0 <= t < V, in float32, stored in the logits' dtype. The list must name each
+// token once: the first phase checks that (bitmap as above; any entry that
+// finds its bit already set flags the row) and that every value is finite,
+// and only a clean row is modified, so a flagged row is left untouched.
+__global__ void __launch_bounds__(kPenThreads) bias_kernel(BiasArgs a) {
+  __shared__ int s_bad;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cnt = a.count[r];
+  if (cnt < 0 || (int64_t)cnt > a.cap) {
+    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    return;
+  }
+  const int32_t* ids = a.ids + (size_t)r * a.cap;
+  const float* vals = a.vals + (size_t)r * a.cap;
+  uint8_t* row = a.logits + (size_t)r * a.row_bytes;
+  if (tid == 0) s_bad = 0;
+  for (int i = tid; i < cnt; i += kPenThreads) {
+    const int t = ids[i];
+    if (t >= 0 && t < a.V) s_seen[t >> 5] = 0u;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int i = tid; i < cnt; i += kPenThreads) {
+    const int t = ids[i];
+    bad = bad || !isfinite(vals[i]);
+    if (t >= 0 && t < a.V) {
+      const uint32_t bit = 1u << (t & 31);
+      const uint32_t old = __hip_atomic_fetch_or(&s_seen[t >> 5], bit, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      bad = bad || (old & bit) != 0u;
+    }
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    return;
+  }
+  for (int i = tid; i < cnt; i += kPenThreads) {
+    const int t = ids[i];
+    if (t < 0 || t >= a.V) continue;
+    if (a.dtype == QS_F32) {
+      float* const p = reinterpret_cast<float*>(row) + t;
+      *p = *p + vals[i];
+    } else {
+      uint16_t* const p = reinterpret_cast<uint16_t*>(row) + t;
+      *p = to_bf16_rne(__uint_as_float((uint32_t)*p << 16) + vals[i]);
+    }
+  }
+  if (tid == 0) a.status[r] = QS_ROW_OK;
+}
+
 }  // namespace
+
+hipError_t launch_bias(const BiasArgs& a, int B, hipStream_t st) {
+  hipLaunchKernelGGL(bias_kernel, dim3((unsigned)B), dim3(kPenThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_penalty(const PenaltyArgs& a, int B, hipStream_t st) {
   hipLaunchKernelGGL(penalty_kernel, dim3((unsigned)B), dim3(kPenThreads), 0, st, a);
