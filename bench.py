@@ -360,6 +360,36 @@ def penalties_bench(args, lib, stream):
         ms, graph, cs = time_graph(pens, args.steps)
         out[mode] = ms / args.steps
         del graph
+    # the logit bias kernel on the same rows: 2048 distinct ids per row, bias 0
+    # (the same work as any bias, rows unchanged)
+    import top_sampling_vocabs_amd as qs
+
+    class BiasCall:
+        def __init__(self, pr, seed):
+            g = torch.Generator()
+            g.manual_seed(seed)
+            w = pr.w
+            self.ids = torch.stack([torch.randperm(w.V, generator=g)[:PenaltyPrepared.H]
+                                    for _ in range(w.B)]).to(torch.int32).cuda()
+            self.vals = torch.zeros(self.ids.shape, dtype=torch.float32, device="cuda")
+            self.cnt = torch.full((w.B,), PenaltyPrepared.H, dtype=torch.int32, device="cuda")
+            self.st = torch.empty(w.B, dtype=torch.int32, device="cuda")
+            P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+            self.args = (P(pr.logits), 1 if w.dtype == "bf16" else 0, w.B, w.V, w.V, P(self.ids),
+                         P(self.vals), PenaltyPrepared.H, P(self.cnt), P(self.st))
+
+        def call(self, stream=None, flags=None):
+            rc = lib.qs_apply_logit_bias(*(self.args + (stream,)))
+            if rc != 0:
+                raise RuntimeError(f"qs_apply_logit_bias returned {rc}")
+
+    bias = [BiasCall(pr, 900 + i) for i, pr in enumerate(preps)]
+    for i in range(args.warmup):
+        bias[i % len(bias)].call(stream)
+    torch.cuda.synchronize()
+    ms, graph, cs = time_graph(bias, args.steps)
+    out["logit_bias"] = ms / args.steps
+    del graph, qs
     B = preps[0].w.B
     H = PenaltyPrepared.H
     nbytes = B * (4 * H + 12 + 2 * 2 * H)  # ids, params, read + write of each penalised logit
@@ -372,7 +402,8 @@ def penalties_bench(args, lib, stream):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "B=256 V=151936 bf16 batch, 2048-token history per row, "
                                "repetition 1.2, presence 0.3",
-                   "penalties_ms": round(per, 5)},
+                   "penalties_ms": round(per, 5),
+                   "logit_bias_ms_2048_ids": round(out["logit_bias"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
                      "peak": 8000.0, "unit": "GB/s",
                      "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,

@@ -101,14 +101,15 @@ def test_penalties_then_sample(qs):
     rep_.check()
 
 
+@pytest.mark.parametrize("cap", [700, 6000])  # one round held in registers; several rounds
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_logit_bias_bitwise(qs, dtype):
+def test_logit_bias_bitwise(qs, dtype, cap):
     """Additive bias lists: every logit bit for bit against the oracle, with ids
     outside [0, V), rows listing a token twice, a non-finite value or a bad
     count (left unchanged and flagged)."""
     import torch
-    rng = np.random.default_rng(41 + (dtype == "bf16"))
-    B, V, cap = 24, 30011, 700
+    rng = np.random.default_rng(41 + (dtype == "bf16") + cap)
+    B, V = 24, 30011
     z = rng.normal(0, 3, (B, V)).astype(np.float32)
     if dtype == "bf16":
         host = (z.view(np.uint32) >> 16).astype(np.uint16)

@@ -119,7 +119,9 @@ __global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
 // 0 <= t < V, in float32, stored in the logits' dtype. The list must name each
 // token once: the first phase checks that (bitmap as above; any entry that
 // finds its bit already set flags the row) and that every value is finite,
-// and only a clean row is modified, so a flagged row is left untouched.
+// and only a clean row is modified, so a flagged row is left untouched. A list
+// of up to 4096 entries is read once and held in registers, its logit loads
+// issued together.
 __global__ void __launch_bounds__(kPenThreads) bias_kernel(BiasArgs a) {
   __shared__ int s_bad;
   const int r = blockIdx.x;
@@ -133,6 +135,58 @@ __global__ void __launch_bounds__(kPenThreads) bias_kernel(BiasArgs a) {
   const float* vals = a.vals + (size_t)r * a.cap;
   uint8_t* row = a.logits + (size_t)r * a.row_bytes;
   if (tid == 0) s_bad = 0;
+  if (cnt <= kPenU * kPenThreads) {  // one round: ids and values stay in registers
+    int t[kPenU];
+    float b[kPenU];
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      const int i = tid + u * kPenThreads;
+      const bool in = i < cnt;
+      const int x = in ? ids[i] : -1;
+      b[u] = in ? vals[i] : 0.0f;
+      t[u] = x >= 0 && x < a.V ? x : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u)
+      if (t[u] >= 0) s_seen[t[u] >> 5] = 0u;
+    __syncthreads();
+    bool bad1 = false;
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      bad1 = bad1 || !isfinite(b[u]);
+      if (t[u] >= 0) {
+        const uint32_t bit = 1u << (t[u] & 31);
+        const uint32_t old = __hip_atomic_fetch_or(&s_seen[t[u] >> 5], bit, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        bad1 = bad1 || (old & bit) != 0u;
+      }
+    }
+    if (bad1) s_bad = 1;
+    __syncthreads();
+    if (s_bad) {
+      if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+      return;
+    }
+    float v[kPenU];
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      v[u] = 0.0f;
+      if (t[u] >= 0) {
+        if (a.dtype == QS_F32) v[u] = reinterpret_cast<float*>(row)[t[u]];
+        else v[u] = __uint_as_float((uint32_t)reinterpret_cast<uint16_t*>(row)[t[u]] << 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPenU; ++u) {
+      if (t[u] >= 0) {
+        const float x = v[u] + b[u];
+        if (a.dtype == QS_F32) reinterpret_cast<float*>(row)[t[u]] = x;
+        else reinterpret_cast<uint16_t*>(row)[t[u]] = to_bf16_rne(x);
+      }
+    }
+    if (tid == 0) a.status[r] = QS_ROW_OK;
+    return;
+  }
   for (int i = tid; i < cnt; i += kPenThreads) {
     const int t = ids[i];
     if (t >= 0 && t < a.V) s_seen[t >> 5] = 0u;
