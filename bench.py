@@ -126,16 +126,21 @@ class Prepared:
                                     self.cprobs, self.ccount, self.offset)]
 
 
+# the translation unit of the filter/sample kernel (the other entry points'
+# kernels live in files of their own and do not change it)
+FILTER_SOURCES = ("qs_device.hpp", "qs_kernels.hip", "qs_launch.hpp", "qs_select.hpp",
+                  "qs_stream.hpp")
+
+
 def source_digest():
-    """sha256 over the HIP sources the library is built from: a stored counter
-    reading applies only to the kernel it was taken on."""
+    """sha256 over the sources the filter/sample kernel is built from: a stored
+    counter reading applies only to the kernel it was taken on."""
     import hashlib
     csrc = os.path.join(ROOT, "top_sampling_vocabs_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in FILTER_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
