@@ -17,7 +17,9 @@ stored in the logits' dtype (bfloat16 round-to-nearest-even). A token repeated
 in the history is penalised once. Other tokens are untouched. A row with r not
 finite or <= 0, a not finite, or a history count outside [0, capacity] is
 left unchanged and reported as BAD_PARAM. Applied to the raw logits, before
-temperature and the rest of the contract.
+temperature and the rest of the contract. An optional frequency penalty f
+then subtracts f times the token's count in the history (the counting variant
+of the same idea: repeated use is penalised more), z_t <- z_t - f*n_t.
 """
 
 import numpy as np
@@ -34,13 +36,24 @@ def _to_bf16_bits(x32):
     return r
 
 
-def apply_penalties_row(z, dtype, history, count, cap, rep, pres):
+FREQ_MAX_HISTORY = 4096  # the C ABI's limit on a history with a frequency penalty
+
+
+def apply_penalties_row(z, dtype, history, count, cap, rep, pres, freq=0.0):
     """z: one row as stored (float32, or bfloat16 bits as uint16). Returns
-    (status, new row as stored)."""
+    (status, new row as stored). A frequency penalty f (0 disables it) then
+    subtracts f times the token's number of occurrences n in the history:
+    z_t <- z_t - f*n, both operations in float32; with f != 0 the history may
+    hold at most FREQ_MAX_HISTORY entries."""
     rep = np.float32(rep)
     pres = np.float32(pres)
-    if not (np.isfinite(rep) and rep > 0 and np.isfinite(pres)) or count < 0 or count > cap:
+    freq = np.float32(freq)
+    if not (np.isfinite(rep) and rep > 0 and np.isfinite(pres) and np.isfinite(freq)) \
+            or count < 0 or count > cap or (freq != 0 and count > FREQ_MAX_HISTORY):
         return ROW_BAD_PARAM, z.copy()
+    counts = {}
+    for t in history[:count]:
+        counts[int(t)] = counts.get(int(t), 0) + 1
     out = z.copy()
     V = len(z)
     seen = set()
@@ -55,11 +68,13 @@ def apply_penalties_row(z, dtype, history, count, cap, rep, pres):
             v = np.float32(z[t])
         v = np.float32(v / rep) if v > 0 else np.float32(v * rep)
         v = np.float32(v - pres)
+        if freq != 0:
+            v = np.float32(v - np.float32(freq * np.float32(counts[t])))
         out[t] = _to_bf16_bits(np.array([v]))[0] if dtype == "bf16" else v
     return ROW_OK, out
 
 
-def apply_penalties_batch(logits, dtype, history, count, rep, pres):
+def apply_penalties_batch(logits, dtype, history, count, rep, pres, freq=None):
     """Row loop: (status [B] int32, new logits) in the input layout."""
     B = logits.shape[0]
     cap = history.shape[1]
@@ -67,7 +82,7 @@ def apply_penalties_batch(logits, dtype, history, count, rep, pres):
     st = np.zeros(B, np.int32)
     for r in range(B):
         st[r], out[r] = apply_penalties_row(logits[r], dtype, history[r], int(count[r]), cap,
-                                            rep[r], pres[r])
+                                            rep[r], pres[r], 0.0 if freq is None else freq[r])
     return st, out
 
 

@@ -604,3 +604,23 @@ def test_logit_bias_hand_example():
     st, out = oracle.apply_logit_bias_row(zb, "bf16", np.array([0, 1]),
                                           np.array([2**-9, 2**-7], np.float32), 2, 2)
     assert out.tolist() == [0x3F80, 0x3F81]
+
+
+def test_frequency_penalty_hand_example():
+    """f times the number of occurrences, after the repetition and presence
+    terms: id 0 occurs 3 times, id 1 once."""
+    z = np.array([2.0, -2.0, 1.0], np.float32)
+    st, out = oracle.apply_penalties_row(z, "f32", np.array([0, 1, 0, 0]), 4, 4, 2.0, 0.5, 0.25)
+    assert st == oracle.ROW_OK
+    assert out.tolist() == [2.0 / 2 - 0.5 - 0.75, -2.0 * 2 - 0.5 - 0.25, 1.0]
+    # f = 0 is the plain repetition / presence result
+    st, out0 = oracle.apply_penalties_row(z, "f32", np.array([0, 1, 0, 0]), 4, 4, 2.0, 0.5, 0.0)
+    assert out0.tolist() == [0.5, -4.5, 1.0]
+    # a non-finite f, or a history longer than the limit with f != 0, flags the row
+    assert oracle.apply_penalties_row(z, "f32", np.array([0]), 1, 1, 1.0, 0.0, np.nan)[0] == \
+        oracle.ROW_BAD_PARAM
+    long_h = np.zeros(5000, np.int64)
+    assert oracle.apply_penalties_row(z, "f32", long_h, 5000, 5000, 1.0, 0.0, 0.1)[0] == \
+        oracle.ROW_BAD_PARAM
+    assert oracle.apply_penalties_row(z, "f32", long_h, 5000, 5000, 1.0, 0.0, 0.0)[0] == \
+        oracle.ROW_OK
