@@ -327,7 +327,7 @@ class PenaltyPrepared:
         self.status = torch.empty(w.B, dtype=torch.int32, device="cuda")
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         self.args = (P(prep.logits), 1 if w.dtype == "bf16" else 0, w.B, w.V, w.V, P(self.hist),
-                     self.H, P(self.cnt), P(self.rep), P(self.pres), P(self.status), None)
+                     self.H, P(self.cnt), P(self.rep), P(self.pres), None, P(self.status), None)
         self.lib, self.prep, self.with_sample = lib, prep, False
 
     def call(self, stream=None, flags=None):

@@ -218,15 +218,21 @@ QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* tar
  *                   place; aligned to its element size; V <= 2^20
  * history           [B][history_cap] int32 token ids; history_count [B] int32
  * repetition_penalty, presence_penalty [B] float32
+ * frequency_penalty [B] float32, optional (NULL: 0): then also
+ *                   z[r][t] <- z - f[r] * n_t (both in float32), n_t the
+ *                   number of times t occurs in the history; a row with
+ *                   f != 0 may hold at most 4096 history entries
  * row_status        [B] int32 out: QS_ROW_OK, or QS_ROW_BAD_PARAM (row left
- *                   unchanged) when rep is not finite or <= 0, pres is not
- *                   finite, or the count lies outside [0, history_cap].
- * Every pointer is required. One kernel launch on `stream`; nothing is
+ *                   unchanged) when rep is not finite or <= 0, pres or f is
+ *                   not finite, the count lies outside [0, history_cap], or
+ *                   f != 0 with more than 4096 entries.
+ * Every pointer but frequency_penalty is required. One kernel launch on `stream`; nothing is
  * allocated. */
 QS_API int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                        const int32_t* history, int64_t history_cap,
                        const int32_t* history_count, const float* repetition_penalty,
-                       const float* presence_penalty, int32_t* row_status, void* stream);
+                       const float* presence_penalty, const float* frequency_penalty,
+                       int32_t* row_status, void* stream);
 
 /* Additive logit bias, applied in place to the logits before qs_filter_mask /
  * qs_sample (page "Sampling 系统设计：从 logits 到可控生成", logits-processor

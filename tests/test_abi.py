@@ -134,16 +134,16 @@ def test_spec_verify_rejects_bad_arguments(lib):
 def test_apply_penalties_rejects_bad_arguments(lib):
     def ap(**kw):
         a = dict(logits=A16, dtype=1, B=2, V=64, stride=64, hist=A16, cap=8, cnt=A16,
-                 rep=A16, pres=A16, status=A16, stream=None)
+                 rep=A16, pres=A16, freq=None, status=A16, stream=None)
         a.update(kw)
         return lib.qs_apply_penalties(a["logits"], a["dtype"], a["B"], a["V"], a["stride"],
                                       a["hist"], a["cap"], a["cnt"], a["rep"], a["pres"],
-                                      a["status"], a["stream"])
+                                      a["freq"], a["status"], a["stream"])
     for kw in (dict(dtype=2), dict(B=-1), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
                dict(stride=63), dict(logits=ctypes.c_void_p(0x100001)),
                dict(dtype=0, logits=ctypes.c_void_p(0x100002)), dict(cap=0), dict(hist=None),
                dict(cnt=None), dict(rep=None), dict(pres=ctypes.c_void_p(0x100002)),
-               dict(status=None)):
+               dict(status=None), dict(freq=ctypes.c_void_p(0x100002))):
         assert ap(**kw) == _lib.QS_ERR_INVALID_ARG, kw
     assert ap(B=0) == _lib.QS_OK
 

@@ -31,9 +31,10 @@ def _history(rng, B, V, cap):
     return hist, cnt
 
 
+@pytest.mark.parametrize("freq_on", [False, True])
 @pytest.mark.parametrize("cap", [600, 9000])  # one round held in registers; several rounds
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_penalties_bitwise(qs, dtype, cap):
+def test_penalties_bitwise(qs, dtype, cap, freq_on):
     import torch
     rng = np.random.default_rng(31 + (dtype == "bf16") + cap)
     B, V = 40, 20011
@@ -57,13 +58,19 @@ def test_penalties_bitwise(qs, dtype, cap):
     pres = rng.choice([0.0, 0.5, -0.3], B).astype(np.float32)
     rep[5], pres[6], cnt[7] = 0.0, np.inf, cap + 1  # invalid rows
     rep[8] = np.nan
+    # frequency penalties (sorted-history counts); with cap 9000 the rows over
+    # 4096 entries and f != 0 are flagged
+    freq = rng.choice([0.0, 0.1, -0.2, 0.05], B).astype(np.float32) if freq_on else None
+    if freq_on:
+        freq[9] = np.inf
     if cap > 4096:
         cnt[8:] = rng.integers(4097, cap + 1, B - 8)
-    print(f"penalties {dtype} B={B} V={V} cap={cap}", flush=True)
+    print(f"penalties {dtype} B={B} V={V} cap={cap} freq={freq_on}", flush=True)
     st = qs.apply_penalties(dev, torch.from_numpy(hist).cuda(), torch.from_numpy(cnt).cuda(),
-                            torch.from_numpy(rep).cuda(), torch.from_numpy(pres).cuda())
+                            torch.from_numpy(rep).cuda(), torch.from_numpy(pres).cuda(),
+                            None if freq is None else torch.from_numpy(freq).cuda())
     torch.cuda.synchronize()
-    want_st, want = oracle.apply_penalties_batch(host, dtype, hist, cnt, rep, pres)
+    want_st, want = oracle.apply_penalties_batch(host, dtype, hist, cnt, rep, pres, freq)
     assert np.array_equal(st.cpu().numpy(), want_st)
     got = dev.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else \
         dev.cpu().numpy()

@@ -80,7 +80,7 @@ def load(path=LIB_PATH):
     lib.qs_apply_penalties.argtypes = [
         _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
         _p, _i64, _p,                        # history, history_cap, history_count
-        _p, _p, _p, _p]                      # repetition, presence, row_status, stream
+        _p, _p, _p, _p, _p]                  # repetition, presence, frequency, status, stream
     lib.qs_apply_logit_bias.restype = _i32
     lib.qs_apply_logit_bias.argtypes = [
         _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
@@ -277,10 +277,11 @@ def spec_verify(target_ids, target_probs, target_count, draft_ids, draft_probs, 
     return out
 
 
-def apply_penalties(logits, history, history_count, repetition, presence):
-    """Repetition and presence penalties over each row's history, applied to
-    logits in place. history: int32 [B, cap]; history_count: int32 [B];
-    repetition, presence: float32 [B]. Returns the row status (int32 [B])."""
+def apply_penalties(logits, history, history_count, repetition, presence, frequency=None):
+    """Repetition, presence and (optional) frequency penalties over each row's
+    history, applied to logits in place. history: int32 [B, cap];
+    history_count: int32 [B]; repetition, presence, frequency: float32 [B].
+    Returns the row status (int32 [B])."""
     import torch
     lib = load()
     if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
@@ -292,10 +293,12 @@ def apply_penalties(logits, history, history_count, repetition, presence):
     _check_rowvec(history_count, B, torch.int32, "history_count")
     _check_rowvec(repetition, B, torch.float32, "repetition")
     _check_rowvec(presence, B, torch.float32, "presence")
+    if frequency is not None:
+        _check_rowvec(frequency, B, torch.float32, "frequency")
     status = torch.empty(B, dtype=torch.int32, device=logits.device)
     rc = lib.qs_apply_penalties(_ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
                                 _ptr(history), history.shape[1], _ptr(history_count),
-                                _ptr(repetition), _ptr(presence), _ptr(status),
+                                _ptr(repetition), _ptr(presence), _ptr(frequency), _ptr(status),
                                 _stream(logits.device))
     _status(rc, "qs_apply_penalties")
     return status

@@ -178,7 +178,8 @@ int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* target_pro
 int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                        const int32_t* history, int64_t history_cap,
                        const int32_t* history_count, const float* repetition_penalty,
-                       const float* presence_penalty, int32_t* row_status, void* stream) {
+                       const float* presence_penalty, const float* frequency_penalty,
+                       int32_t* row_status, void* stream) {
   if (dtype != QS_F32 && dtype != QS_BF16) return QS_ERR_INVALID_ARG;
   if (B < 0 || B > kMaxB || V < 1 || V > qs::kPenaltyMaxV) return QS_ERR_INVALID_ARG;
   if (B == 0) return QS_OK;
@@ -188,6 +189,7 @@ int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t ro
   const void* req4[] = {history, history_count, repetition_penalty, presence_penalty, row_status};
   for (const void* p : req4)
     if (!p || !aligned(p, 4)) return QS_ERR_INVALID_ARG;
+  if (!aligned(frequency_penalty, 4)) return QS_ERR_INVALID_ARG;
   qs::PenaltyArgs a;
   a.logits = static_cast<uint8_t*>(logits);
   a.row_bytes = row_stride * es;
@@ -198,6 +200,7 @@ int qs_apply_penalties(void* logits, int dtype, int64_t B, int64_t V, int64_t ro
   a.count = history_count;
   a.rep = repetition_penalty;
   a.pres = presence_penalty;
+  a.freq = frequency_penalty;
   a.status = row_status;
   hipError_t e = qs::launch_penalty(a, (int)B, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;

@@ -76,6 +76,7 @@ struct PenaltyArgs {
   const int32_t* count;
   const float* rep;
   const float* pres;
+  const float* freq;       // optional (NULL: 0)
   int32_t* status;
 };
 

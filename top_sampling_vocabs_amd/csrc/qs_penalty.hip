@@ -5,7 +5,8 @@
 // logits processor fed by that history; the page leaves the formula open.
 // Taken here: for each distinct token t of the row's history (0 <= t < V),
 //   z_t <- (z_t > 0 ? z_t / r : z_t * r) - a
-// in float32, each operation rounded, stored back in the logits' dtype
+// in float32, each operation rounded (contraction is off in these kernels: no
+// multiply is fused with the subtraction after it), stored back in the logits' dtype
 // (bfloat16 round to nearest even). Every other logit is untouched, so the
 // work is O(history), not O(V): the sampling kernels then read the modified
 // row as they read any other.
@@ -31,6 +32,9 @@ constexpr int kPenThreads = 1024;
 constexpr int kPenU = 4;  // history entries per thread per round, their loads issued together
 __shared__ uint32_t s_seen[kPenaltyMaxV / 32];  // 128 KB
 
+constexpr int kFreqMax = 4096;  // history length with a frequency penalty (sorted in LDS)
+__shared__ int32_t s_sort[kFreqMax];  // 16 KB
+
 __device__ __forceinline__ uint16_t to_bf16_rne(float v) {
   const uint32_t b = __float_as_uint(v);
   if (v != v) return (uint16_t)((b >> 16) | 0x40u);  // NaN stays NaN (quiet)
@@ -38,18 +42,70 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float v) {
 }
 
 __global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
+#pragma clang fp contract(off)
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int cnt = a.count[r];
   const float rep = a.rep[r], pres = a.pres[r];
-  const bool ok = isfinite(rep) && rep > 0.0f && isfinite(pres) && cnt >= 0 &&
-                  (int64_t)cnt <= a.hist_cap;
+  const float freq = a.freq ? a.freq[r] : 0.0f;
+  const bool ok = isfinite(rep) && rep > 0.0f && isfinite(pres) && isfinite(freq) &&
+                  cnt >= 0 && (int64_t)cnt <= a.hist_cap && (freq == 0.0f || cnt <= kFreqMax);
   if (!ok) {
     if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
     return;
   }
   const int32_t* h = a.hist + (size_t)r * a.hist_cap;
   uint8_t* row = a.logits + (size_t)r * a.row_bytes;
+  if (freq != 0.0f) {
+    // counts: the history sorted ascending in LDS (bitonic; ids outside [0, V)
+    // and the padding sort last as INT_MAX); the first entry of each run of
+    // equal ids owns its token, and the run's length is its count
+    for (int i = tid; i < kFreqMax; i += kPenThreads) {
+      const int x = i < cnt ? h[i] : -1;
+      s_sort[i] = x >= 0 && x < a.V ? x : INT32_MAX;
+    }
+    __syncthreads();
+    for (int k = 2; k <= kFreqMax; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < kFreqMax; i += kPenThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const int x = s_sort[i], y = s_sort[l];
+            if ((x > y) == ((i & k) == 0)) {
+              s_sort[i] = y;
+              s_sort[l] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < kFreqMax; i += kPenThreads) {
+      const int t = s_sort[i];
+      if (t == INT32_MAX || (i > 0 && s_sort[i - 1] == t)) continue;
+      int lo = i + 1, len = kFreqMax - lo;  // first index past the run of t
+      while (len > 0) {
+        const int half = len >> 1;
+        if (s_sort[lo + half] <= t) {
+          lo += half + 1;
+          len -= half + 1;
+        } else {
+          len = half;
+        }
+      }
+      const float n = (float)(lo - i);
+      float v;
+      if (a.dtype == QS_F32) v = reinterpret_cast<float*>(row)[t];
+      else v = __uint_as_float((uint32_t)reinterpret_cast<uint16_t*>(row)[t] << 16);
+      v = v > 0.0f ? v / rep : v * rep;
+      v = v - pres;
+      v = v - freq * n;
+      if (a.dtype == QS_F32) reinterpret_cast<float*>(row)[t] = v;
+      else reinterpret_cast<uint16_t*>(row)[t] = to_bf16_rne(v);
+    }
+    if (tid == 0) a.status[r] = QS_ROW_OK;
+    return;
+  }
   auto load_ids = [&](int i0, int (&t)[kPenU]) {
 #pragma unroll
     for (int u = 0; u < kPenU; ++u) {
@@ -123,6 +179,7 @@ __global__ void __launch_bounds__(kPenThreads) penalty_kernel(PenaltyArgs a) {
 // of up to 4096 entries is read once and held in registers, its logit loads
 // issued together.
 __global__ void __launch_bounds__(kPenThreads) bias_kernel(BiasArgs a) {
+#pragma clang fp contract(off)
   __shared__ int s_bad;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
