@@ -7,6 +7,7 @@
 
 #include "../../include/qs.h"
 
+#include "qs_aux.hpp"
 #include "qs_launch.hpp"
 
 namespace {

@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "../../include/qs.h"
+#include "qs_aux.hpp"
 #include "qs_launch.hpp"
 
 namespace qs {

@@ -33,6 +33,7 @@
 
 #include "../../include/qs.h"
 #include "qs_device.hpp"
+#include "qs_aux.hpp"
 #include "qs_launch.hpp"
 
 namespace qs {
