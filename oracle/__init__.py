@@ -26,7 +26,8 @@ Modules:
 from .sampling import (  # noqa: F401
     ROW_OK, ROW_EMPTY, ROW_ALL_NEG_INF, ROW_NONFINITE, ROW_BAD_PARAM,
     ROW_CAND_OVERFLOW, TOP_P_BAND, RowResult, bf16_bits_to_float64,
-    legal_from_bitmask, filter_row, sample_from, token_logprob, keep_mask_words,
+    legal_from_bitmask, filter_row, sample_from, token_logprob, top_logprobs_row,
+    keep_mask_words,
     argmax_row, params_valid)
 from .exact import exact_filter, brute_force_filter  # noqa: F401
 from .philox import philox4x32, uniform  # noqa: F401

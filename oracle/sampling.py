@@ -265,3 +265,24 @@ def argmax_row(z, legal=None):
         return ROW_ALL_NEG_INF, -1
     zf = z[fin]
     return ROW_OK, int(fin[np.nonzero(zf == zf.max())[0][0]])
+
+
+def top_logprobs_row(ids, probs, count, cap, n):
+    """The n most probable tokens of a candidate list and their log-probabilities
+    under the final distribution (page "Sampling 系统设计：从 logits 到可控生成",
+    logprobs section: besides the chosen token's log-probability a sampler may
+    return the top tokens with theirs). Order: probability descending (the
+    list's float32 values compared exactly), ties by ascending id. Returns
+    (status, ids[n], logprobs[n]); slots past the list's length hold id -1 and
+    -inf. A count outside [0, cap] is BAD_PARAM (all slots -1 / -inf)."""
+    out_i = np.full(n, -1, np.int64)
+    out_l = np.full(n, -np.inf)
+    if count < 0 or count > cap:
+        return ROW_BAD_PARAM, out_i, out_l
+    q = np.asarray(probs[:count], np.float32)
+    t = np.asarray(ids[:count], np.int64)
+    order = sorted(range(count), key=lambda i: (-float(q[i]), int(t[i])))[:n]
+    for j, i in enumerate(order):
+        out_i[j] = t[i]
+        out_l[j] = np.log(np.float64(q[i])) if q[i] > 0 else -np.inf
+    return ROW_OK, out_i, out_l

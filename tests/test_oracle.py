@@ -624,3 +624,25 @@ def test_frequency_penalty_hand_example():
         oracle.ROW_BAD_PARAM
     assert oracle.apply_penalties_row(z, "f32", long_h, 5000, 5000, 1.0, 0.0, 0.0)[0] == \
         oracle.ROW_OK
+
+
+def test_top_logprobs_worked_example():
+    """The page's top-p example keeps A/B/C at 4/9, 3/9, 2/9: the top two are A
+    and B with log(4/9) and log(1/3). Ties go to the lower id; slots past the
+    list are (-1, -inf)."""
+    probs = np.array([4 / 9, 3 / 9, 2 / 9], np.float32)
+    st, ti, tl = oracle.top_logprobs_row(np.array([0, 1, 2]), probs, 3, 3, 2)
+    assert st == oracle.ROW_OK and ti.tolist() == [0, 1]
+    assert np.allclose(tl, np.log(probs[:2].astype(np.float64)))
+    st, ti, tl = oracle.top_logprobs_row(np.array([3, 5, 9]), np.array([0.25, 0.5, 0.25],
+                                         np.float32), 3, 3, 5)
+    assert ti.tolist() == [5, 3, 9, -1, -1] and np.isneginf(tl[3:]).all()
+    assert oracle.top_logprobs_row(np.array([1]), np.array([1.0], np.float32), 2, 1, 1)[0] == \
+        oracle.ROW_BAD_PARAM
+    # against a brute-force ordering of a random list with many ties
+    rng = np.random.default_rng(5)
+    ids = np.sort(rng.choice(1000, 200, replace=False))
+    pr = rng.choice([0.5, 0.25, 0.125, 0.0], 200).astype(np.float32)
+    st, ti, tl = oracle.top_logprobs_row(ids, pr, 200, 200, 30)
+    best = sorted(zip(-pr.astype(np.float64), ids))[:30]
+    assert ti.tolist() == [int(b[1]) for b in best]
