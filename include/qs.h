@@ -256,6 +256,28 @@ QS_API int qs_apply_logit_bias(void* logits, int dtype, int64_t B, int64_t V, in
                         const int32_t* bias_ids, const float* bias_values, int64_t bias_cap,
                         const int32_t* bias_count, int32_t* row_status, void* stream);
 
+/* The n most probable tokens of each row's candidate list and their natural
+ * log-probabilities under the final distribution (page "Sampling 系统设计：从
+ * logits 到可控生成", logprobs section: top tokens with their log-probabilities
+ * besides the chosen one's). The lists are those qs_filter_mask / qs_sample
+ * write (the final, renormalised distribution). Order: probability descending
+ * (float32 values compared exactly), ties by ascending id.
+ *
+ * cand_ids, cand_probs [B][cand_cap]; cand_count [B] int32
+ * n            slots per row, 1 <= n <= 4096
+ * top_ids      [B][n] int32 out: the ids, -1 past the list's length
+ * top_logprobs [B][n] float32 out: their log-probabilities (ln 2 (e + log2 m)
+ *              from frexp and the hardware log2, within about 1e-7), -inf past
+ *              the list's length (and for a probability of 0)
+ * row_status   [B] int32 out: QS_ROW_OK, or QS_ROW_BAD_PARAM (every slot
+ *              empty) when the count lies outside [0, cand_cap]
+ * Every pointer is required. One kernel launch on `stream`; nothing is
+ * allocated. */
+QS_API int qs_top_logprobs(int64_t B, const int32_t* cand_ids, const float* cand_probs,
+                    const int32_t* cand_count, int64_t cand_cap, int64_t n,
+                    int32_t* top_ids, float* top_logprobs, int32_t* row_status,
+                    void* stream);
+
 /* Library version string (static storage). */
 QS_API const char* qs_version(void);
 

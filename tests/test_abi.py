@@ -162,3 +162,17 @@ def test_apply_logit_bias_rejects_bad_arguments(lib):
                dict(status=None)):
         assert ab(**kw) == _lib.QS_ERR_INVALID_ARG, kw
     assert ab(B=0) == _lib.QS_OK
+
+
+def test_top_logprobs_rejects_bad_arguments(lib):
+    def tp(**kw):
+        a = dict(B=2, ids=A16, probs=A16, cnt=A16, cap=8, n=4, tid=A16, tlp=A16, status=A16,
+                 stream=None)
+        a.update(kw)
+        return lib.qs_top_logprobs(a["B"], a["ids"], a["probs"], a["cnt"], a["cap"], a["n"],
+                                   a["tid"], a["tlp"], a["status"], a["stream"])
+    for kw in (dict(B=-1), dict(cap=0), dict(n=0), dict(n=4097), dict(ids=None),
+               dict(probs=ctypes.c_void_p(0x100002)), dict(cnt=None), dict(tid=None),
+               dict(tlp=None), dict(status=None)):
+        assert tp(**kw) == _lib.QS_ERR_INVALID_ARG, kw
+    assert tp(B=0) == _lib.QS_OK

@@ -7,7 +7,8 @@ stream. The library is loaded on first use; calls raise if it is missing.
 """
 
 from ._lib import (  # noqa: F401
-    filter_mask, sample, argmax, spec_verify, apply_penalties, apply_logit_bias, load,
+    filter_mask, sample, argmax, spec_verify, apply_penalties, apply_logit_bias, top_logprobs,
+    load,
     LIB_PATH,
     ROW_OK, ROW_EMPTY, ROW_ALL_NEG_INF, ROW_NONFINITE, ROW_BAD_PARAM,
     ROW_CAND_OVERFLOW, ROW_INTERNAL, FLAG_FORCE_MISS, FLAG_NO_TRUNCATION,

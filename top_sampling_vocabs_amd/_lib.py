@@ -34,7 +34,7 @@ FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
 EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_apply_penalties",
-           "qs_apply_logit_bias", "qs_version")
+           "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
 
 _lib = None
 
@@ -86,6 +86,10 @@ def load(path=LIB_PATH):
         _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
         _p, _p, _i64, _p,                    # bias ids, values, cap, count
         _p, _p]                              # row_status, stream
+    lib.qs_top_logprobs.restype = _i32
+    lib.qs_top_logprobs.argtypes = [
+        _i64, _p, _p, _p, _i64, _i64,        # B, ids, probs, count, cap, n
+        _p, _p, _p, _p]                      # top ids, top logprobs, row_status, stream
     lib.qs_version.restype = ctypes.c_char_p
     lib.qs_version.argtypes = []
     if path == LIB_PATH:
@@ -327,3 +331,27 @@ def apply_logit_bias(logits, bias_ids, bias_values, bias_count):
                                  _ptr(bias_count), _ptr(status), _stream(logits.device))
     _status(rc, "qs_apply_logit_bias")
     return status
+
+
+def top_logprobs(cand_ids, cand_probs, cand_count, n):
+    """The n most probable tokens of each candidate list (as filter_mask / sample
+    return them) and their log-probabilities: (ids int32 [B, n], logprobs
+    float32 [B, n], status int32 [B])."""
+    import torch
+    lib = load()
+    B = int(cand_count.shape[0])
+    dev = cand_count.device
+    for t, dt, name in ((cand_ids, torch.int32, "cand_ids"), (cand_probs, torch.float32,
+                                                              "cand_probs")):
+        if t.dim() != 2 or t.shape[0] != B or t.dtype != dt or not t.is_contiguous() \
+                or t.device != dev:
+            raise ValueError(f"{name}: need a contiguous [B, cap] {dt} tensor on {dev}")
+    _check_rowvec(cand_count, B, torch.int32, "cand_count")
+    ids = torch.empty((B, n), dtype=torch.int32, device=dev)
+    lp = torch.empty((B, n), dtype=torch.float32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = lib.qs_top_logprobs(B, _ptr(cand_ids), _ptr(cand_probs), _ptr(cand_count),
+                             cand_ids.shape[1], int(n), _ptr(ids), _ptr(lp), _ptr(status),
+                             _stream(dev))
+    _status(rc, "qs_top_logprobs")
+    return ids, lp, status

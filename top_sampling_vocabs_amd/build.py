@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqs.so")
-SOURCES = ["qs_kernels.hip", "qs_api.hip", "qs_spec.hip", "qs_penalty.hip"]
+SOURCES = ["qs_kernels.hip", "qs_api.hip", "qs_spec.hip", "qs_penalty.hip", "qs_toplp.hip"]
 ARCH = os.environ.get("QS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

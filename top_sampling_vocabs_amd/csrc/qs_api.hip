@@ -233,6 +233,28 @@ int qs_apply_logit_bias(void* logits, int dtype, int64_t B, int64_t V, int64_t r
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;
 }
 
+int qs_top_logprobs(int64_t B, const int32_t* cand_ids, const float* cand_probs,
+                    const int32_t* cand_count, int64_t cand_cap, int64_t n, int32_t* top_ids,
+                    float* top_logprobs, int32_t* row_status, void* stream) {
+  if (B < 0 || B > kMaxB) return QS_ERR_INVALID_ARG;
+  if (B == 0) return QS_OK;
+  if (cand_cap < 1 || cand_cap > kMaxV || n < 1 || n > 4096) return QS_ERR_INVALID_ARG;
+  const void* req4[] = {cand_ids, cand_probs, cand_count, top_ids, top_logprobs, row_status};
+  for (const void* p : req4)
+    if (!p || !aligned(p, 4)) return QS_ERR_INVALID_ARG;
+  qs::TopArgs a;
+  a.ids = cand_ids;
+  a.probs = cand_probs;
+  a.count = cand_count;
+  a.cap = cand_cap;
+  a.n = (int)n;
+  a.out_ids = top_ids;
+  a.out_lp = top_logprobs;
+  a.status = row_status;
+  hipError_t e = qs::launch_top(a, (int)B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QS_OK : QS_ERR_HIP;
+}
+
 const char* qs_version(void) { return "qs 0.1.0 gfx950"; }
 
 }  // extern "C"

@@ -54,7 +54,19 @@ struct BiasArgs {
   int32_t* status;
 };
 
+struct TopArgs {
+  const int32_t* ids;      // [B][cap] candidate lists
+  const float* probs;
+  const int32_t* count;
+  int64_t cap;
+  int n;                   // slots per row
+  int32_t* out_ids;        // [B][n]
+  float* out_lp;           // [B][n]
+  int32_t* status;
+};
+
 hipError_t launch_spec(const SpecArgs& a, int B, hipStream_t st);
+hipError_t launch_top(const TopArgs& a, int B, hipStream_t st);
 hipError_t launch_penalty(const PenaltyArgs& a, int B, hipStream_t st);
 hipError_t launch_bias(const BiasArgs& a, int B, hipStream_t st);
 
