@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--spec", action="store_true",
                     help="instead of the headline line, time the speculative verifier "
                          "(qs_spec_verify) on candidate lists of the headline workload")
+    ap.add_argument("--toplp", type=int, default=0, metavar="N",
+                    help="instead of the headline line, time qs_top_logprobs (the N most "
+                         "probable tokens) on candidate lists of the headline workload")
     ap.add_argument("--penalties", action="store_true",
                     help="instead of the headline line, time qs_apply_penalties (2048-token "
                          "histories) on the headline batch, alone and followed by qs_sample")
@@ -309,6 +312,75 @@ def spec_bench(args, lib, stream):
     print(json.dumps(line), flush=True)
 
 
+class TopLPPrepared:
+    """Candidate lists of one input set, made on the device by the filter, and
+    the ctypes argument tuple of qs_top_logprobs for n slots a row."""
+
+    def __init__(self, lib, w, cap, n, stream):
+        import torch
+        import top_sampling_vocabs_amd as qs
+        dev = "cuda"
+        z = torch.from_numpy(w.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        T = torch.from_numpy(w.T).to(dev)
+        T = torch.where(T > 0, T, torch.ones_like(T))
+        k = torch.from_numpy(w.k).to(dev)
+        p = torch.from_numpy(w.p).to(dev)
+        bm = None if w.bitmask is None else torch.from_numpy(w.bitmask.view(np.int32)).to(dev)
+        self.t = qs.filter_mask(z, T, k, p, bm, cand_cap=cap)
+        self.ids = torch.empty(w.B, n, dtype=torch.int32, device=dev)
+        self.lp = torch.empty(w.B, n, dtype=torch.float32, device=dev)
+        self.status = torch.empty(w.B, dtype=torch.int32, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.args = (w.B, P(self.t["cand_ids"]), P(self.t["cand_probs"]), P(self.t["cand_count"]),
+                     cap, n, P(self.ids), P(self.lp), P(self.status), stream)
+        self.n = n
+        self.lib = lib
+
+    def call(self, stream=None, flags=None):
+        args = self.args if stream is None else self.args[:-1] + (stream,)
+        rc = self.lib.qs_top_logprobs(*args)
+        if rc != 0:
+            raise RuntimeError(f"qs_top_logprobs returned {rc}")
+
+    def bytes_moved(self):
+        """Algorithmic bytes: each row reads its count and its list once (8 bytes
+        an entry) and writes n (id, logprob) slots."""
+        tc = self.t["cand_count"].cpu().numpy().astype(np.int64)
+        assert (self.status.cpu().numpy() == 0).all()
+        return int(len(tc) * (4 + 8 * self.n) + 8 * tc.sum()), float(tc.mean())
+
+
+def toplp_bench(args, lib, stream):
+    import torch
+    cap = 16384
+    preps = [TopLPPrepared(lib, workloads.make(args.workload, seed=workloads.BASE_SEED +
+                                               args.workload + 1000 * i), cap, args.toplp, stream)
+             for i in range(args.sets)]
+    for i in range(args.warmup):
+        preps[i % len(preps)].call()
+    torch.cuda.synchronize()
+    ms, graph, cs = time_graph(preps, args.steps)
+    per = ms / args.steps
+    stats = [pr.bytes_moved() for pr in preps]
+    nbytes = sum(s[0] for s in stats) / len(stats)
+    B = preps[0].args[0]
+    line = {
+        "metric": f"top-{args.toplp} logprobs rows/sec over candidate lists, B=256 V=151936",
+        "value": round(B / (per * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(per, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "candidate lists (cap 16384) of the B=256 V=151936 bf16 batch",
+                   "n": args.toplp,
+                   "mean_list_length": round(float(np.mean([s[1] for s in stats])), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,
+                     "bytes_per_launch": int(nbytes)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 class PenaltyPrepared:
     """A 2048-token history per row (uniform ids, so about 2,030 distinct),
     repetition 1.2 and presence 0.3, and the ctypes tuple of qs_apply_penalties
@@ -496,6 +568,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.penalties:
         penalties_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        return
+    if args.toplp:
+        toplp_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         return
     if args.spec:
         spec_bench(args, lib, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))

@@ -21,12 +21,14 @@ def qs():
     return qs
 
 
-@pytest.mark.parametrize("n", [1, 20, 700])
-def test_top_logprobs_parity(qs, n):
+# (n, cap): n <= 64 with cap <= 16384 takes the register path (per-wave top n,
+# then one wave merges them); the others the block-wide rounds
+@pytest.mark.parametrize("n,cap", [(1, 9000), (20, 9000), (64, 9000), (65, 9000),
+                                   (20, 17000), (700, 9000)])
+def test_top_logprobs_parity(qs, n, cap):
     import torch
     w = workloads.make(3, B=24, V=9000)
     res = oracle.filter_batch(w.logits, w.dtype, w.T, w.k, w.p, w.bitmask)
-    cap = w.V
     ids = np.zeros((w.B, cap), np.int32)
     pr = np.zeros((w.B, cap), np.float32)
     cnt = np.zeros(w.B, np.int32)
@@ -37,7 +39,7 @@ def test_top_logprobs_parity(qs, n):
         cnt[r] = m
     pr[3, :cnt[3]] = np.float32(1.0 / max(cnt[3], 1))  # one row of exact ties
     cnt[5] = cap + 1                                     # a bad count
-    print(f"top logprobs n={n}", flush=True)
+    print(f"top logprobs n={n} cap={cap}", flush=True)
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     ti, tl, st = qs.top_logprobs(g(ids), g(pr), g(cnt), n)
     torch.cuda.synchronize()

@@ -12,6 +12,13 @@
 // takes the largest key below round j-1's winner: a block-wide maximum (wave
 // reductions, then the 4 waves' results through LDS), so no entry is marked
 // or moved. The log is ln 2 (e + log2 m) from frexp and the hardware log2.
+//
+// For n <= 64 over lists of at most 16,384 entries a second kernel keeps each
+// thread's 16 keys in registers and never waits on the block per round: each
+// of its 16 waves finds the top n of its own keys by wave-wide maxima, writes
+// them to LDS, and after the one barrier wave 0 takes the top n of those
+// 16 n survivors the same way. The global top n lie among the survivors,
+// since a key beaten by n larger keys of its own wave is beaten overall.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,6 +40,85 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallPer = 16;   // keys a thread holds: lists up to 16,384 entries
+constexpr int kSmallN = 64;     // largest n of the register path
+
+__device__ __forceinline__ float key_logprob(uint64_t b) {
+  const float q = __uint_as_float((uint32_t)(b >> 32));
+  int e;
+  const float m = frexpf(q, &e);
+  return q > 0.0f ? (float)(((double)e + (double)__log2f(m)) * 0.6931471805599453)
+                  : -INFINITY;
+}
+
+// Largest key below `prev` among this lane's keys, then across the wave.
+template <int N>
+__device__ __forceinline__ uint64_t wave_next_below(const uint64_t (&key)[N], uint64_t prev) {
+  uint64_t best = 0u;
+#pragma unroll
+  for (int t = 0; t < N; ++t) best = (key[t] < prev && key[t] > best) ? key[t] : best;
+  return wave_max_u64(best);
+}
+
+__global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopArgs a) {
+  __shared__ uint64_t s_cand[kSmallWaves * kSmallN];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid >> 6;
+  const int cnt = a.count[r];
+  int32_t* const out_id = a.out_ids + (size_t)r * a.n;
+  float* const out_lp = a.out_lp + (size_t)r * a.n;
+  if (cnt < 0 || (int64_t)cnt > a.cap) {
+    for (int j = tid; j < a.n; j += kSmallThreads) {
+      out_id[j] = -1;
+      out_lp[j] = -INFINITY;
+    }
+    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    return;
+  }
+  const int32_t* ids = a.ids + (size_t)r * a.cap;
+  const float* pr = a.probs + (size_t)r * a.cap;
+  uint64_t key[kSmallPer];
+#pragma unroll
+  for (int t = 0; t < kSmallPer; ++t) {
+    const int i = tid + t * kSmallThreads;
+    key[t] = i < cnt ? ((uint64_t)__float_as_uint(pr[i]) << 32) | (uint32_t)~ids[i] : 0u;
+  }
+  s_cand[tid] = 0u;  // slots a wave leaves unused read as "no key"
+  __syncthreads();
+  uint64_t prev = ~0ull;
+  for (int j = 0; j < a.n; ++j) {
+    const uint64_t b = wave_next_below(key, prev);
+    if (b == 0u) break;  // wave-uniform: this wave has no more keys
+    if (lane == 0) s_cand[w * kSmallN + j] = b;
+    prev = b;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  uint64_t cand[kSmallWaves];
+#pragma unroll
+  for (int t = 0; t < kSmallWaves; ++t) cand[t] = s_cand[t * kSmallN + lane];
+  prev = ~0ull;
+  int j = 0;
+  for (; j < a.n; ++j) {
+    const uint64_t b = wave_next_below(cand, prev);
+    if (b == 0u) break;
+    if (lane == 0) {
+      out_id[j] = (int32_t)~(uint32_t)b;
+      out_lp[j] = key_logprob(b);
+    }
+    prev = b;
+  }
+  for (int k = j + lane; k < a.n; k += 64) {  // fewer entries than n
+    out_id[k] = -1;
+    out_lp[k] = -INFINITY;
+  }
+  if (lane == 0) a.status[r] = QS_ROW_OK;
 }
 
 __global__ void __launch_bounds__(kTopThreads) top_logprobs_kernel(TopArgs a) {
@@ -73,12 +159,8 @@ __global__ void __launch_bounds__(kTopThreads) top_logprobs_kernel(TopArgs a) {
         out_id[j] = -1;
         out_lp[j] = -INFINITY;
       } else {
-        const float q = __uint_as_float((uint32_t)(b >> 32));
         out_id[j] = (int32_t)~(uint32_t)b;
-        int e;
-        const float m = frexpf(q, &e);
-        out_lp[j] = q > 0.0f ? (float)(((double)e + (double)__log2f(m)) * 0.6931471805599453)
-                             : -INFINITY;
+        out_lp[j] = key_logprob(b);
       }
     }
     prev = b;
@@ -96,6 +178,11 @@ __global__ void __launch_bounds__(kTopThreads) top_logprobs_kernel(TopArgs a) {
 }  // namespace
 
 hipError_t launch_top(const TopArgs& a, int B, hipStream_t st) {
+  if (a.n <= kSmallN && a.cap <= (int64_t)kSmallThreads * kSmallPer) {
+    hipLaunchKernelGGL(top_logprobs_small_kernel, dim3((unsigned)B), dim3(kSmallThreads), 0, st,
+                       a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(top_logprobs_kernel, dim3((unsigned)B), dim3(kTopThreads), 0, st, a);
   return hipGetLastError();
 }
