@@ -55,13 +55,41 @@ __device__ __forceinline__ float key_logprob(uint64_t b) {
                   : -INFINITY;
 }
 
+// One step of a wave maximum: the value of the lane the DPP pattern names
+// (both halves moved with the same pattern), kept if larger.
+template <int Ctrl>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, Ctrl, 0xF, 0xF, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), Ctrl, 0xF, 0xF, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Wave maximum: within each row of 16 lanes by DPP moves (swap neighbours,
+// swap pairs, mirror each half row, mirror the row: after each step every
+// lane holds the maximum of a group twice as large), then across the four
+// rows by two lane shuffles. Every lane of the wave must be active.
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm(1,0,3,2)
+  v = dpp_max_step<0x4E>(v);   // quad_perm(2,3,0,1)
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    const uint64_t o = (uint64_t)__shfl_xor((long long)v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 // Largest key below `prev` among this lane's keys, then across the wave.
 template <int N>
 __device__ __forceinline__ uint64_t wave_next_below(const uint64_t (&key)[N], uint64_t prev) {
   uint64_t best = 0u;
 #pragma unroll
   for (int t = 0; t < N; ++t) best = (key[t] < prev && key[t] > best) ? key[t] : best;
-  return wave_max_u64(best);
+  return wave_max_u64_dpp(best);
 }
 
 __global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopArgs a) {
