@@ -22,8 +22,10 @@ def qs():
 
 
 # (n, cap): n <= 64 with cap <= 16384 takes the register path (per-wave top n,
-# then one wave merges them); the others the block-wide rounds
-@pytest.mark.parametrize("n,cap", [(1, 9000), (20, 9000), (64, 9000), (65, 9000),
+# then one wave merges them; lanes sort their keys first from n = 16 on); the
+# others the block-wide rounds
+@pytest.mark.parametrize("n,cap", [(1, 9000), (15, 9000), (16, 9000), (20, 9000), (64, 9000),
+                                   (65, 9000),
                                    (20, 17000), (700, 9000)])
 def test_top_logprobs_parity(qs, n, cap):
     import torch

@@ -46,6 +46,7 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallPer = 16;   // keys a thread holds: lists up to 16,384 entries
 constexpr int kSmallN = 64;     // largest n of the register path
+constexpr int kSortFromN = 16;  // from this n on, lanes sort their keys first
 
 __device__ __forceinline__ float key_logprob(uint64_t b) {
   const float q = __uint_as_float((uint32_t)(b >> 32));
@@ -83,6 +84,42 @@ __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
   return v;
 }
 
+// Sorts a lane's keys into descending order (bitonic network; every index is
+// a compile-time constant, so the keys stay in registers).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool desc = (i & k) == 0;
+          const uint64_t x = key[i], y = key[l];
+          const bool sw = desc ? x < y : x > y;
+          key[i] = sw ? y : x;
+          key[l] = sw ? x : y;
+        }
+      }
+    }
+  }
+}
+
+// Takes the wave's largest head key; the lane that held it (keys are
+// distinct) moves its next key up. Returns 0 once every lane is empty.
+template <int N>
+__device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
+  const uint64_t b = wave_max_u64_dpp(key[0]);
+  if (b != 0u && key[0] == b) {
+#pragma unroll
+    for (int t = 0; t + 1 < N; ++t) key[t] = key[t + 1];
+    key[N - 1] = 0u;
+  }
+  return b;
+}
+
 // Largest key below `prev` among this lane's keys, then across the wave.
 template <int N>
 __device__ __forceinline__ uint64_t wave_next_below(const uint64_t (&key)[N], uint64_t prev) {
@@ -92,6 +129,9 @@ __device__ __forceinline__ uint64_t wave_next_below(const uint64_t (&key)[N], ui
   return wave_max_u64_dpp(best);
 }
 
+// Sorted: each lane sorts its keys once and a round looks at heads only (pays
+// off from about 16 rounds on); else every round scans all of a lane's keys.
+template <bool kSorted>
 __global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopArgs a) {
   __shared__ uint64_t s_cand[kSmallWaves * kSmallN];
   const int r = blockIdx.x;
@@ -119,9 +159,10 @@ __global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopAr
   }
   s_cand[tid] = 0u;  // slots a wave leaves unused read as "no key"
   __syncthreads();
+  if (kSorted) sort_desc(key);
   uint64_t prev = ~0ull;
   for (int j = 0; j < a.n; ++j) {
-    const uint64_t b = wave_next_below(key, prev);
+    const uint64_t b = kSorted ? wave_pop_max(key) : wave_next_below(key, prev);
     if (b == 0u) break;  // wave-uniform: this wave has no more keys
     if (lane == 0) s_cand[w * kSmallN + j] = b;
     prev = b;
@@ -131,10 +172,11 @@ __global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopAr
   uint64_t cand[kSmallWaves];
 #pragma unroll
   for (int t = 0; t < kSmallWaves; ++t) cand[t] = s_cand[t * kSmallN + lane];
+  if (kSorted) sort_desc(cand);
   prev = ~0ull;
   int j = 0;
   for (; j < a.n; ++j) {
-    const uint64_t b = wave_next_below(cand, prev);
+    const uint64_t b = kSorted ? wave_pop_max(cand) : wave_next_below(cand, prev);
     if (b == 0u) break;
     if (lane == 0) {
       out_id[j] = (int32_t)~(uint32_t)b;
@@ -207,8 +249,12 @@ __global__ void __launch_bounds__(kTopThreads) top_logprobs_kernel(TopArgs a) {
 
 hipError_t launch_top(const TopArgs& a, int B, hipStream_t st) {
   if (a.n <= kSmallN && a.cap <= (int64_t)kSmallThreads * kSmallPer) {
-    hipLaunchKernelGGL(top_logprobs_small_kernel, dim3((unsigned)B), dim3(kSmallThreads), 0, st,
-                       a);
+    if (a.n >= kSortFromN)
+      hipLaunchKernelGGL(top_logprobs_small_kernel<true>, dim3((unsigned)B), dim3(kSmallThreads),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL(top_logprobs_small_kernel<false>, dim3((unsigned)B), dim3(kSmallThreads),
+                         0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(top_logprobs_kernel, dim3((unsigned)B), dim3(kTopThreads), 0, st, a);
