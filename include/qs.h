@@ -269,8 +269,11 @@ QS_API int qs_apply_logit_bias(void* logits, int dtype, int64_t B, int64_t V, in
  * top_logprobs [B][n] float32 out: their log-probabilities (ln 2 (e + log2 m)
  *              from frexp and the hardware log2, within about 1e-7), -inf past
  *              the list's length (and for a probability of 0)
- * row_status   [B] int32 out: QS_ROW_OK, or QS_ROW_BAD_PARAM (every slot
- *              empty) when the count lies outside [0, cand_cap]
+ * row_status   [B] int32 out: QS_ROW_OK; QS_ROW_BAD_PARAM (every slot
+ *              empty) for a negative count; QS_ROW_CAND_OVERFLOW (every slot
+ *              empty) for a count above cand_cap, which is how the filter
+ *              reports a list it truncated: the filter's cand_cap must be at
+ *              least |P| for the top tokens of a row to be known
  * Every pointer is required. One kernel launch on `stream`; nothing is
  * allocated. */
 QS_API int qs_top_logprobs(int64_t B, const int32_t* cand_ids, const float* cand_probs,

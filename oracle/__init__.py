@@ -13,8 +13,8 @@ Modules:
   log-probability, keep-mask packing.
 * ``exact``    — rational-arithmetic mode for the pages' worked examples and a
   brute-force subset enumerator for tiny vocabularies.
-* ``philox``   — Philox4x32-10 from its published definition (parity unpinned:
-  the pages give no test vectors; pinned statistically only).
+* ``philox``   — Philox4x32-10 from its published definition, pinned by known
+  answers from rocRAND's independent implementation (host build of its header).
 * ``spec``     — exact speculative-decoding verification (accept with
   min(1, p/q), else resample from max(0, p - q)) over candidate lists.
 * ``penalties`` — repetition and presence penalties over each row's history,

@@ -18,10 +18,12 @@ not name a generator; the plain reading used throughout is Philox4x32-10 with
 counter = (offset_lo, offset_hi, 0, 0), key = (seed_lo, seed_hi) and a 24-bit
 uniform u = (x0 >> 8) * 2**-24 in [0, 1).
 
-Parity unpinned: the pages print no Philox values, so this generator is pinned
-only by statistical properties (uniformity, independence across offsets and
-seeds, bijectivity on a counter range) and by agreeing with the independent HIP
-implementation.
+Pinned by known answers from an independent implementation: rocRAND's
+Philox4x32-10 engine, compiled for the host from its header source in the ROCm
+installation (tests/test_philox_rocrand.py), on counters with non-zero high
+words and carries across 2**32, and for the (seed, offset) layout above (the
+draw at offset n is rocRAND's first output after rocrand_init(seed, 0, 4 n)).
+The pages themselves print no Philox values.
 """
 
 MASK32 = 0xFFFFFFFF

@@ -274,11 +274,14 @@ def top_logprobs_row(ids, probs, count, cap, n):
     return the top tokens with theirs). Order: probability descending (the
     list's float32 values compared exactly), ties by ascending id. Returns
     (status, ids[n], logprobs[n]); slots past the list's length hold id -1 and
-    -inf. A count outside [0, cap] is BAD_PARAM (all slots -1 / -inf)."""
+    -inf. A negative count is BAD_PARAM; a count above cap is a list the filter
+    truncated, CAND_OVERFLOW (all slots -1 / -inf either way)."""
     out_i = np.full(n, -1, np.int64)
     out_l = np.full(n, -np.inf)
-    if count < 0 or count > cap:
+    if count < 0:
         return ROW_BAD_PARAM, out_i, out_l
+    if count > cap:
+        return ROW_CAND_OVERFLOW, out_i, out_l
     q = np.asarray(probs[:count], np.float32)
     t = np.asarray(ids[:count], np.int64)
     order = sorted(range(count), key=lambda i: (-float(q[i]), int(t[i])))[:n]

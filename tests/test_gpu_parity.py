@@ -458,3 +458,37 @@ def test_histogram_pool_overflow_declines(qs):
     dbg = out["debug"].cpu().numpy()
     assert (dbg[:3, 1] >= 1).all(), dbg.tolist()   # declined: truncation path rounds
     assert (dbg[3:, 1] == 0).all(), dbg.tolist()   # settled by the value histogram
+
+
+@pytest.mark.gpu
+def test_topk_rank_among_zero_logits(qs):
+    """bf16 rows holding a few positive logits and thousands of exact zeros,
+    with k between the count of non-zero logits and the count of legal tokens:
+    the k-th largest value is 0, which the value histogram does not rank, so
+    those rows must leave that path and still match the oracle (top-k alone
+    and top-k followed by top-p). Ordinary top-k rows run first in the same
+    launch (more rows than compute units), so a workgroup that ran one of them
+    left its selection in LDS before a zero row reuses the unit."""
+    rng = np.random.default_rng(4242)
+    B, V = 600, 9000
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    k = rng.integers(20, 200, size=B).astype(np.int32)
+    p = np.ones(B, np.float32)
+    zero_rows = np.arange(320, B)
+    for r in zero_rows:
+        z[r] = 0.0
+        pos = rng.choice(V, size=10, replace=False)
+        z[r, pos] = rng.uniform(0.5, 4.0, size=10)
+        neg = rng.choice(V, size=50, replace=False)
+        z[r, neg] = -rng.uniform(0.5, 4.0, size=50)
+        k[r] = rng.integers(11, 2000)
+        p[r] = 1.0 if r % 2 else rng.uniform(0.3, 0.99)
+    bits = workloads._random_bitmask(rng, B, V, 0.6)
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=np.ones(B, np.float32), k=k, p=p,
+                           bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rows = list(range(0, 320, 16)) + zero_rows.tolist()
+    rep, out = check_workload(qs, w, rows=rows, seed=12, cand_cap=V, dense=False)
+    assert (out["status"].cpu().numpy()[zero_rows] == 0).all()

@@ -40,7 +40,8 @@ def test_top_logprobs_parity(qs, n, cap):
         pr[r, :m] = rr.q.astype(np.float32)
         cnt[r] = m
     pr[3, :cnt[3]] = np.float32(1.0 / max(cnt[3], 1))  # one row of exact ties
-    cnt[5] = cap + 1                                     # a bad count
+    cnt[5] = cap + 1                                     # a truncated list
+    cnt[6] = -1                                          # a bad count
     print(f"top logprobs n={n} cap={cap}", flush=True)
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     ti, tl, st = qs.top_logprobs(g(ids), g(pr), g(cnt), n)

@@ -325,8 +325,8 @@ def test_sampling_frequencies_match_q():
 
 
 def test_philox_uniform_statistics():
-    """Parity unpinned (no published vectors in the pages): the generator's
-    uniforms pass chi-square and independence checks, differ across seeds, and
+    """Statistical properties (the known-answer pin is in
+    test_philox_rocrand.py): the generator's uniforms pass chi-square and independence checks, differ across seeds, and
     distinct counters give distinct outputs (Philox is a bijection)."""
     us = np.array([oracle.uniform(12345, off) for off in range(20000)])
     hist, _ = np.histogram(us, bins=40, range=(0, 1))
@@ -520,6 +520,26 @@ def test_spec_verify_output_is_target(seed):
     assert abs(acc - (1.0 - 0.5 * float(np.abs(p - q).sum()))) < 2.0 / 512
 
 
+def test_spec_verify_lecture_exercise_3():
+    """Lecture exercise 3 and its answer (page "第 9 讲 · 生成与推测解码",
+    exercises): p = (0.5, 0.3, 0.2), q = (0.2, 0.5, 0.3) give the acceptance
+    rate 0.7, a residual that renormalises to (1, 0, 0) (every rejection
+    resamples token 0), and P(output 0) = 0.2 + 0.3 = 0.5 (grid 1/1000)."""
+    ids = np.arange(3)
+    p = np.array([0.5, 0.3, 0.2], np.float32)
+    q = np.array([0.2, 0.5, 0.3], np.float32)
+    out, acc = _out_distribution(ids, p, ids, q, n_grid=1000)
+    assert abs(acc - 0.7) < 2e-3, acc
+    for x in ids:
+        for u2 in (0.0, 0.3, 0.77, 0.999):
+            st, tok, a, _ = oracle.spec_verify_row(ids, p, 3, 3, ids, q, 3, 3, int(x), 0.999999,
+                                                   u2)
+            assert st == oracle.ROW_OK
+            assert a == 1 or tok == 0, (x, u2, tok)   # residual (1, 0, 0)
+    assert abs(out.get(0, 0.0) - 0.5) < 2e-3, out
+    assert abs(out.get(1, 0.0) - 0.3) < 2e-3 and abs(out.get(2, 0.0) - 0.2) < 2e-3, out
+
+
 def test_spec_verify_special_cases():
     ids = np.array([3, 7, 11, 20])
     p = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
@@ -637,7 +657,11 @@ def test_top_logprobs_worked_example():
     st, ti, tl = oracle.top_logprobs_row(np.array([3, 5, 9]), np.array([0.25, 0.5, 0.25],
                                          np.float32), 3, 3, 5)
     assert ti.tolist() == [5, 3, 9, -1, -1] and np.isneginf(tl[3:]).all()
+    # a count above the capacity is a truncated list (the filter's overflow
+    # status); a negative count is bad input
     assert oracle.top_logprobs_row(np.array([1]), np.array([1.0], np.float32), 2, 1, 1)[0] == \
+        oracle.ROW_CAND_OVERFLOW
+    assert oracle.top_logprobs_row(np.array([1]), np.array([1.0], np.float32), -1, 1, 1)[0] == \
         oracle.ROW_BAD_PARAM
     # against a brute-force ordering of a random list with many ties
     rng = np.random.default_rng(5)

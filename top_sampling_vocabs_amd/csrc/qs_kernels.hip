@@ -1682,12 +1682,6 @@ int resident_steps(int V) {
 
 template <int DT, bool S>
 hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
-#ifdef QS_DEV_ONE
-  if (DT != QS_DEV_DT || !S) return hipErrorInvalidValue;
-  a.seg = resident_steps(a.V) * kStep;
-  hipLaunchKernelGGL((filter_rows_kernel<QS_DEV_DT, true, QS_DEV_NL>), dim3((unsigned)B), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-#else
   dim3 grid((unsigned)B), block(kThreads);
   const int n = resident_steps(a.V);
   const bool stream = (a.flags & QS_FLAG_STREAM) != 0u;
@@ -1702,7 +1696,6 @@ hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
     hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0>), grid, block, 0, st, a);
   }
   return hipGetLastError();
-#endif
 }
 
 }  // namespace

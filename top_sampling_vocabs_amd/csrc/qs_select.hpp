@@ -148,7 +148,13 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     uint4* const h4 = reinterpret_cast<uint4*>(hist);
     for (int i = tid; i < sel::kBins / 4; i += kThreads) h4[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  if (tid == 0) info.claim = ~0ull;
+  if (tid == 0) {
+    info.claim = ~0ull;
+    // no run holds rank k when k lies past the exact values (tiny values,
+    // zeros among them, are not ranked): the k search then finds nothing and
+    // the row declines
+    info.sel_u[0] = sel::kNone;
+  }
   __syncthreads();  // cleared histogram
   static_for<kEarly, kLook>(issue);
 

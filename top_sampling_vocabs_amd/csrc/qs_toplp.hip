@@ -146,7 +146,9 @@ __global__ void __launch_bounds__(kSmallThreads) top_logprobs_small_kernel(TopAr
       out_id[j] = -1;
       out_lp[j] = -INFINITY;
     }
-    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    // a count above the capacity is a list the filter truncated (its overflow
+    // status); a negative count is bad input
+    if (tid == 0) a.status[r] = cnt < 0 ? QS_ROW_BAD_PARAM : QS_ROW_CAND_OVERFLOW;
     return;
   }
   const int32_t* ids = a.ids + (size_t)r * a.cap;
@@ -205,7 +207,9 @@ __global__ void __launch_bounds__(kTopThreads) top_logprobs_kernel(TopArgs a) {
       out_id[j] = -1;
       out_lp[j] = -INFINITY;
     }
-    if (tid == 0) a.status[r] = QS_ROW_BAD_PARAM;
+    // a count above the capacity is a list the filter truncated (its overflow
+    // status); a negative count is bad input
+    if (tid == 0) a.status[r] = cnt < 0 ? QS_ROW_BAD_PARAM : QS_ROW_CAND_OVERFLOW;
     return;
   }
   const int32_t* ids = a.ids + (size_t)r * a.cap;
