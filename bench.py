@@ -78,8 +78,9 @@ class Prepared:
     """One input set on the device with preallocated outputs and the ctypes
     argument tuple for qs_sample (no Python-side allocation in the loop)."""
 
-    def __init__(self, lib, w, cand_cap, flags, stream):
+    def __init__(self, lib, w, cand_cap, flags, stream, workspace=None):
         import torch
+        import top_sampling_vocabs_amd as qs
         dev = "cuda"
         self.w = w
         if w.dtype == "bf16":
@@ -100,6 +101,13 @@ class Prepared:
         self.cids = torch.empty((w.B, cand_cap), dtype=torch.int32, device=dev)
         self.cprobs = torch.empty((w.B, cand_cap), dtype=torch.float32, device=dev)
         self.ccount = torch.empty(w.B, dtype=torch.int32, device=dev)
+        # the caller-owned scratch (input sets of one shape may share one: the
+        # calls run one after another on one stream)
+        need = qs.workspace_bytes(w.B, w.V, 1 if w.dtype == "bf16" else 0, cand_cap)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.ws = workspace
+        self.ws_bytes = need
         P = ctypes.c_void_p
         self.args = (
             P(self.logits.data_ptr()), 1 if w.dtype == "bf16" else 0, w.B, w.V, w.V,
@@ -109,17 +117,21 @@ class Prepared:
             P(self.seed.data_ptr()), P(self.offset.data_ptr()), None,
             P(self.tokens.data_ptr()), None, P(self.keep.data_ptr()), P(self.cids.data_ptr()),
             P(self.cprobs.data_ptr()), P(self.ccount.data_ptr()), cand_cap, None,
-            P(self.status.data_ptr()), None, flags, stream)
+            P(self.status.data_ptr()), None, flags,
+            None if workspace is None else P(workspace.data_ptr()), need, stream)
         self.lib = lib
 
+    # positions in the argument tuple, counted from its end
+    _FLAGS, _DEBUG = -4, -5
+
     def call(self, stream=None, flags=None, debug=None):
-        args = self.args
+        args = list(self.args)
         if flags is not None:
-            args = args[:-2] + (flags, args[-1])
+            args[self._FLAGS] = flags
         if debug is not None:
-            args = args[:-3] + (ctypes.c_void_p(debug.data_ptr()),) + args[-2:]
+            args[self._DEBUG] = ctypes.c_void_p(debug.data_ptr())
         if stream is not None:
-            args = args[:-1] + (stream,)
+            args[-1] = stream
         rc = self.lib.qs_sample(*args)
         if rc != 0:
             raise RuntimeError(f"qs_sample returned {rc}")
@@ -131,8 +143,9 @@ class Prepared:
 
 # the translation unit of the filter/sample kernel (the other entry points'
 # kernels live in files of their own and do not change it)
-FILTER_SOURCES = ("qs_device.hpp", "qs_kernels.hip", "qs_launch.hpp", "qs_select.hpp",
-                  "qs_stream.hpp")
+FILTER_SOURCES = ("qs_device.hpp", "qs_filter.hpp", "qs_filter_bf16.hip", "qs_filter_f32.hip",
+                  "qs_launch.hpp", "qs_select.hpp", "qs_stream.hpp", "qs_merge.hpp",
+                  "qs_bins.hpp", "qs_chunk.hpp", "qs_chunk.hip")
 
 
 def source_digest():
@@ -583,7 +596,9 @@ def main():
     sets = [base] + [workloads.make(cfg, seed=workloads.BASE_SEED + cfg + 1000 * i)
                      for i in range(1, args.sets)]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    preps = [Prepared(lib, w, args.cand_cap, args.flags, stream) for w in sets]
+    preps = [Prepared(lib, w, args.cand_cap, args.flags, stream) for w in sets[:1]]
+    preps += [Prepared(lib, w, args.cand_cap, args.flags, stream, workspace=preps[0].ws)
+              for w in sets[1:]]
     torch.cuda.synchronize()
     bytes_read = workloads.bytes_read(base)
     B = base.B

@@ -12,8 +12,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Every array argument is a DEVICE pointer owned by the caller. The library
- *   allocates nothing, keeps no state between calls and never synchronises:
+ * - Every array argument is a DEVICE pointer owned by the caller, scratch
+ *   included (the `workspace` argument). The library allocates nothing, keeps
+ *   no state between calls and never synchronises:
  *   work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *   default stream). Row outputs are valid once the caller has synchronised
  *   with that stream. Concurrent calls on different streams are safe.
@@ -24,9 +25,11 @@
  *   32-bit word (i >> 5); W = ceil(V/32) words per row, rows `bitmask_stride`
  *   words apart (>= W). Bits at positions >= V are ignored. NULL = all legal.
  * - Return value: QS_OK, or QS_ERR_INVALID_ARG when a pointer, size, stride or
- *   alignment check fails (reported before any HIP call, nothing is
- *   enqueued), or QS_ERR_HIP when the launch fails. Row errors are reported
- *   per row in `row_status` (qs_row_status), never by the return value.
+ *   alignment check fails, or QS_ERR_WORKSPACE when the workspace is missing,
+ *   misaligned or smaller than qs_workspace_bytes (both reported before any
+ *   HIP call, nothing is enqueued), or QS_ERR_HIP when a launch fails. Row
+ *   errors are reported per row in `row_status` (qs_row_status), never by
+ *   the return value.
  * - Parameter semantics (page "Sampling 系统设计", temperature section: T = 0 is
  *   greedy, and T < 0, p > 1, k < 0 must be rejected): T finite and >= 0,
  *   T == 0 selects the greedy argmax path; k == 0 disables top-k and k >= the
@@ -58,6 +61,7 @@ extern "C" {
 typedef enum {
   QS_OK = 0,
   QS_ERR_INVALID_ARG = 1,
+  QS_ERR_WORKSPACE = 2,      /* workspace missing, misaligned or too small  */
   QS_ERR_HIP = 3
 } qs_status;
 
@@ -88,6 +92,27 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
 #define QS_FLAG_BINARY_PIVOT  16u  /* one pivot per search round (the interval's
                                       midpoint) instead of three (ablation)     */
 
+/* Device scratch a qs_filter_mask / qs_sample call on B rows of V tokens of
+ * `dtype` needs, in bytes (0: none). The caller owns it and passes it as
+ * `workspace` / `workspace_bytes`; the library never allocates.
+ *
+ * It holds the candidate set compacted from each row before the selection
+ * (page "Qrita", overall framework: the truncation pass writes a small
+ * candidate set that the pivot searches then work on; its closing section
+ * names full-vocabulary temporaries as a cost, so the buffer is capped:
+ * at most 896 entries of every 4096-token segment of a row, plus 32 bytes
+ * per segment and 32 per 16384-token chunk). For bf16 rows of up to 2^20
+ * tokens, with S = ceil(V / 16384) chunks a row, it is
+ *   align256(B * 4S * 32) + align256(B * S * 32) + B * 4S * 896 * 4 bytes;
+ * other calls need none. cand_cap does not change it (the caller's candidate
+ * lists are outputs, not scratch). Pure function of its arguments; 0 for
+ * invalid ones.
+ *
+ * The workspace must be 256-byte aligned. Its contents on entry do not
+ * matter and are left undefined; two calls that may run at the same time
+ * (different streams) need different workspaces. */
+QS_API size_t qs_workspace_bytes(int64_t B, int64_t V, int dtype, int64_t cand_cap);
+
 /* Filter a batch: kept-candidate mask and renormalised probabilities.
  *
  * Defines the candidate set O of page "Qrita" (overall framework: strict
@@ -106,11 +131,16 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
  *              (0 outside P)
  * row_status   [B] int32 out, required (qs_row_status)
  * debug_stats  [B][4] int32 out, optional: {path (0 candidate pool, 1 full
- *              row), search rounds, |Z_t| (candidates above the truncation
- *              threshold), |P|}; bf16 rows settled by the value histogram
- *              report path 0 with 0 rounds and |Z_t| = the tokens at or above
- *              the final boundary value
+ *              row, 2 candidates of the chunked first pass), search rounds,
+ *              |Z_t| (candidates above the truncation threshold), |P|}; bf16
+ *              rows settled by a value histogram report 0 rounds (path 0 with
+ *              |Z_t| = the tokens at or above the final boundary value when
+ *              the row was held in registers)
  * flags        QS_FLAG_* bits, 0 normally
+ * workspace, workspace_bytes
+ *              device scratch of at least qs_workspace_bytes(B, V, dtype,
+ *              cand_cap) bytes, 256-byte aligned (NULL / 0 when that is 0);
+ *              otherwise QS_ERR_WORKSPACE is returned before any HIP call.
  */
 QS_API int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V,
                    int64_t row_stride, const float* temperature,
@@ -119,12 +149,12 @@ QS_API int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V,
                    uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
                    int32_t* cand_count, int64_t cand_cap, float* dense_probs,
                    int32_t* row_status, int32_t* debug_stats, uint32_t flags,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Filter and draw one token per row.
  *
- * Same inputs and optional outputs as qs_filter_mask (keep_mask is optional
- * here). The draw walks P in ascending token id and returns the first id whose
+ * Same inputs, optional outputs and workspace as qs_filter_mask (keep_mask
+ * is optional here). The draw walks P in ascending token id and returns the first id whose
  * cumulative probability exceeds u (page "Attention算完，还没有选出下一个token",
  * section 02 widget: CDF by token id; right-open intervals).
  *
@@ -153,7 +183,7 @@ QS_API int qs_sample(const void* logits, int dtype, int64_t B, int64_t V,
               int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
               float* cand_probs, int32_t* cand_count, int64_t cand_cap,
               float* dense_probs, int32_t* row_status, int32_t* debug_stats,
-              uint32_t flags, void* stream);
+              uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Greedy selection: tokens[r] = lowest token id holding the largest finite
  * legal logit. No softmax and no random number (page "第 9 讲 · 生成与推测解码",

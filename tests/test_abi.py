@@ -46,18 +46,21 @@ def test_missing_library_fails_loudly(tmp_path):
 # dereferences or launches anything, so no GPU is needed.
 A16 = ctypes.c_void_p(0x100000)
 A8 = ctypes.c_void_p(0x200000)
+WS = ctypes.c_void_p(0x400000)   # a 256-byte aligned workspace address
+WSN = 1 << 30                    # and a size above any requirement below
 
 
 def filt(lib, **kw):
     args = dict(logits=A16, dtype=0, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
                 bitmask=None, bms=0, keep=A16, cids=None, cprobs=None, ccount=None,
-                cap=0, dense=None, status=A16, dbg=None, flags=0, stream=None)
+                cap=0, dense=None, status=A16, dbg=None, flags=0, ws=WS, wsn=WSN, stream=None)
     args.update(kw)
     return lib.qs_filter_mask(args["logits"], args["dtype"], args["B"], args["V"],
                               args["stride"], args["T"], args["k"], args["p"],
                               args["bitmask"], args["bms"], args["keep"], args["cids"],
                               args["cprobs"], args["ccount"], args["cap"], args["dense"],
-                              args["status"], args["dbg"], args["flags"], args["stream"])
+                              args["status"], args["dbg"], args["flags"], args["ws"],
+                              args["wsn"], args["stream"])
 
 
 @pytest.mark.parametrize("kw", [
@@ -82,14 +85,14 @@ def smp(lib, **kw):
     args = dict(logits=A16, dtype=1, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
                 bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16, lp=None,
                 keep=None, cids=None, cprobs=None, ccount=None, cap=0, dense=None,
-                status=A16, dbg=None, flags=0, stream=None)
+                status=A16, dbg=None, flags=0, ws=WS, wsn=WSN, stream=None)
     args.update(kw)
     return lib.qs_sample(args["logits"], args["dtype"], args["B"], args["V"], args["stride"],
                          args["T"], args["k"], args["p"], args["bitmask"], args["bms"],
                          args["seed"], args["offset"], args["uni"], args["tokens"],
                          args["lp"], args["keep"], args["cids"], args["cprobs"], args["ccount"],
                          args["cap"], args["dense"], args["status"], args["dbg"],
-                         args["flags"], args["stream"])
+                         args["flags"], args["ws"], args["wsn"], args["stream"])
 
 
 @pytest.mark.parametrize("kw", [
@@ -100,6 +103,42 @@ def smp(lib, **kw):
 ])
 def test_sample_rejects_bad_arguments(lib, kw):
     assert smp(lib, **kw) == _lib.QS_ERR_INVALID_ARG
+
+
+def test_workspace_bytes(lib):
+    """bf16 calls need per 4096-token segment of a row 32 bytes and 896
+    candidate entries of 4 bytes, plus 32 bytes per 16384-token chunk (each part
+    rounded up to 256 bytes);
+    fp32 calls and invalid arguments need none; cand_cap does not matter."""
+    def want(B, V):
+        S = -(-V // 16384)
+        a256 = lambda x: -(-x // 256) * 256  # noqa: E731
+        return a256(B * 4 * S * 32) + a256(B * S * 32) + B * 4 * S * 896 * 4
+    for B, V in ((4, 64), (256, 151936), (512, 151936), (3, 16384), (1, 16385),
+                 (2, 64 * 16384)):
+        assert lib.qs_workspace_bytes(B, V, 1, 0) == want(B, V), (B, V)
+        assert lib.qs_workspace_bytes(B, V, 1, 12345) == want(B, V)
+        assert lib.qs_workspace_bytes(B, V, 0, 0) == 0
+    assert lib.qs_workspace_bytes(0, 100, 1, 0) == 0
+    assert lib.qs_workspace_bytes(4, 0, 1, 0) == 0
+    assert lib.qs_workspace_bytes(-1, 100, 1, 0) == 0
+    assert lib.qs_workspace_bytes(4, 100, 7, 0) == 0
+    assert lib.qs_workspace_bytes(4, 64 * 16384 + 1, 1, 0) == 0   # rows past 64 chunks
+
+
+@pytest.mark.parametrize("call", ["filter", "sample"])
+def test_workspace_rejected_before_any_hip_call(lib, call):
+    """A missing, misaligned or short workspace is QS_ERR_WORKSPACE; argument
+    errors are still reported first; fp32 calls need no workspace."""
+    f = (lambda **kw: filt(lib, dtype=1, stride=64, **kw)) if call == "filter" else \
+        (lambda **kw: smp(lib, **kw))
+    need = lib.qs_workspace_bytes(4, 64, 1, 0)
+    assert f(ws=None, wsn=0) == _lib.QS_ERR_WORKSPACE
+    assert f(ws=None, wsn=need) == _lib.QS_ERR_WORKSPACE
+    assert f(ws=ctypes.c_void_p(0x400010), wsn=need) == _lib.QS_ERR_WORKSPACE
+    assert f(ws=WS, wsn=need - 1) == _lib.QS_ERR_WORKSPACE
+    assert f(ws=None, wsn=0, T=None) == _lib.QS_ERR_INVALID_ARG
+    assert f(ws=None, wsn=0, B=0) == _lib.QS_OK
 
 
 def test_argmax_rejects_bad_arguments(lib):

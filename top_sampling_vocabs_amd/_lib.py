@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG, "libqs.so")
 
 QS_OK = 0
 QS_ERR_INVALID_ARG = 1
+QS_ERR_WORKSPACE = 2
 QS_ERR_HIP = 3
 
 ROW_OK = 0
@@ -33,8 +34,8 @@ FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
-EXPORTS = ("qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify", "qs_apply_penalties",
-           "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
+EXPORTS = ("qs_workspace_bytes", "qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify",
+           "qs_apply_penalties", "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
 
 _lib = None
 
@@ -42,6 +43,7 @@ _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int
 _u32 = ctypes.c_uint32
+_sz = ctypes.c_size_t
 
 
 def load(path=LIB_PATH):
@@ -53,13 +55,16 @@ def load(path=LIB_PATH):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m top_sampling_vocabs_amd.build`")
     lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    lib.qs_workspace_bytes.restype = _sz
+    lib.qs_workspace_bytes.argtypes = [_i64, _i64, _i32, _i64]   # B, V, dtype, cand_cap
     lib.qs_filter_mask.restype = _i32
     lib.qs_filter_mask.argtypes = [
         _p, _i32, _i64, _i64, _i64,          # logits, dtype, B, V, row_stride
         _p, _p, _p,                          # temperature, top_k, top_p
         _p, _i64,                            # bitmask, bitmask_stride
         _p, _p, _p, _p, _i64,                # keep_mask, cand_ids, cand_probs, cand_count, cand_cap
-        _p, _p, _p, _u32, _p]                # dense, row_status, debug, flags, stream
+        _p, _p, _p, _u32,                    # dense, row_status, debug, flags
+        _p, _sz, _p]                         # workspace, workspace_bytes, stream
     lib.qs_sample.restype = _i32
     lib.qs_sample.argtypes = [
         _p, _i32, _i64, _i64, _i64,
@@ -67,7 +72,8 @@ def load(path=LIB_PATH):
         _p, _i64,
         _p, _p, _p, _p, _p,                  # seed, offset, uniforms, tokens, logprobs
         _p, _p, _p, _p, _i64,
-        _p, _p, _p, _u32, _p]
+        _p, _p, _p, _u32,
+        _p, _sz, _p]
     lib.qs_argmax.restype = _i32
     lib.qs_argmax.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
     lib.qs_spec_verify.restype = _i32
@@ -136,12 +142,37 @@ def _check_logits(logits, bitmask):
 
 def _status(rc, what):
     if rc != QS_OK:
-        name = {QS_ERR_INVALID_ARG: "QS_ERR_INVALID_ARG", QS_ERR_HIP: "QS_ERR_HIP"}.get(rc, rc)
+        name = {QS_ERR_INVALID_ARG: "QS_ERR_INVALID_ARG", QS_ERR_WORKSPACE: "QS_ERR_WORKSPACE",
+                QS_ERR_HIP: "QS_ERR_HIP"}.get(rc, rc)
         raise RuntimeError(f"{what} returned {name}")
 
 
+def workspace_bytes(B, V, dtype_code, cand_cap=0):
+    """Device scratch (bytes) a filter_mask / sample call on [B, V] logits needs."""
+    return int(load().qs_workspace_bytes(int(B), int(V), int(dtype_code), int(cand_cap)))
+
+
+def workspace_for(logits, cand_cap=0):
+    """A workspace tensor (uint8, on the logits' device) sized for these logits,
+    or None when the call needs none. Reuse it across calls on one stream."""
+    import torch
+    B, V = logits.shape
+    n = workspace_bytes(B, V, _dtype_code(logits), cand_cap)
+    return torch.empty(n, dtype=torch.uint8, device=logits.device) if n else None
+
+
+def _workspace_args(workspace, logits, cand_cap):
+    if workspace is None:
+        workspace = workspace_for(logits, cand_cap)
+    if workspace is None:
+        return None, 0, None
+    if not workspace.is_cuda or workspace.device != logits.device:
+        raise ValueError("workspace must be a CUDA tensor on the logits' device")
+    return _ptr(workspace), workspace.numel() * workspace.element_size(), workspace
+
+
 def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
-                dense=False, debug=False, flags=0):
+                dense=False, debug=False, flags=0, workspace=None):
     """Kept-candidate mask and renormalised probabilities for every row.
 
     logits [B, V] float32 / bfloat16 (CUDA); temperature, top_p float32 [B];
@@ -149,7 +180,9 @@ def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
     None. Returns a dict of device tensors: keep_mask (int32 words [B, W]),
     status [B], and if requested cand_ids / cand_probs [B, cand_cap],
     cand_count [B], dense [B, V], debug [B, 4]. Enqueued on the current stream;
-    synchronise before reading.
+    synchronise before reading. workspace: a device buffer of at least
+    workspace_bytes(...) bytes (workspace_for(logits) makes one); allocated
+    per call when omitted.
     """
     import torch
     lib = load()
@@ -169,20 +202,21 @@ def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
         out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
     if debug:
         out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
     rc = lib.qs_filter_mask(
         _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
         _ptr(temperature), _ptr(top_k), _ptr(top_p),
         _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
         _ptr(out["keep_mask"]), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
         _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
-        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), _stream(dev))
+        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), ws_p, ws_n, _stream(dev))
     _status(rc, "qs_filter_mask")
     return out
 
 
 def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset=None,
            uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False,
-           logprobs=False, flags=0):
+           logprobs=False, flags=0, workspace=None):
     """Filter and draw one token per row.
 
     seed, offset: int64 [B] CUDA tensors holding the uint64 RNG state; offset is
@@ -190,7 +224,7 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
     [B] to use fixed u values instead (offsets untouched). logprobs: also
     return the log-probability of each drawn token under the distribution it
     was drawn from (float32 [B]). Returns a dict with tokens [B], status [B]
-    and the optional outputs of filter_mask.
+    and the optional outputs of filter_mask. workspace as for filter_mask.
     """
     import torch
     lib = load()
@@ -219,6 +253,7 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
         out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
     if debug:
         out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
     rc = lib.qs_sample(
         _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
         _ptr(temperature), _ptr(top_k), _ptr(top_p),
@@ -227,7 +262,7 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
         _ptr(offset) if uniforms is None else None, _ptr(uniforms), _ptr(out["tokens"]),
         _ptr(out.get("logprobs")), _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
         _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
-        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), _stream(dev))
+        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), ws_p, ws_n, _stream(dev))
     _status(rc, "qs_sample")
     return out
 

@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation (before any HIP call), launch
-// geometry, and error mapping. Every entry point enqueues exactly one kernel
-// launch on the caller's stream and returns without synchronising.
+// geometry, and error mapping. Every entry point enqueues its kernels on the
+// caller's stream (one launch; two for bf16 filter calls: the chunk pass and
+// the per-row filter) and returns without synchronising.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,6 +9,7 @@
 #include "../../include/qs.h"
 
 #include "qs_aux.hpp"
+#include "qs_chunk.hpp"
 #include "qs_launch.hpp"
 
 namespace {
@@ -16,6 +18,13 @@ constexpr int64_t kMaxV = (int64_t)1 << 30;
 constexpr int64_t kMaxB = ((int64_t)1 << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Workspace of the chunked first pass: bf16 rows of up to kMaxChunks chunks.
+size_t ws_bytes(int64_t B, int64_t V, int dtype) {
+  if (dtype != QS_BF16 || B == 0) return 0;
+  if (qs::chunk::chunks_for(V) > qs::chunk::kMaxChunks) return 0;
+  return qs::chunk::workspace_bytes(B, V);
+}
 
 // Shared checks of the logits / bitmask description.
 int check_input(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
@@ -40,7 +49,8 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
                   int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
                   float* cand_probs,
                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
-                  int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* stream) {
+                  int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
   if (rc != QS_OK) return rc;
   if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION | QS_FLAG_PIVOT_SEARCH |
@@ -62,6 +72,10 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
       !aligned(debug_stats, 4) || !aligned(tokens, 4) || !aligned(logprobs, 4) ||
       !aligned(seed, 8) || !aligned(offset, 8) || !aligned(uniforms, 8))
     return QS_ERR_INVALID_ARG;
+  const size_t need = ws_bytes(B, V, dtype);
+  if (need > 0) {
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return QS_ERR_WORKSPACE;
+  }
 
   qs::FilterArgs a;
   a.logits = static_cast<const uint8_t*>(logits);
@@ -87,7 +101,38 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.status = row_status;
   a.dbg = debug_stats;
   a.flags = flags;
-  hipError_t e = qs::launch_filter(a, dtype, sample, (int)B, static_cast<hipStream_t>(stream));
+  a.ws_segs = nullptr;
+  a.ws_mass = nullptr;
+  a.ws_cands = nullptr;
+  a.S = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (need > 0 && flags == 0u) {
+    // bf16: the chunk kernel streams every row first, the filter kernel then
+    // settles each row from the chunks' candidates (path switches skip it)
+    qs::chunk::Args ca;
+    ca.logits = a.logits;
+    ca.row_bytes = a.row_bytes;
+    ca.V = a.V;
+    ca.B = (int)B;
+    ca.S = qs::chunk::chunks_for(V);
+    ca.stride = qs::chunk::sample_stride(V);
+    ca.T = temperature;
+    ca.k = top_k;
+    ca.p = top_p;
+    ca.bitmask = bitmask;
+    ca.bm_stride = bitmask_stride;
+    uint8_t* const ws = static_cast<uint8_t*>(workspace);
+    ca.segs = reinterpret_cast<qs::chunk::SegSummary*>(ws);
+    ca.mass = reinterpret_cast<qs::chunk::ChunkMass*>(ws + qs::chunk::seg_bytes(B, V));
+    ca.cands = reinterpret_cast<uint32_t*>(ws + qs::chunk::seg_bytes(B, V) +
+                                           qs::chunk::mass_bytes(B, V));
+    if (qs::chunk::launch_scan_bf16(ca, st) != hipSuccess) return QS_ERR_HIP;
+    a.ws_segs = ca.segs;
+    a.ws_mass = ca.mass;
+    a.ws_cands = ca.cands;
+    a.S = ca.S;
+  }
+  hipError_t e = qs::launch_filter(a, dtype, sample, (int)B, st);
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;
 }
 
@@ -95,16 +140,23 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
 
 extern "C" {
 
+size_t qs_workspace_bytes(int64_t B, int64_t V, int dtype, int64_t cand_cap) {
+  (void)cand_cap;
+  if (B < 0 || B > kMaxB || V < 1 || V > kMaxV || (dtype != QS_F32 && dtype != QS_BF16))
+    return 0;
+  return ws_bytes(B, V, dtype);
+}
+
 int qs_filter_mask(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                    const float* temperature, const int32_t* top_k, const float* top_p,
                    const uint32_t* bitmask, int64_t bitmask_stride, uint32_t* keep_mask,
                    int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
                    float* dense_probs, int32_t* row_status, int32_t* debug_stats,
-                   uint32_t flags, void* stream) {
+                   uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
   return filter_common(false, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
                        bitmask, bitmask_stride, nullptr, nullptr, nullptr, nullptr, nullptr, keep_mask,
                        cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
-                       debug_stats, flags, stream);
+                       debug_stats, flags, workspace, workspace_bytes, stream);
 }
 
 int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
@@ -113,11 +165,11 @@ int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_s
               uint64_t* offset, const double* uniforms, int32_t* tokens, float* logprobs,
               uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs, int32_t* cand_count, int64_t cand_cap,
               float* dense_probs, int32_t* row_status, int32_t* debug_stats, uint32_t flags,
-              void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream) {
   return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
                        bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
                        keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
-                       debug_stats, flags, stream);
+                       debug_stats, flags, workspace, workspace_bytes, stream);
 }
 
 int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,

@@ -295,4 +295,65 @@ __device__ __forceinline__ uint32_t philox_u24(uint64_t seed, uint64_t offset) {
   return c0 >> 8;
 }
 
+// ---------------------------------------------------------------------------
+// Packed 16-bit views of a 32-bit register (two bf16 tokens per register).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ s16x2 as_s2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
+__device__ __forceinline__ u16x2 as_u2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t bits_of(s16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ uint32_t bits_of(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  return (m & a) | (~m & b);
+}
+
+// The sigma-truncation threshold as a value (page "Qrita", key design 1 and
+// the lookup table of the training-strategy paragraph): delta = Phi^-1(1 -
+// k/V) for top-k; for top-p the mass-weighted Gaussian N(mu + sigma^2/T,
+// sigma^2), truncated at the sample maximum, gives the value above which a
+// fraction p of the mass lies. t = t0 - 0.2|t0|, never above the sample max.
+// The quantiles are single precision: t only decides how many tokens are
+// compacted, never which tokens are kept. Returns -inf when every finite
+// legal token must be a candidate.
+__device__ __forceinline__ double truncation_value(double n_s, double sum, double sumsq,
+                                                   double ms, double frac_legal, int V,
+                                                   bool greedy, bool topk_on, int k,
+                                                   bool topp_on, double p, double invT) {
+  const double ninf = -__builtin_inf();
+  if (n_s < 1.0) return ninf;
+  if (greedy) return ms;
+  const double mu = sum / n_s;
+  const double var = sumsq / n_s - mu * mu;
+  const double sd = var > 0.0 ? sqrt(var) : 0.0;
+  double t0;
+  if (topk_on) {
+    const double q = (double)k / (frac_legal * (double)V);
+    if (!(q < 1.0)) return ninf;
+    t0 = mu + sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * q)));
+  } else if (topp_on) {
+    if (!(sd > 0.0)) return ninf;
+    const double mp = mu + sd * sd * invT;
+    const double a = (ms - mp) / sd;
+    const double c = (1.0 - p) * 0.5 * (double)erfcf((float)(-a * 0.7071067811865476));
+    if (!(c > 0.0)) return ninf;
+    t0 = mp - sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * c)));
+  } else {
+    return ninf;
+  }
+  double t = t0 - 0.2 * fabs(t0);
+  if (!(t < ms)) t = ms;
+  if (!(t > -3.0e38)) return ninf;
+  return t;
+}
+
+// The largest bf16 / fp32 value <= t (t finite), as raw bits.
+template <int DT>
+__device__ __forceinline__ uint32_t raw_floor(double t) {
+  const uint32_t b = __float_as_uint(__double2float_rd(t));
+  if constexpr (DT == 0) return b;
+  uint32_t h = b >> 16;
+  if ((b & 0x80000000u) && (b & 0xFFFFu)) h += 1u;  // negative: round away from 0
+  return h;
+}
+
 }  // namespace qs

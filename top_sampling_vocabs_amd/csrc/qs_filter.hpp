@@ -1,4 +1,6 @@
-// Exact top-k / top-p filter-and-sample kernels for gfx950 (MI355X).
+// Exact top-k / top-p filter-and-sample kernels for gfx950 (MI355X). This
+// file holds the kernel templates; qs_filter_f32.hip and qs_filter_bf16.hip
+// instantiate them per dtype.
 //
 // One 1024-thread workgroup owns one row. Its 16 wave64s each own a
 // contiguous slice of the vocabulary (a multiple of 512 tokens for rows held
@@ -37,22 +39,15 @@
 
 #include <type_traits>
 
+#pragma once
+
 #include "qs_device.hpp"
 #include "qs_launch.hpp"
 #include "qs_stream.hpp"
+#include "qs_bins.hpp"
 #include "../../include/qs.h"
 
 namespace qs {
-
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ s16x2 as_s2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
-__device__ __forceinline__ u16x2 as_u2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
-__device__ __forceinline__ uint32_t bits_of(s16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ uint32_t bits_of(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
-  return (m & a) | (~m & b);
-}
 
 constexpr int kHistBins = kThreads;   // bf16 pool histogram: one key per thread
 
@@ -98,6 +93,7 @@ __device__ __forceinline__ double last_token_q(int my_last_id, double my_last_q,
 }
 
 #include "qs_select.hpp"
+#include "qs_merge.hpp"
 
 // Relative error bound of one hardware exp2 (v_exp_f32), taken as 4 ulp.
 constexpr double kExp2Err = 2.384185791015625e-07;  // 2^-22
@@ -106,55 +102,6 @@ constexpr double kExp2Err = 2.384185791015625e-07;  // 2^-22
 template <int DT>
 __device__ __forceinline__ double weight(uint32_t key, double m, double invT) {
   return exp64(((double)Keys<DT>::value(key) - m) * invT);
-}
-
-// The sigma-truncation threshold as a value (page "Qrita", key design 1 and
-// the lookup table of the training-strategy paragraph): delta = Phi^-1(1 -
-// k/V) for top-k; for top-p the mass-weighted Gaussian N(mu + sigma^2/T,
-// sigma^2), truncated at the sample maximum, gives the value above which a
-// fraction p of the mass lies. t = t0 - 0.2|t0|, never above the sample max.
-// The quantiles are single precision: t only decides how many tokens are
-// compacted, never which tokens are kept. Returns -inf when every finite
-// legal token must be a candidate.
-__device__ __forceinline__ double truncation_value(double n_s, double sum, double sumsq,
-                                                   double ms, double frac_legal, int V,
-                                                   bool greedy, bool topk_on, int k,
-                                                   bool topp_on, double p, double invT) {
-  const double ninf = -__builtin_inf();
-  if (n_s < 1.0) return ninf;
-  if (greedy) return ms;
-  const double mu = sum / n_s;
-  const double var = sumsq / n_s - mu * mu;
-  const double sd = var > 0.0 ? sqrt(var) : 0.0;
-  double t0;
-  if (topk_on) {
-    const double q = (double)k / (frac_legal * (double)V);
-    if (!(q < 1.0)) return ninf;
-    t0 = mu + sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * q)));
-  } else if (topp_on) {
-    if (!(sd > 0.0)) return ninf;
-    const double mp = mu + sd * sd * invT;
-    const double a = (ms - mp) / sd;
-    const double c = (1.0 - p) * 0.5 * (double)erfcf((float)(-a * 0.7071067811865476));
-    if (!(c > 0.0)) return ninf;
-    t0 = mp - sd * (1.4142135623730951 * (double)erfcinvf((float)(2.0 * c)));
-  } else {
-    return ninf;
-  }
-  double t = t0 - 0.2 * fabs(t0);
-  if (!(t < ms)) t = ms;
-  if (!(t > -3.0e38)) return ninf;
-  return t;
-}
-
-// The largest bf16 / fp32 value <= t (t finite), as raw bits.
-template <int DT>
-__device__ __forceinline__ uint32_t raw_floor(double t) {
-  const uint32_t b = __float_as_uint(__double2float_rd(t));
-  if constexpr (DT == 0) return b;
-  uint32_t h = b >> 16;
-  if ((b & 0x80000000u) && (b & 0xFFFFu)) h += 1u;  // negative: round away from 0
-  return h;
 }
 
 // ---------------------------------------------------------------------------
@@ -184,6 +131,17 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
 
   const int r = blockIdx.x;
   const int w = uni((int)threadIdx.x >> 6);  // wave index, kept in a scalar register
+
+  // -- bf16 rows scanned by the chunk kernel: settled from its candidates --------
+  if constexpr (DT == 1) {
+    if (a.ws_segs != nullptr) {
+      const int tid = threadIdx.x;
+      if (merge_row<SAMPLE>(a, r, tid, w, tid & 63, pool_raw, &stage[0][0], hist, binw, red,
+                            info))
+        return;
+      __syncthreads();  // the other paths reuse the LDS
+    }
+  }
 
   // -- bf16 rows held in registers: the value-histogram path ---------------------
   // (rows it cannot settle exactly, and the path switches, take the general
@@ -1664,18 +1622,11 @@ __global__ void __launch_bounds__(kThreads) argmax_rows_kernel(ArgmaxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launchers (host side of this translation unit).
-
-// Slice length of the streamed pass: V split in 16, rounded up to 32 tokens.
-int seg_for(int V) {
-  int s = (V + kWaves - 1) / kWaves;
-  return (s + 31) & ~31;
-}
-
-namespace {
+// Launch of one dtype's instances (each dtype's translation unit includes this
+// file and instantiates its own).
 
 // Steps of 512 tokens per wave slice when the row is held in registers.
-int resident_steps(int V) {
+inline int resident_steps(int V) {
   const int per_wave = (V + kWaves - 1) / kWaves;
   return (per_wave + kStep - 1) / kStep;
 }
@@ -1698,17 +1649,9 @@ hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st) {
-  if (dtype == QS_F32) return sample ? launch_dt<0, true>(a, B, st) : launch_dt<0, false>(a, B, st);
-  return sample ? launch_dt<1, true>(a, B, st) : launch_dt<1, false>(a, B, st);
-}
-
-hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st) {
-  dim3 grid((unsigned)B), block(kThreads);
-  if (dtype == QS_F32) hipLaunchKernelGGL((argmax_rows_kernel<0>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((argmax_rows_kernel<1>), grid, block, 0, st, a);
+template <int DT>
+hipError_t launch_argmax_dt(const ArgmaxArgs& a, int B, hipStream_t st) {
+  hipLaunchKernelGGL((argmax_rows_kernel<DT>), dim3((unsigned)B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

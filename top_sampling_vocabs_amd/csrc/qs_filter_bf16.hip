@@ -1,0 +1,14 @@
+// bf16 instances of the filter/sample and argmax kernels.
+#include "qs_filter.hpp"
+
+namespace qs {
+
+hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream_t st) {
+  return sample ? launch_dt<1, true>(a, B, st) : launch_dt<1, false>(a, B, st);
+}
+
+hipError_t launch_argmax_bf16(const ArgmaxArgs& a, int B, hipStream_t st) {
+  return launch_argmax_dt<1>(a, B, st);
+}
+
+}  // namespace qs

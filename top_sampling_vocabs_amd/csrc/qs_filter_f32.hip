@@ -1,0 +1,26 @@
+// fp32 instances of the filter/sample and argmax kernels, and the launchers
+// that pick a dtype's instances.
+#include "qs_filter.hpp"
+
+namespace qs {
+
+// Slice length of the streamed pass: V split in 16, rounded up to 32 tokens.
+int seg_for(int V) {
+  int s = (V + kWaves - 1) / kWaves;
+  return (s + 31) & ~31;
+}
+
+hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream_t st);
+hipError_t launch_argmax_bf16(const ArgmaxArgs& a, int B, hipStream_t st);
+
+hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st) {
+  if (dtype == QS_F32) return sample ? launch_dt<0, true>(a, B, st) : launch_dt<0, false>(a, B, st);
+  return launch_filter_bf16(a, sample, B, st);
+}
+
+hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st) {
+  if (dtype == QS_F32) return launch_argmax_dt<0>(a, B, st);
+  return launch_argmax_bf16(a, B, st);
+}
+
+}  // namespace qs

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qs_chunk.hpp"
+
 namespace qs {
 
 struct FilterArgs {
@@ -34,6 +36,12 @@ struct FilterArgs {
   // their offsets: moving them changed how the compiler keeps the arguments
   // in scalar registers and cost the filter kernel about 1 us.
   float* logprobs;
+  // the chunked first pass's results in the caller's workspace (bf16 rows),
+  // or null: the filter kernel then reads every row itself
+  const chunk::SegSummary* ws_segs;
+  const chunk::ChunkMass* ws_mass;
+  const uint32_t* ws_cands;
+  int S;                  // chunks per row
 };
 
 struct ArgmaxArgs {

@@ -31,7 +31,7 @@ template <> struct Raw<1> {  // bf16: pairs, element 2p in the low half of r[p]
 
 // 32 zero bytes: what a lane whose chunk is not a full chunk of its slice reads,
 // so that every lane issues the same loads from a valid address.
-__constant__ __align__(16) uint4 kZeroChunk[2] = {};
+static __constant__ __align__(16) uint4 kZeroChunk[2] = {};
 
 template <int DT>
 __device__ __forceinline__ const uint8_t* chunk_ptr(const uint8_t* row, int e) {
