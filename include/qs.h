@@ -185,6 +185,30 @@ QS_API int qs_sample(const void* logits, int dtype, int64_t B, int64_t V,
               float* dense_probs, int32_t* row_status, int32_t* debug_stats,
               uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 
+/* qs_sample without a caller workspace, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same arguments, outputs and
+ * results as qs_sample, minus workspace / workspace_bytes: the scratch of the
+ * chunked pass is a fixed array inside the library, QS_SCRATCH_BYTES per GPU
+ * (held by each GPU the library runs on until the process ends; its address
+ * is taken once per device on the first call there). Calls whose
+ * qs_workspace_bytes(B, V, dtype, cand_cap) exceeds QS_SCRATCH_BYTES return
+ * QS_ERR_WORKSPACE before any HIP call (64 MiB: e.g. 256 rows of up to
+ * 262144 bf16 tokens). Calls on one GPU share its array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and must not be
+ * issued; calls in order on one stream are safe. Nothing is allocated, and
+ * the array needs no clearing between calls. */
+#define QS_SCRATCH_BYTES ((size_t)64 << 20)
+QS_API int qs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V,
+              int64_t row_stride, const float* temperature,
+              const int32_t* top_k, const float* top_p,
+              const uint32_t* bitmask, int64_t bitmask_stride,
+              const uint64_t* seed, uint64_t* offset, const double* uniforms,
+              int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+              float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+              uint32_t flags, void* stream);
+
 /* Greedy selection: tokens[r] = lowest token id holding the largest finite
  * legal logit. No softmax and no random number (page "第 9 讲 · 生成与推测解码",
  * section 1: argmax needs no normalisation; exercise 1: ties by vocabulary

@@ -215,3 +215,36 @@ def test_top_logprobs_rejects_bad_arguments(lib):
                dict(tlp=None), dict(status=None)):
         assert tp(**kw) == _lib.QS_ERR_INVALID_ARG, kw
     assert tp(B=0) == _lib.QS_OK
+
+
+def test_sample_noalloc_rejects_before_any_hip_call(lib):
+    """qs_sample_noalloc: argument errors first, then QS_ERR_WORKSPACE when the
+    call's workspace would exceed the library's fixed scratch; both before any
+    HIP call (no GPU here). B = 0 is a no-op."""
+    assert _lib.SCRATCH_BYTES == 64 << 20
+
+    def na(**kw):
+        args = dict(logits=A16, dtype=1, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
+                    bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16, lp=None,
+                    keep=None, cids=None, cprobs=None, ccount=None, cap=0, dense=None,
+                    status=A16, dbg=None, flags=0, stream=None)
+        args.update(kw)
+        return lib.qs_sample_noalloc(
+            args["logits"], args["dtype"], args["B"], args["V"], args["stride"], args["T"],
+            args["k"], args["p"], args["bitmask"], args["bms"], args["seed"], args["offset"],
+            args["uni"], args["tokens"], args["lp"], args["keep"], args["cids"],
+            args["cprobs"], args["ccount"], args["cap"], args["dense"], args["status"],
+            args["dbg"], args["flags"], args["stream"])
+    assert na(stride=60) == _lib.QS_ERR_INVALID_ARG
+    assert na(V=-5) == _lib.QS_ERR_INVALID_ARG
+    assert na(B=0) == _lib.QS_OK
+    # the largest batch of 151936-token bf16 rows the scratch holds, and one more
+    V = 151936
+    per_row = lib.qs_workspace_bytes(1024, V, 1, 0) / 1024
+    fit = int(_lib.SCRATCH_BYTES // per_row)
+    while lib.qs_workspace_bytes(fit, V, 1, 0) > _lib.SCRATCH_BYTES:
+        fit -= 1
+    while lib.qs_workspace_bytes(fit + 1, V, 1, 0) <= _lib.SCRATCH_BYTES:
+        fit += 1
+    assert fit >= 256
+    assert na(B=fit + 1, V=V, stride=V) == _lib.QS_ERR_WORKSPACE

@@ -34,7 +34,11 @@ FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
 
-EXPORTS = ("qs_workspace_bytes", "qs_filter_mask", "qs_sample", "qs_argmax", "qs_spec_verify",
+# size of the fixed per-GPU scratch behind qs_sample_noalloc (QS_SCRATCH_BYTES)
+SCRATCH_BYTES = 64 << 20
+
+EXPORTS = ("qs_workspace_bytes", "qs_filter_mask", "qs_sample", "qs_sample_noalloc", "qs_argmax",
+           "qs_spec_verify",
            "qs_apply_penalties", "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
 
 _lib = None
@@ -74,6 +78,8 @@ def load(path=LIB_PATH):
         _p, _p, _p, _p, _i64,
         _p, _p, _p, _u32,
         _p, _sz, _p]
+    lib.qs_sample_noalloc.restype = _i32
+    lib.qs_sample_noalloc.argtypes = lib.qs_sample.argtypes[:-3] + [_p]
     lib.qs_argmax.restype = _i32
     lib.qs_argmax.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
     lib.qs_spec_verify.restype = _i32
@@ -226,6 +232,22 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
     was drawn from (float32 [B]). Returns a dict with tokens [B], status [B]
     and the optional outputs of filter_mask. workspace as for filter_mask.
     """
+    return _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms,
+                   keep_mask, cand_cap, dense, debug, logprobs, flags, workspace, False)
+
+
+def sample_noalloc(logits, temperature, top_k, top_p, bitmask=None, *, seed=None,
+                   offset=None, uniforms=None, keep_mask=False, cand_cap=0, dense=False,
+                   debug=False, logprobs=False, flags=0):
+    """sample() through qs_sample_noalloc: the library's fixed per-GPU scratch
+    instead of a workspace (the outputs are still allocated here). Calls on
+    one GPU must not overlap in time."""
+    return _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms,
+                   keep_mask, cand_cap, dense, debug, logprobs, flags, None, True)
+
+
+def _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms, keep_mask,
+            cand_cap, dense, debug, logprobs, flags, workspace, noalloc):
     import torch
     lib = load()
     B, V = _check_logits(logits, bitmask)
@@ -253,16 +275,21 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
         out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
     if debug:
         out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
-    ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
-    rc = lib.qs_sample(
+    args = (
         _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
         _ptr(temperature), _ptr(top_k), _ptr(top_p),
         _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
         _ptr(seed) if uniforms is None else None,
         _ptr(offset) if uniforms is None else None, _ptr(uniforms), _ptr(out["tokens"]),
-        _ptr(out.get("logprobs")), _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
-        _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
-        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), ws_p, ws_n, _stream(dev))
+        _ptr(out.get("logprobs")), _ptr(out.get("keep_mask")), _ptr(out.get("cand_ids")),
+        _ptr(out.get("cand_probs")), _ptr(out.get("cand_count")), int(cand_cap),
+        _ptr(out.get("dense")), _ptr(out["status"]), _ptr(out.get("debug")), int(flags))
+    if noalloc:
+        rc = lib.qs_sample_noalloc(*args, _stream(dev))
+        _status(rc, "qs_sample_noalloc")
+        return out
+    ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
+    rc = lib.qs_sample(*args, ws_p, ws_n, _stream(dev))
     _status(rc, "qs_sample")
     return out
 

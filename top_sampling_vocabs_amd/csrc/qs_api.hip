@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/qs.h"
 
 #include "qs_aux.hpp"
@@ -136,6 +138,27 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   return e == hipSuccess ? QS_OK : QS_ERR_HIP;
 }
 
+// The chunked pass's scratch for qs_sample_noalloc, one copy per GPU. In
+// host code `scratch` names a host-side stand-in: kernels and copies get the
+// device address from hipGetSymbolAddress (taken once per device, with that
+// device current), never the array's name.
+static __device__ __align__(256) uint8_t scratch[QS_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of this device's `scratch` (nullptr on a HIP error).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +193,27 @@ int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_s
                        bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
                        keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
                        debug_stats, flags, workspace, workspace_bytes, stream);
+}
+
+int qs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const float* temperature, const int32_t* top_k, const float* top_p,
+                      const uint32_t* bitmask, int64_t bitmask_stride, const uint64_t* seed,
+                      uint64_t* offset, const double* uniforms, int32_t* tokens,
+                      float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+                      float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+                      float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+                      uint32_t flags, void* stream) {
+  // the size check first, as qs_sample's (before any HIP call)
+  int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
+  if (rc != QS_OK) return rc;
+  if (B == 0) return QS_OK;
+  if (ws_bytes(B, V, dtype) > QS_SCRATCH_BYTES) return QS_ERR_WORKSPACE;
+  void* const ws = scratch_address();
+  if (ws == nullptr) return QS_ERR_HIP;
+  return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
+                       keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs,
+                       row_status, debug_stats, flags, ws, QS_SCRATCH_BYTES, stream);
 }
 
 int qs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
