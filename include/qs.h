@@ -101,10 +101,13 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
  * candidate set that the pivot searches then work on; its closing section
  * names full-vocabulary temporaries as a cost, so the buffer is capped:
  * at most 896 entries of every 4096-token segment of a row, plus 32 bytes
- * per segment and 32 per 16384-token chunk). For bf16 rows of up to 2^20
- * tokens, with S = ceil(V / 16384) chunks a row, it is
+ * per segment and 32 per 16384-token chunk). Only bf16 rows longer than
+ * the per-row kernel holds in registers (V > 155648) and of at most 2^20
+ * tokens take that chunked pass; with S = ceil(V / 16384) chunks a row, they
+ * need
  *   align256(B * 4S * 32) + align256(B * S * 32) + B * 4S * 896 * 4 bytes;
- * other calls need none. cand_cap does not change it (the caller's candidate
+ * other calls (fp32, bf16 rows of up to 155648 tokens, longer than 2^20)
+ * need none. cand_cap does not change it (the caller's candidate
  * lists are outputs, not scratch). Pure function of its arguments; 0 for
  * invalid ones.
  *

@@ -106,19 +106,22 @@ def test_sample_rejects_bad_arguments(lib, kw):
 
 
 def test_workspace_bytes(lib):
-    """bf16 calls need per 4096-token segment of a row 32 bytes and 896
-    candidate entries of 4 bytes, plus 32 bytes per 16384-token chunk (each part
-    rounded up to 256 bytes);
-    fp32 calls and invalid arguments need none; cand_cap does not matter."""
+    """bf16 rows longer than the per-row kernel's register tiers (155648
+    tokens) need per 4096-token segment of a row 32 bytes and 896 candidate
+    entries of 4 bytes, plus 32 bytes per 16384-token chunk (each part
+    rounded up to 256 bytes); shorter bf16 rows, fp32 calls and invalid
+    arguments need none; cand_cap does not matter."""
     def want(B, V):
         S = -(-V // 16384)
         a256 = lambda x: -(-x // 256) * 256  # noqa: E731
         return a256(B * 4 * S * 32) + a256(B * S * 32) + B * 4 * S * 896 * 4
-    for B, V in ((4, 64), (256, 151936), (512, 151936), (3, 16384), (1, 16385),
+    for B, V in ((4, 155649), (256, 262144), (512, 200000), (3, 163840), (1, 524289),
                  (2, 64 * 16384)):
         assert lib.qs_workspace_bytes(B, V, 1, 0) == want(B, V), (B, V)
         assert lib.qs_workspace_bytes(B, V, 1, 12345) == want(B, V)
         assert lib.qs_workspace_bytes(B, V, 0, 0) == 0
+    for B, V in ((4, 64), (256, 151936), (512, 155648), (3, 16384)):
+        assert lib.qs_workspace_bytes(B, V, 1, 0) == 0, (B, V)
     assert lib.qs_workspace_bytes(0, 100, 1, 0) == 0
     assert lib.qs_workspace_bytes(4, 0, 1, 0) == 0
     assert lib.qs_workspace_bytes(-1, 100, 1, 0) == 0
@@ -130,9 +133,11 @@ def test_workspace_bytes(lib):
 def test_workspace_rejected_before_any_hip_call(lib, call):
     """A missing, misaligned or short workspace is QS_ERR_WORKSPACE; argument
     errors are still reported first; fp32 calls need no workspace."""
-    f = (lambda **kw: filt(lib, dtype=1, stride=64, **kw)) if call == "filter" else \
-        (lambda **kw: smp(lib, **kw))
-    need = lib.qs_workspace_bytes(4, 64, 1, 0)
+    V = 200000   # bf16 rows past the register tiers: the chunked pass
+    f = (lambda **kw: filt(lib, dtype=1, V=V, stride=V, **kw)) if call == "filter" else \
+        (lambda **kw: smp(lib, V=V, stride=V, **kw))
+    need = lib.qs_workspace_bytes(4, V, 1, 0)
+    assert need > 0
     assert f(ws=None, wsn=0) == _lib.QS_ERR_WORKSPACE
     assert f(ws=None, wsn=need) == _lib.QS_ERR_WORKSPACE
     assert f(ws=ctypes.c_void_p(0x400010), wsn=need) == _lib.QS_ERR_WORKSPACE
@@ -238,8 +243,9 @@ def test_sample_noalloc_rejects_before_any_hip_call(lib):
     assert na(stride=60) == _lib.QS_ERR_INVALID_ARG
     assert na(V=-5) == _lib.QS_ERR_INVALID_ARG
     assert na(B=0) == _lib.QS_OK
-    # the largest batch of 151936-token bf16 rows the scratch holds, and one more
-    V = 151936
+    # the largest batch of 262144-token bf16 rows (the chunked pass) the
+    # scratch holds, and one more
+    V = 262144
     per_row = lib.qs_workspace_bytes(1024, V, 1, 0) / 1024
     fit = int(_lib.SCRATCH_BYTES // per_row)
     while lib.qs_workspace_bytes(fit, V, 1, 0) > _lib.SCRATCH_BYTES:

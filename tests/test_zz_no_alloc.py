@@ -53,14 +53,15 @@ def _both(qs, w, cand_cap):
 
 
 def test_noalloc_matches_workspace_call_twice(qs):
-    # the 256-row, 151936-token bf16 batch (thirds top-k / top-p / both, 30 %
-    # legal bitmask), then a smaller batch of the same kinds: the second call
-    # reuses the scratch the first one left behind
-    big = workloads.make(3)
+    # 128 rows of 262144 bf16 tokens (the chunked pass, whose workspace the
+    # scratch replaces; thirds top-k / top-p / both, 30 % legal bitmask), then
+    # a smaller batch of the same kinds: the second call reuses the scratch
+    # the first one left behind
+    big = workloads.make(3, B=128, V=262144)
     print(f"noalloc call 1: B={big.B} V={big.V} {big.dtype}", flush=True)
     ref = _both(qs, big, 8192)
-    assert (ref["debug"].cpu().numpy()[:, 0] == 2).mean() > 0.95   # the chunked path ran
-    small = workloads.make(3, B=37, V=50000, seed=workloads.BASE_SEED + 77)
+    assert (ref["debug"].cpu().numpy()[:, 0] == 2).mean() > 0.3   # the chunked path ran
+    small = workloads.make(3, B=37, V=200000, seed=workloads.BASE_SEED + 77)
     print(f"noalloc call 2: B={small.B} V={small.V} {small.dtype}", flush=True)
     _both(qs, small, 4096)
 

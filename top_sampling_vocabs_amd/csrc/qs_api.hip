@@ -1,7 +1,8 @@
 // C-ABI entry points: argument validation (before any HIP call), launch
 // geometry, and error mapping. Every entry point enqueues its kernels on the
-// caller's stream (one launch; two for bf16 filter calls: the chunk pass and
-// the per-row filter) and returns without synchronising.
+// caller's stream (one launch; two for filter calls on bf16 rows longer than
+// the per-row kernel holds in registers: the chunk pass and the per-row
+// filter) and returns without synchronising.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,10 +22,16 @@ constexpr int64_t kMaxB = ((int64_t)1 << 31) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Workspace of the chunked first pass: bf16 rows of up to kMaxChunks chunks.
+// Workspace of the chunked first pass, which takes bf16 rows longer than the
+// per-row kernel holds in registers (those stream there, one workgroup per
+// row) and of at most kMaxChunks chunks. Rows held in registers fill the GPU
+// with one workgroup each and need no workspace.
+bool chunked_rows(int64_t V, int dtype) {
+  return dtype == QS_BF16 && !qs::filter_row_resident(QS_BF16, (int)V) &&
+         qs::chunk::chunks_for(V) <= qs::chunk::kMaxChunks;
+}
 size_t ws_bytes(int64_t B, int64_t V, int dtype) {
-  if (dtype != QS_BF16 || B == 0) return 0;
-  if (qs::chunk::chunks_for(V) > qs::chunk::kMaxChunks) return 0;
+  if (B == 0 || !chunked_rows(V, dtype)) return 0;
   return qs::chunk::workspace_bytes(B, V);
 }
 
@@ -109,8 +116,9 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.S = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (need > 0 && flags == 0u) {
-    // bf16: the chunk kernel streams every row first, the filter kernel then
-    // settles each row from the chunks' candidates (path switches skip it)
+    // long bf16 rows: the chunk kernel streams every row first, the filter
+    // kernel then settles each row from the chunks' candidates (path switches
+    // skip it)
     qs::chunk::Args ca;
     ca.logits = a.logits;
     ca.row_bytes = a.row_bytes;

@@ -7,6 +7,10 @@ hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream
   return sample ? launch_dt<1, true>(a, B, st) : launch_dt<1, false>(a, B, st);
 }
 
+bool filter_row_resident(int dtype, int V) {
+  return resident_steps(V) <= kResidentTier[dtype == 1 ? 1 : 0][1];
+}
+
 hipError_t launch_argmax_bf16(const ArgmaxArgs& a, int B, hipStream_t st) {
   return launch_argmax_dt<1>(a, B, st);
 }

@@ -57,6 +57,9 @@ struct ArgmaxArgs {
 
 int seg_for(int V);
 hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st);
+// Whether the per-row filter kernel holds a row of V tokens of this dtype in
+// registers (its resident tiers); longer rows stream.
+bool filter_row_resident(int dtype, int V);
 hipError_t launch_argmax(const ArgmaxArgs& a, int dtype, int B, hipStream_t st);
 
 }  // namespace qs

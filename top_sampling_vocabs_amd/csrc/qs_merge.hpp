@@ -259,7 +259,8 @@ __device__ __forceinline__ bool merge_row(const FilterArgs& a, int r, int tid, i
     return false;
   if (!topk_on && !topp_on) return false;              // every token kept
   if (topk_on && N < (uint32_t)kk) return false;       // the k-th value lies below t
-  if (mask_row && W > mrg::kMaskWords) return false;
+  // masks wider than the LDS stage: cleared in memory here, bits set there
+  const bool mask_direct = mask_row && W > mrg::kMaskWords;
   if (V > (int)mrg::kIdMask) return false;
   const int32_t tS = mrg::skey1(thr);
   double m_bg = 0.0, m_bg_err = 0.0;
@@ -269,8 +270,12 @@ __device__ __forceinline__ bool merge_row(const FilterArgs& a, int r, int tid, i
     m_bg_err = uni(info.sc_d[1]);
     if (uni(info.sc_u[0]) != 0u) return false;        // a background mass that is not exact
   }
-  if (dense_row) {  // zero in memory first (the scatter below lands after these stores)
-    for (int i = tid; i < V; i += kThreads) dense_row[i] = 0.0f;
+  if (dense_row || mask_direct) {
+    // zero in memory first (the scatter below lands after these stores)
+    if (dense_row)
+      for (int i = tid; i < V; i += kThreads) dense_row[i] = 0.0f;
+    if (mask_direct)
+      for (int i = tid; i < W; i += kThreads) mask_row[i] = 0u;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -591,7 +596,10 @@ __device__ __forceinline__ bool merge_row(const FilterArgs& a, int r, int tid, i
           if (probs_row) __builtin_nontemporal_store(qf, probs_row + pos);
         }
         if (dense_row) dense_row[id] = qf;
-        if (mask_row)
+        if (mask_direct)
+          __hip_atomic_fetch_or(mask_row + (id >> 5), 1u << (id & 31u), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        else if (mask_row)
           __hip_atomic_fetch_or(mstage + (id >> 5), 1u << (id & 31u), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         if (qq > 0.0) last_e = e[q];
@@ -622,7 +630,7 @@ __device__ __forceinline__ bool merge_row(const FilterArgs& a, int r, int tid, i
     }
   }
   __syncthreads();  // the staged mask words
-  if (mask_row)
+  if (mask_row && !mask_direct)
     for (int i = tid; i < W; i += kThreads) __builtin_nontemporal_store(mstage[i], mask_row + i);
   // the token: from wave sw; if rounding left u at or above wave sw's last
   // cumulative sum, that wave's last kept id with q > 0; if u lies past every
