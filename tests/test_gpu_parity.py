@@ -424,8 +424,19 @@ def test_topp_background_extremes(qs):
     assert st[5] == oracle.ROW_NONFINITE
     dbg = out["debug"].cpu().numpy()
     # candidate keys spanning more than the 1024-key histogram: some rows are
-    # settled by pivot rounds on the pool (more rounds than the two scans)
-    assert (dbg[:, 1] >= 3).any(), dbg.tolist()
+    # settled by the radix select on the pool (two 8-bit levels of the bf16
+    # key per search), and the pivot rounds the ablation switches keep
+    # settle the same rows identically
+    assert (dbg[:, 1] >= 2).any(), dbg.tolist()
+    d = to_device(w)
+    pv = qs.filter_mask(d["logits"], d["T"], d["k"], d["p"], d["bitmask"], cand_cap=w.V,
+                        debug=True, flags=qs.FLAG_PIVOT_SEARCH)
+    fm = qs.filter_mask(d["logits"], d["T"], d["k"], d["p"], d["bitmask"], cand_cap=w.V,
+                        debug=True)
+    import torch
+    torch.cuda.synchronize()
+    assert np.array_equal(words_u32(pv["keep_mask"]), words_u32(fm["keep_mask"]))
+    assert (pv["debug"].cpu().numpy()[:, 1] >= 3).any()
 
 
 @pytest.mark.gpu

@@ -121,6 +121,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint4 lut[DT == 1 ? 256 : 1];
   __shared__ uint32_t hist[kHB];
   __shared__ double binw[kHB];
+  // fp32 rows: the radix select's bins (bf16 rows use hist and binw)
+  __shared__ uint32_t rb_c_f32[DT == 0 ? 256 : 1];
+  __shared__ double rb_m_f32[DT == 0 ? 256 : 1];
   // the background histogram plus one dump bin per lane (excluded tokens)
   __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
@@ -1104,8 +1107,136 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // pivot runs); the stop tests are unchanged, only the round count grows
   const bool binary_pivot = (a.flags & QS_FLAG_BINARY_PIVOT) != 0u;
 
+  // Radix select (flags 0; sources other than the bf16 pool histogram, which
+  // the scans above settle): the key digits from the top, 8 bits a level, so
+  // a search walks its items (pool or row) once per level (2 for bf16 keys, 4
+  // for fp32) rather than once per pivot round. Bins of counts and fp64
+  // masses for one level are shared by the waves (LDS atomics; the masses
+  // only place the boundary, the outputs' probabilities come from the walks
+  // below); wave 0 scans them from the top digit down, 4 bins a lane.
+  // Switched runs keep the page's pivot rounds.
+  const bool radix = a.flags == 0u && !use_hist;
+  constexpr int kKeyBits = DT == 1 ? 16 : 32;
+  uint32_t* const rb_c = DT == 1 ? hist : rb_c_f32;
+  double* const rb_m = DT == 1 ? binw : rb_m_f32;
+  // One level: bins of the digit at `shift` of the source keys that share
+  // the digits above it with `prefix` (and, with masses, lie above `excl`),
+  // plus an extra bucket of xcnt tokens of key xkey (the top-k boundary
+  // tokens inside the top-k set). Returns, through info, the digit b whose
+  // bin holds the `need`-th largest key (counts) or where the descending mass
+  // from `above` reaches `target` (masses), with the count or mass of the
+  // bins above b and b's own count.
+  auto radix_level = [&](int shift, uint32_t prefix, bool masses, uint32_t excl, double above,
+                         uint32_t need, double target, uint32_t xkey, uint32_t xcnt,
+                         double xmass) {
+    if (tid < 256) {
+      rb_c[tid] = 0u;
+      rb_m[tid] = 0.0;
+    }
+    __syncthreads();
+    const uint32_t hmask = shift + 8 >= 32 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const uint32_t hpre = prefix & hmask;
+    for_items([&](uint32_t x, uint32_t c) {
+      if ((x & hmask) == hpre && (!masses || x > excl)) {
+        const uint32_t b = (x >> shift) & 255u;
+        __hip_atomic_fetch_add(rb_c + b, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (masses)
+          __hip_atomic_fetch_add(rb_m + b, (double)c * wkey(x), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    });
+    if (tid == 0 && xcnt && (xkey & hmask) == hpre) {
+      const uint32_t b = (xkey >> shift) & 255u;
+      __hip_atomic_fetch_add(rb_c + b, xcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (masses)
+        __hip_atomic_fetch_add(rb_m + b, xmass, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l: bins 255 - 4l .. 252 - 4l, descending
+      uint32_t c4[4];
+      double m4[4];
+      uint32_t cl = 0u;
+      double ml = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 255 - 4 * lane - q;
+        c4[q] = rb_c[b];
+        m4[q] = masses ? rb_m[b] : 0.0;
+        cl += c4[q];
+        ml += m4[q];
+      }
+      int b_hit = -1;
+      uint32_t c_above = 0u, c_hit = 0u;
+      double m_above = 0.0;
+      if (!masses) {
+        const uint32_t incl = scan_incl_u32(cl);
+        uint32_t run = incl - cl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (b_hit < 0 && run < need && need <= run + c4[q]) {
+            b_hit = 255 - 4 * lane - q;
+            c_above = run;
+            c_hit = c4[q];
+          }
+          run += c4[q];
+        }
+      } else {
+        const double incl = scan_incl_f64(ml);
+        double run = above + incl_shift1_f64(incl);
+        int b_last = -1;
+        double m_last = 0.0;
+        uint32_t c_last = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (c4[q]) {
+            if (b_hit < 0 && run < target && run + m4[q] >= target) {
+              b_hit = 255 - 4 * lane - q;
+              m_above = run;
+              c_hit = c4[q];
+            }
+            if (b_hit < 0) {
+              b_last = 255 - 4 * lane - q;
+              m_last = run;
+              c_last = c4[q];
+            }
+          }
+          run += m4[q];
+        }
+        if (ballot(b_hit >= 0) == 0u) {
+          // rounding left the target above every prefix: the lowest weighted bin
+          const uint64_t anyb = ballot(b_last >= 0);
+          const int L = anyb ? 63 - __clzll((long long)anyb) : -1;
+          if (L >= 0 && lane == L) { b_hit = b_last; m_above = m_last; c_hit = c_last; }
+        }
+      }
+      const uint64_t f = ballot(b_hit >= 0);
+      const int L = f ? __ffsll((unsigned long long)f) - 1 : -1;
+      if (lane == (L < 0 ? 0 : L)) {
+        info.sc_u[0] = L < 0 ? 0xFFFFFFFFu : (uint32_t)b_hit;
+        info.sc_u[1] = c_above;
+        info.sc_u[2] = c_hit;
+        info.sc_d[0] = m_above;
+      }
+    }
+    __syncthreads();
+  };
+
   // -- the k-th largest key (top-k) ----------------------------------------------
-  if (topk_eff && !settled) {
+  if (topk_eff && !settled && radix) {
+    uint32_t prefix = 0u, need = (uint32_t)kk;
+    for (int shift = kKeyBits - 8; shift >= 0 && !failed; shift -= 8) {
+      radix_level(shift, prefix, false, 0u, 0.0, need, 0.0, 0u, 0u, 0.0);
+      const uint32_t b = uni(info.sc_u[0]);
+      if (b == 0xFFFFFFFFu) { failed = true; break; }  // (never: k <= the finite count)
+      need -= uni(info.sc_u[1]);
+      prefix |= b << shift;
+      ++rounds;
+      __syncthreads();  // info is rewritten by the next level
+    }
+    kap = prefix;
+    n_keep_k = need;
+  } else if (topk_eff && !settled) {
     // quaternary three-pivot search on counts (page "Qrita", key design 2)
     uint32_t lo = src_lo - 1u, hi = maxk;
     bool found = false;
@@ -1200,7 +1331,43 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         uint32_t lo = (topk_eff ? kap : src_lo) - 1u, hi = maxk;
         const uint32_t excl = topk_eff ? kap : 0u;  // per-item terms only for key > excl
         bool found = false, refine = false;
-        while (!found) {
+        if (radix) {
+          // digits from the top; the top-k boundary key counts n_keep_k tokens
+          uint32_t prefix = 0u, c_star = 0u;
+          double above = 0.0;
+          for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
+            radix_level(shift, prefix, true, excl, above, 0u, target, kap,
+                        topk_eff ? n_keep_k : 0u, topk_eff ? (double)n_keep_k * w_kap : 0.0);
+            const uint32_t b = uni(info.sc_u[0]);
+            const double m_ab = uni(info.sc_d[0]);
+            c_star = uni(info.sc_u[2]);   // at the last level: the tokens of the key itself
+            __syncthreads();  // info is rewritten by the next level
+            ++rounds;
+            if (b == 0xFFFFFFFFu) { failed = true; break; }  // (never: the top key has weight 1)
+            above = m_ab;
+            prefix |= b << shift;
+          }
+          if (!failed) {
+            // the boundary key, its count and weight, and the smallest count of
+            // its tokens that reaches the target
+            pstar = prefix;
+            const double wz = wkey(pstar);
+            const uint32_t c = c_star;   // (n_keep_k when pstar is the top-k boundary)
+            const double below = above;
+            w_star = wz;
+            const double need = (target - below) / wz;
+            uint32_t nk = need <= 1.0 ? 1u : (need >= (double)c ? c : (uint32_t)ceil(need));
+            while (nk > 1u && below + (double)(nk - 1u) * wz >= target) --nk;
+            while (nk < c && below + (double)nk * wz < target) ++nk;
+            n_keep = nk;
+            const double w_p = below + (double)nk * wz;
+            const double lo_t = p * (w_k - err), hi_t = p * (w_k + err);
+            const double prev = below + (double)(nk - 1u) * wz;
+            refine = err > 0.0 && !(prev < lo_t && hi_t <= w_p);
+            found = true;
+          }
+        }
+        while (!found && !failed) {
           if (rounds >= 96) { failed = true; break; }
           const uint32_t d = hi - lo;
           uint32_t tau[3];
