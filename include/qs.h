@@ -134,7 +134,8 @@ QS_API size_t qs_workspace_bytes(int64_t B, int64_t V, int dtype, int64_t cand_c
  *              (0 outside P)
  * row_status   [B] int32 out, required (qs_row_status)
  * debug_stats  [B][4] int32 out, optional: {path (0 candidate pool, 1 full
- *              row, 2 candidates of the chunked first pass), search rounds,
+ *              row, 2 candidates of the chunked first pass, 3 full row for
+ *              the top-k search, then its top-k set), search rounds,
  *              |Z_t| (candidates above the truncation threshold), |P|}; bf16
  *              rows settled by a value histogram report 0 rounds (path 0 with
  *              |Z_t| = the tokens at or above the final boundary value when

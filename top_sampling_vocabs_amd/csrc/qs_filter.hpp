@@ -121,9 +121,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint4 lut[DT == 1 ? 256 : 1];
   __shared__ uint32_t hist[kHB];
   __shared__ double binw[kHB];
-  // fp32 rows: the radix select's bins (bf16 rows use hist and binw)
-  __shared__ uint32_t rb_c_f32[DT == 0 ? 256 : 1];
-  __shared__ double rb_m_f32[DT == 0 ? 256 : 1];
+  // fp32 rows: the radix select's bins, 32 KB (bf16 rows use hist and binw)
+  __shared__ __align__(16) uint32_t rb_f32[DT == 0 ? 8192 : 4];
   // the background histogram plus one dump bin per lane (excluded tokens)
   __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
@@ -653,7 +652,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
 
   const PKey* pk = my_pk;
   const uint16_t* pid = my_pid;
-  const int my_cnt = (int)min(my_wcnt, kCap);
+  int my_cnt = (int)min(my_wcnt, kCap);
   // pool usable: complete, 16-bit ids fit, not forced off
   const bool pool_ok = !overflow && ccount_all > 0u && !(a.flags & QS_FLAG_FORCE_MISS) &&
                        !no_trunc && a.seg <= 65536;
@@ -1065,7 +1064,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
   const bool topk_eff = !greedy && kk > 0 && (uint32_t)kk < (use_pool ? ccount : nfin);
   const bool use_hist = hist_t && use_pool;
-  const uint32_t src_lo = use_pool ? tkey : K::kNegInf + 1u;  // every source key >= src_lo
+  uint32_t src_lo = use_pool ? tkey : K::kNegInf + 1u;  // every source key >= src_lo
 
   // items of the pivot searches: (key, multiplicity) from the histogram, else tokens
   auto for_items = [&](auto&& f) {
@@ -1108,63 +1107,119 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const bool binary_pivot = (a.flags & QS_FLAG_BINARY_PIVOT) != 0u;
 
   // Radix select (flags 0; sources other than the bf16 pool histogram, which
-  // the scans above settle): the key digits from the top, 8 bits a level, so
-  // a search walks its items (pool or row) once per level (2 for bf16 keys, 4
-  // for fp32) rather than once per pivot round. Bins of counts and fp64
-  // masses for one level are shared by the waves (LDS atomics; the masses
-  // only place the boundary, the outputs' probabilities come from the walks
-  // below); wave 0 scans them from the top digit down, 4 bins a lane.
-  // Switched runs keep the page's pivot rounds.
-  const bool radix = a.flags == 0u && !use_hist;
+  // the scans above settle): the key digits from the top, so that a search
+  // walks its items (pool or row) once per level: fp32 keys in three levels
+  // (11, 11 and 10 bits, 2048 bins), bf16 keys in two (8 bits, 256 bins),
+  // rather than once per pivot round. Bins of counts and fp64 masses for one
+  // level are shared by the waves (LDS atomics; the masses only place the
+  // boundary, the outputs' probabilities come from the walks below); wave 0
+  // scans them from the top digit down. Switched runs keep the page's pivot
+  // rounds.
   constexpr int kKeyBits = DT == 1 ? 16 : 32;
-  uint32_t* const rb_c = DT == 1 ? hist : rb_c_f32;
-  double* const rb_m = DT == 1 ? binw : rb_m_f32;
-  // One level: bins of the digit at `shift` of the source keys that share
-  // the digits above it with `prefix` (and, with masses, lie above `excl`),
-  // plus an extra bucket of xcnt tokens of key xkey (the top-k boundary
-  // tokens inside the top-k set). Returns, through info, the digit b whose
-  // bin holds the `need`-th largest key (counts) or where the descending mass
-  // from `above` reaches `target` (masses), with the count or mass of the
-  // bins above b and b's own count.
-  auto radix_level = [&](int shift, uint32_t prefix, bool masses, uint32_t excl, double above,
-                         uint32_t need, double target, uint32_t xkey, uint32_t xcnt,
-                         double xmass) {
-    if (tid < 256) {
-      rb_c[tid] = 0u;
-      rb_m[tid] = 0.0;
+  const bool radix = a.flags == 0u && !use_hist;
+  bool to_pool = false;  // a full-row source replaced by a key range of it in the pools
+  constexpr int kRBins = DT == 1 ? 256 : 2048;
+  // digits of a search: 8 bits a level over pools and samples (few items, 256
+  // bins), 11 + 11 + 10 over fp32 rows (every token walked once per level)
+  auto n_levels = [](bool wide) { return DT == 1 ? 2 : (wide ? 3 : 4); };
+  auto lvl_shift = [](bool wide, int l) {
+    return (DT == 1 || !wide) ? kKeyBits - 8 - 8 * l : (l == 0 ? 21 : (l == 1 ? 10 : 0));
+  };
+  auto lvl_width = [](bool wide, int l) { return (DT == 1 || !wide) ? 8 : (l == 2 ? 10 : 11); };
+  // counts: 4 interleaved copies (entry 4 b + lane % 4) on levels without
+  // masses, so that the lanes of one wave that hit one bin spread over 4 LDS
+  // banks; one copy next to the masses otherwise
+  uint32_t* const rb_c = DT == 1 ? hist : rb_f32;
+  double* const rb_m = DT == 1 ? binw : reinterpret_cast<double*>(rb_f32 + kRBins);
+  static_assert(DT == 1 || kRBins + 2 * kRBins <= 8192, "fp32 radix masses");
+  static_assert(DT == 1 || 4 * kRBins <= 8192, "fp32 radix bins");
+  static_assert(DT == 0 || 4 * kRBins <= kHistBins, "bf16 radix bins");
+  // One level: bins of the digit at `shift` (`width` bits) of the source keys
+  // that share the digits above it with `prefix` (and, with masses, lie above
+  // `excl`), plus an extra bucket of xcnt tokens of key xkey (the top-k
+  // boundary tokens inside the top-k set). Returns, through info, the digit b
+  // whose bin holds the `need`-th largest key (counts) or where the
+  // descending mass from `above` reaches `target` (masses), with the count or
+  // mass of the bins above b and b's own count.
+  // The bins are clear when a level starts: radix_begin clears them before a
+  // search, and wave 0 clears them again once it has scanned a level. The
+  // results alternate between two slots of info, so that a level's result is
+  // read while the next level's is being written without another barrier.
+  int rpar = 0;
+  auto radix_begin = [&]() {
+    for (int i = tid; i < kRBins; i += kThreads) {
+      reinterpret_cast<uint4*>(rb_c)[i] = make_uint4(0u, 0u, 0u, 0u);
+      rb_m[i] = 0.0;
     }
     __syncthreads();
-    const uint32_t hmask = shift + 8 >= 32 ? 0u : (0xFFFFFFFFu << (shift + 8));
+  };
+  struct RLevel {
+    uint32_t b, c_above, c_hit;
+    double m_above;
+  };
+  auto radix_level = [&](auto&& items, int shift, int width, uint32_t prefix, bool masses,
+                         uint32_t excl, double above, uint32_t need, double target,
+                         uint32_t xkey, uint32_t xcnt, double xmass) -> RLevel {
+    const int nb = width > 8 ? kRBins : 256;  // bins of this level (a multiple of 64)
+    const int bpl = nb / 64;                  // bins per lane of the scan
+    const int slot = rpar;
+    rpar ^= 1;
+    const uint32_t hmask = shift + width >= 32 ? 0u : (0xFFFFFFFFu << (shift + width));
+    const uint32_t dmask = (1u << width) - 1u;
     const uint32_t hpre = prefix & hmask;
-    for_items([&](uint32_t x, uint32_t c) {
+    // masses: consecutive items of one bin are summed in the lane first, one
+    // pair of atomics per run of the same bin
+    uint32_t run_b = 0xFFFFFFFFu, run_c = 0u;
+    double run_m = 0.0;
+    items([&](uint32_t x, uint32_t c) {
       if ((x & hmask) == hpre && (!masses || x > excl)) {
-        const uint32_t b = (x >> shift) & 255u;
-        __hip_atomic_fetch_add(rb_c + b, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (masses)
-          __hip_atomic_fetch_add(rb_m + b, (double)c * wkey(x), __ATOMIC_RELAXED,
+        const uint32_t b = (x >> shift) & dmask;
+        if (!masses) {
+          __hip_atomic_fetch_add(rb_c + 4u * b + (uint32_t)(lane & 3), c, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+          if (b != run_b) {
+            if (run_b != 0xFFFFFFFFu) {
+              __hip_atomic_fetch_add(rb_c + run_b, run_c, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+              __hip_atomic_fetch_add(rb_m + run_b, run_m, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            run_b = b;
+            run_c = 0u;
+            run_m = 0.0;
+          }
+          run_c += c;
+          run_m += (double)c * wkey(x);
+        }
       }
     });
+    if (run_b != 0xFFFFFFFFu) {
+      __hip_atomic_fetch_add(rb_c + run_b, run_c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(rb_m + run_b, run_m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (tid == 0 && xcnt && (xkey & hmask) == hpre) {
-      const uint32_t b = (xkey >> shift) & 255u;
-      __hip_atomic_fetch_add(rb_c + b, xcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t b = (xkey >> shift) & dmask;
+      __hip_atomic_fetch_add(rb_c + (masses ? b : 4u * b), xcnt, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
       if (masses)
         __hip_atomic_fetch_add(rb_m + b, xmass, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     if (w == 0) {
-      // lane l: bins 255 - 4l .. 252 - 4l, descending
-      uint32_t c4[4];
-      double m4[4];
+      // lane l: bins top - bpl l down to top - bpl l - bpl + 1 (descending)
+      const int top = nb - 1 - bpl * lane;
+      auto cnt_of = [&](int b) -> uint32_t {
+        if (masses) return rb_c[b];
+        const uint4 v = reinterpret_cast<const uint4*>(rb_c)[b];
+        return (v.x + v.y) + (v.z + v.w);
+      };
       uint32_t cl = 0u;
       double ml = 0.0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 255 - 4 * lane - q;
-        c4[q] = rb_c[b];
-        m4[q] = masses ? rb_m[b] : 0.0;
-        cl += c4[q];
-        ml += m4[q];
+#pragma unroll 4
+      for (int q = 0; q < bpl; ++q) {
+        cl += cnt_of(top - q);
+        if (masses) ml += rb_m[top - q];
       }
       int b_hit = -1;
       uint32_t c_above = 0u, c_hit = 0u;
@@ -1172,14 +1227,17 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       if (!masses) {
         const uint32_t incl = scan_incl_u32(cl);
         uint32_t run = incl - cl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (b_hit < 0 && run < need && need <= run + c4[q]) {
-            b_hit = 255 - 4 * lane - q;
-            c_above = run;
-            c_hit = c4[q];
+        if (run < need && need <= incl) {
+#pragma unroll 4
+          for (int q = 0; q < bpl; ++q) {
+            const uint32_t cq = cnt_of(top - q);
+            if (b_hit < 0 && run < need && need <= run + cq) {
+              b_hit = top - q;
+              c_above = run;
+              c_hit = cq;
+            }
+            run += cq;
           }
-          run += c4[q];
         }
       } else {
         const double incl = scan_incl_f64(ml);
@@ -1187,21 +1245,25 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
         int b_last = -1;
         double m_last = 0.0;
         uint32_t c_last = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (c4[q]) {
-            if (b_hit < 0 && run < target && run + m4[q] >= target) {
-              b_hit = 255 - 4 * lane - q;
-              m_above = run;
-              c_hit = c4[q];
+        if (cl) {
+#pragma unroll 4
+          for (int q = 0; q < bpl; ++q) {
+            const uint32_t cq = rb_c[top - q];
+            const double mq = rb_m[top - q];
+            if (cq) {
+              if (b_hit < 0 && run < target && run + mq >= target) {
+                b_hit = top - q;
+                m_above = run;
+                c_hit = cq;
+              }
+              if (b_hit < 0) {
+                b_last = top - q;
+                m_last = run;
+                c_last = cq;
+              }
             }
-            if (b_hit < 0) {
-              b_last = 255 - 4 * lane - q;
-              m_last = run;
-              c_last = c4[q];
-            }
+            run += mq;
           }
-          run += m4[q];
         }
         if (ballot(b_hit >= 0) == 0u) {
           // rounding left the target above every prefix: the lowest weighted bin
@@ -1213,29 +1275,135 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       const uint64_t f = ballot(b_hit >= 0);
       const int L = f ? __ffsll((unsigned long long)f) - 1 : -1;
       if (lane == (L < 0 ? 0 : L)) {
-        info.sc_u[0] = L < 0 ? 0xFFFFFFFFu : (uint32_t)b_hit;
-        info.sc_u[1] = c_above;
-        info.sc_u[2] = c_hit;
-        info.sc_d[0] = m_above;
+        info.sc_u[4 * slot + 0] = L < 0 ? 0xFFFFFFFFu : (uint32_t)b_hit;
+        info.sc_u[4 * slot + 1] = c_above;
+        info.sc_u[4 * slot + 2] = c_hit;
+        info.sc_d[slot] = m_above;
+      }
+      // clear this level's bins for the next one
+      for (int i = lane; i < nb; i += 64) {
+        reinterpret_cast<uint4*>(rb_c)[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (masses) rb_m[i] = 0.0;
       }
     }
     __syncthreads();
+    RLevel res;
+    res.b = uni(info.sc_u[4 * slot + 0]);
+    res.c_above = uni(info.sc_u[4 * slot + 1]);
+    res.c_hit = uni(info.sc_u[4 * slot + 2]);
+    res.m_above = uni(info.sc_d[slot]);
+    return res;
   };
+
+  // -- a missed truncation with top-k: a second threshold from the sample -----------
+  // The source is the whole row. The first step of every slice (the tokens
+  // the row statistics came from) estimates the key above which about 2k
+  // tokens of the row lie: the sample's R-th largest key, R = 2k n_s / |F| + 8
+  // (a radix select over the sample). One walk appends every legal token at
+  // or above it to the wave pools; when they hold all of them and at least k,
+  // the k-th largest key is among them and the pools become the source of the
+  // searches and output walks below. Otherwise the row stays the source.
+  if (topk_eff && radix && !use_pool && a.seg <= 65536) {
+    Raw<DT> sraw;
+    uint32_t smb = 0u;
+    {
+      RowReader<DT, 1> rd(sl, lane);
+      if (rd.n > 0) {
+        rd.issue(0, 0);
+        rd.fetch(0, 0, sraw, smb);
+      }
+    }
+    uint32_t skey[8], svm = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      skey[j] = K::of(sraw.bits(j));
+      const bool ok = ((smb >> j) & 1u) && skey[j] > K::kNegInf && skey[j] < K::kPosInf;
+      svm |= (ok ? 1u : 0u) << j;
+    }
+    const uint32_t ns = uni(block_sum_u32((uint32_t)__popc(svm)));
+    if (ns > 0u) {
+      const uint64_t r2 = (2ull * (uint64_t)kk * ns + nfin - 1u) / nfin + 8u;
+      uint32_t need = (uint32_t)min(r2, (uint64_t)ns);
+      auto sample_items = [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((svm >> j) & 1u) f(skey[j], 1u);
+      };
+      uint32_t lk = 0u;
+      radix_begin();
+      for (int l = 0; l < n_levels(false); ++l) {
+        const int shift = lvl_shift(false, l);
+        const RLevel rl =
+            radix_level(sample_items, shift, 8, lk, false, 0u, 0.0, need, 0.0, 0u, 0u, 0.0);
+        if (rl.b == 0xFFFFFFFFu) { lk = K::kMax; break; }  // (never: need <= n_s)
+        need -= rl.c_above;
+        lk |= rl.b << shift;
+      }
+      if (lk != K::kMax) {
+        uint32_t pc = 0u;
+        stream_slice<DT, 2>(sl, lane, [&](const Raw<DT>& raw, uint32_t mb, int e) {
+          uint32_t cb = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            cb |= (((mb >> j) & 1u) && K::of(raw.bits(j)) >= lk) ? (1u << j) : 0u;
+          pc = append_pool<DT>(cb, raw, (uint32_t)(e - sl.wb), pc, my_pk, my_pid);
+        });
+        if (lane == 0) info.cnt[w] = pc;
+        __syncthreads();
+        const uint32_t cn = act16 ? info.cnt[lane] : 0u;
+        const bool ovf = uni(wave_reduce<OpMax>(cn > kCap ? 1u : 0u)) != 0u;
+        const uint32_t tot = uni(wave_reduce<OpSum>(cn));
+        __syncthreads();  // info.cnt is read before it is written again
+        if (!ovf && tot >= (uint32_t)kk) {
+          use_pool = true;
+          to_pool = true;
+          my_cnt = (int)pc;
+          src_lo = lk;
+        }
+      }
+    }
+  }
 
   // -- the k-th largest key (top-k) ----------------------------------------------
   if (topk_eff && !settled && radix) {
-    uint32_t prefix = 0u, need = (uint32_t)kk;
-    for (int shift = kKeyBits - 8; shift >= 0 && !failed; shift -= 8) {
-      radix_level(shift, prefix, false, 0u, 0.0, need, 0.0, 0u, 0u, 0.0);
-      const uint32_t b = uni(info.sc_u[0]);
-      if (b == 0xFFFFFFFFu) { failed = true; break; }  // (never: k <= the finite count)
-      need -= uni(info.sc_u[1]);
-      prefix |= b << shift;
+    uint32_t prefix = 0u, need = (uint32_t)kk, c_kap = 0u;
+    const bool wide = !use_pool;
+    radix_begin();
+    for (int l = 0; l < n_levels(wide) && !failed; ++l) {
+      const int shift = lvl_shift(wide, l);
+      const RLevel rl = radix_level(for_items, shift, lvl_width(wide, l), prefix, false, 0u, 0.0,
+                                    need, 0.0, 0u, 0u, 0.0);
+      if (rl.b == 0xFFFFFFFFu) { failed = true; break; }  // (never: k <= the finite count)
+      need -= rl.c_above;
+      c_kap = rl.c_hit;  // at the last level: the tokens of the key itself
+      prefix |= rl.b << shift;
       ++rounds;
-      __syncthreads();  // info is rewritten by the next level
     }
     kap = prefix;
     n_keep_k = need;
+    // A full-row source: every token at or above the k-th largest key (the
+    // top-k set and the other ties at its boundary key) is appended, in id
+    // order, to the wave pools, which replace the row as the source when they
+    // hold it; the top-p search and the output walks then read the pools.
+    if (!failed && !use_pool && a.seg <= 65536 &&
+        (uint32_t)kk - n_keep_k + c_kap <= (uint32_t)(kWaves * kCap / 2)) {
+      uint32_t pc = 0u;
+      stream_slice<DT, 2>(sl, lane, [&](const Raw<DT>& raw, uint32_t mb, int e) {
+        uint32_t cb = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          cb |= (((mb >> j) & 1u) && K::of(raw.bits(j)) >= kap) ? (1u << j) : 0u;
+        pc = append_pool<DT>(cb, raw, (uint32_t)(e - sl.wb), pc, my_pk, my_pid);
+      });
+      if (lane == 0) info.cnt[w] = pc;
+      __syncthreads();
+      const bool ovf = uni(wave_reduce<OpMax>(act16 && info.cnt[lane] > kCap ? 1u : 0u)) != 0u;
+      if (!ovf) {
+        use_pool = true;
+        to_pool = true;
+        my_cnt = (int)pc;
+      }
+    }
   } else if (topk_eff && !settled) {
     // quaternary three-pivot search on counts (page "Qrita", key design 2)
     uint32_t lo = src_lo - 1u, hi = maxk;
@@ -1335,17 +1503,18 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           // digits from the top; the top-k boundary key counts n_keep_k tokens
           uint32_t prefix = 0u, c_star = 0u;
           double above = 0.0;
-          for (int shift = kKeyBits - 8; shift >= 0; shift -= 8) {
-            radix_level(shift, prefix, true, excl, above, 0u, target, kap,
-                        topk_eff ? n_keep_k : 0u, topk_eff ? (double)n_keep_k * w_kap : 0.0);
-            const uint32_t b = uni(info.sc_u[0]);
-            const double m_ab = uni(info.sc_d[0]);
-            c_star = uni(info.sc_u[2]);   // at the last level: the tokens of the key itself
-            __syncthreads();  // info is rewritten by the next level
+          const bool wide = !use_pool;
+          radix_begin();
+          for (int l = 0; l < n_levels(wide); ++l) {
+            const int shift = lvl_shift(wide, l);
+            const RLevel rl = radix_level(
+                for_items, shift, lvl_width(wide, l), prefix, true, excl, above, 0u, target, kap,
+                topk_eff ? n_keep_k : 0u, topk_eff ? (double)n_keep_k * w_kap : 0.0);
+            c_star = rl.c_hit;   // at the last level: the tokens of the key itself
             ++rounds;
-            if (b == 0xFFFFFFFFu) { failed = true; break; }  // (never: the top key has weight 1)
-            above = m_ab;
-            prefix |= b << shift;
+            if (rl.b == 0xFFFFFFFFu) { failed = true; break; }  // (never: the top key has weight 1)
+            above = rl.m_above;
+            prefix |= rl.b << shift;
           }
           if (!failed) {
             // the boundary key, its count and weight, and the smallest count of
@@ -1722,7 +1891,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     if (a.cand_count) a.cand_count[r] = (int32_t)n_p;
     if (SAMPLE && sampled && !a.uniforms) a.offset[r] = a.offset[r] + 1u;
     if (a.dbg) {
-      a.dbg[4 * r + 0] = use_pool ? 0 : 1;
+      a.dbg[4 * r + 0] = to_pool ? 3 : (use_pool ? 0 : 1);
       a.dbg[4 * r + 1] = rounds;
       a.dbg[4 * r + 2] = (int32_t)ccount;
       a.dbg[4 * r + 3] = (int32_t)n_p;
