@@ -1157,10 +1157,12 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     uint32_t b, c_above, c_hit;
     double m_above;
   };
+  // (items may pass keys as offsets from kofs: the weights are those of x + kofs)
   auto radix_level = [&](auto&& items, int shift, int width, uint32_t prefix, bool masses,
                          uint32_t excl, double above, uint32_t need, double target,
-                         uint32_t xkey, uint32_t xcnt, double xmass) -> RLevel {
-    const int nb = width > 8 ? kRBins : 256;  // bins of this level (a multiple of 64)
+                         uint32_t xkey, uint32_t xcnt, double xmass,
+                         uint32_t kofs = 0u) -> RLevel {
+    const int nb = 1 << (width > 8 ? width : 8);  // bins of this level (a multiple of 64)
     const int bpl = nb / 64;                  // bins per lane of the scan
     const int slot = rpar;
     rpar ^= 1;
@@ -1172,7 +1174,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     uint32_t run_b = 0xFFFFFFFFu, run_c = 0u;
     double run_m = 0.0;
     items([&](uint32_t x, uint32_t c) {
-      if ((x & hmask) == hpre && (!masses || x > excl)) {
+      if ((x & hmask) == hpre && (!masses || x + kofs > excl)) {
         const uint32_t b = (x >> shift) & dmask;
         if (!masses) {
           __hip_atomic_fetch_add(rb_c + 4u * b + (uint32_t)(lane & 3), c, __ATOMIC_RELAXED,
@@ -1190,7 +1192,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
             run_m = 0.0;
           }
           run_c += c;
-          run_m += (double)c * wkey(x);
+          run_m += (double)c * wkey(x + kofs);
         }
       }
     });
@@ -1295,6 +1297,133 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     return res;
   };
 
+  // Bucket select over an fp32 pool (flags 0): the pool keys lie in [lo, hi];
+  // one level counts them in 1024 buckets of width 2^s spanning that range
+  // (s from the span, so the buckets follow the keys actually present rather
+  // than fixed digits), and the level's boundary bucket becomes the range of
+  // the next. Once that bucket holds at most 64 tokens, its tokens are
+  // gathered into one wave, sorted by key and searched directly. Returns the
+  // boundary key, the count of its tokens, and what lies above it (the count
+  // still needed, or the mass). Masses: only items above excl count; the
+  // extra bucket holds xcnt tokens of key xkey (the top-k set's boundary).
+  struct RSel {
+    bool ok;
+    uint32_t key, c_key, need_rest;
+    double above;
+  };
+  // 256 buckets for pools of up to 4096 tokens, 1024 above
+  const int kBktBits = ccount_all <= 4096u ? 8 : 10;
+  uint32_t* const glist = DT == 0 ? rb_f32 + 4096 : hist;  // 64 (key, count) pairs, a counter
+  auto bucket_select = [&](bool masses, uint32_t lo, uint32_t hi, uint32_t excl, uint32_t need,
+                           double target, uint32_t xkey, uint32_t xcnt, double xmass) -> RSel {
+    RSel out{false, 0u, 0u, need, 0.0};
+    double above = 0.0;
+    radix_begin();
+    for (int it = 0; it < 6; ++it) {
+      const uint32_t span = hi - lo;
+      const int nbits = span == 0u ? 0 : 32 - __clz(span);
+      const int sh = nbits > kBktBits ? nbits - kBktBits : 0;
+      const uint32_t blo = lo, bhi = hi;
+      auto items = [&](auto&& f) {
+        for_items([&](uint32_t x, uint32_t c) {
+          if (x >= blo && x <= bhi && (!masses || x > excl)) f(x - blo, c);
+        });
+      };
+      const bool xin = xcnt && xkey >= lo && xkey <= hi;
+      const RLevel rl = radix_level(items, sh, kBktBits, 0u, masses, excl, above, need, target,
+                                    xin ? xkey - lo : 0u, xin ? xcnt : 0u, xmass, lo);
+      ++rounds;
+      if (rl.b == 0xFFFFFFFFu) return out;  // (never: the range holds the boundary)
+      if (masses) above = rl.m_above;
+      else need -= rl.c_above;
+      lo = blo + (rl.b << sh);
+      hi = min(bhi, lo + ((1u << sh) - 1u));
+      if (sh == 0) {  // one key
+        out.ok = true;
+        out.key = lo;
+        out.c_key = rl.c_hit;
+        out.need_rest = need;
+        out.above = above;
+        return out;
+      }
+      if (rl.c_hit > 64u) continue;
+      // gather the bucket's tokens (at most 64 entries) and finish in wave 0
+      if (tid == 0) glist[128] = 0u;
+      __syncthreads();
+      const uint32_t glo = lo, ghi = hi;
+      for_items([&](uint32_t x, uint32_t c) {
+        if (x >= glo && x <= ghi && (!masses || x > excl)) {
+          const uint32_t q = atomicAdd(glist + 128, 1u);
+          if (q < 64u) { glist[2 * q] = x; glist[2 * q + 1] = c; }
+        }
+      });
+      if (tid == 0 && xcnt && xkey >= glo && xkey <= ghi) {
+        const uint32_t q = atomicAdd(glist + 128, 1u);
+        if (q < 64u) { glist[2 * q] = xkey; glist[2 * q + 1] = xcnt; }
+      }
+      __syncthreads();
+      const int slot = rpar;
+      rpar ^= 1;
+      if (w == 0) {
+        const uint32_t n = uni(min(glist[128], 64u));
+        uint32_t key = (uint32_t)lane < n ? glist[2 * lane] : 0u;
+        uint32_t cnt = (uint32_t)lane < n ? glist[2 * lane + 1] : 0u;
+        // every entry against every other (readlane broadcasts, no ordering
+        // needed): the tokens, and for masses the mass, of the larger keys
+        const double wl = (masses && cnt) ? (double)cnt * wkey(key) : 0.0;
+        uint32_t c_gt = 0u, c_eq = 0u;
+        double m_gt = 0.0, m_eq = 0.0;
+        for (int jj = 0; jj < (int)n; ++jj) {
+          const uint32_t kj = readlane_u32(key, jj);
+          const uint32_t cj = readlane_u32(cnt, jj);
+          c_gt += kj > key ? cj : 0u;
+          c_eq += kj == key ? cj : 0u;
+          if (masses) {
+            const double wj = readlane_f64(wl, jj);
+            m_gt += kj > key ? wj : 0.0;
+            m_eq += kj == key ? wj : 0.0;
+          }
+        }
+        // the boundary: the largest key whose tokens, with those above, reach
+        // the count or the mass
+        const bool live = (uint32_t)lane < n && cnt != 0u;
+        bool q;
+        if (!masses) q = live && c_gt < need && need <= c_gt + c_eq;
+        else q = live && above + m_gt < target && above + m_gt + m_eq >= target;
+        uint64_t hit = ballot(q);
+        if (masses && !hit) {
+          // rounding left the target above every prefix: the lowest weighted key
+          const uint32_t kmin = wave_reduce<OpMin>(live && wl > 0.0 ? key : 0xFFFFFFFFu);
+          hit = ballot(live && key == kmin);
+        }
+        const int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+        const uint32_t kL = L < 0 ? 0u : readlane_u32(key, L < 0 ? 0 : L);
+        const uint32_t cgtL = L < 0 ? 0u : readlane_u32(c_gt, L < 0 ? 0 : L);
+        const uint32_t ceqL = L < 0 ? 0u : readlane_u32(c_eq, L < 0 ? 0 : L);
+        const double mgtL = L < 0 ? 0.0 : readlane_f64(m_gt, L < 0 ? 0 : L);
+        if (lane == 0) {
+          info.sc_u[4 * slot + 0] = (L < 0 || glist[128] > 64u) ? 0xFFFFFFFFu : kL;
+          info.sc_u[4 * slot + 1] = cgtL;
+          info.sc_u[4 * slot + 2] = ceqL;
+          info.sc_d[slot] = above + mgtL;
+        }
+      }
+      __syncthreads();
+      const uint32_t kr = uni(info.sc_u[4 * slot + 0]);
+      if (kr == 0xFFFFFFFFu) return out;  // (never: at most 64 entries hold the boundary)
+      out.ok = true;
+      out.key = kr;
+      out.c_key = uni(info.sc_u[4 * slot + 2]);
+      out.need_rest = need - uni(info.sc_u[4 * slot + 1]);
+      out.above = uni(info.sc_d[slot]);
+      return out;
+    }
+    return out;
+  };
+  // the bucket select serves fp32 pools; bf16 pools without a value histogram
+  // and full rows take the radix levels
+  auto use_bucket = [&]() { return DT == 0 && radix && use_pool; };
+
   // -- a missed truncation with top-k: a second threshold from the sample -----------
   // The source is the whole row. The first step of every slice (the tokens
   // the row statistics came from) estimates the key above which about 2k
@@ -1368,8 +1497,16 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   if (topk_eff && !settled && radix) {
     uint32_t prefix = 0u, need = (uint32_t)kk, c_kap = 0u;
     const bool wide = !use_pool;
-    radix_begin();
-    for (int l = 0; l < n_levels(wide) && !failed; ++l) {
+    if (use_bucket()) {
+      const RSel rs = bucket_select(false, src_lo, maxk, 0u, need, 0.0, 0u, 0u, 0.0);
+      if (!rs.ok) failed = true;
+      prefix = rs.key;
+      need = rs.need_rest;
+      c_kap = rs.c_key;
+    } else {
+      radix_begin();
+    }
+    for (int l = 0; l < (use_bucket() ? 0 : n_levels(wide)) && !failed; ++l) {
       const int shift = lvl_shift(wide, l);
       const RLevel rl = radix_level(for_items, shift, lvl_width(wide, l), prefix, false, 0u, 0.0,
                                     need, 0.0, 0u, 0u, 0.0);
@@ -1504,8 +1641,18 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           uint32_t prefix = 0u, c_star = 0u;
           double above = 0.0;
           const bool wide = !use_pool;
-          radix_begin();
-          for (int l = 0; l < n_levels(wide); ++l) {
+          if (use_bucket()) {
+            const RSel rs = bucket_select(true, topk_eff ? kap : src_lo, maxk, excl, 0u, target,
+                                          kap, topk_eff ? n_keep_k : 0u,
+                                          topk_eff ? (double)n_keep_k * w_kap : 0.0);
+            if (!rs.ok) failed = true;
+            prefix = rs.key;
+            c_star = rs.c_key;
+            above = rs.above;
+          } else {
+            radix_begin();
+          }
+          for (int l = 0; l < (use_bucket() ? 0 : n_levels(wide)) && !failed; ++l) {
             const int shift = lvl_shift(wide, l);
             const RLevel rl = radix_level(
                 for_items, shift, lvl_width(wide, l), prefix, true, excl, above, 0u, target, kap,
