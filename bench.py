@@ -164,7 +164,7 @@ def stored_traffic(cfg):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
     (scaled by a plain copy of known size), from profiles/, or None when the
     kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_workload{cfg}.txt")
+    path = os.path.join(ROOT, "profiles", f"filter_kernel_workload{cfg}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
