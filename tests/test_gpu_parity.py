@@ -470,19 +470,23 @@ def test_small_temperature_large_logits(qs):
 
 
 @pytest.mark.gpu
-def test_histogram_pool_overflow_declines(qs):
+def test_histogram_pool_overflow_direct(qs):
     """bf16 rows whose kept set is larger than the value-histogram path's
-    pools (flat logits, p close to 1, every token legal): the path declines
-    and the truncation path settles the row (search rounds are reported);
-    rows with a small kept set stay on the histogram path (no rounds). Both
-    must match the oracle."""
+    pools (every token legal, a large temperature and p close to 1, a
+    positive boundary value): the waves whose pools overflow emit their
+    outputs from the registers that hold the row, so these rows stay on the
+    histogram path (no search rounds) like the rows with a small kept set. A
+    flat row whose boundary is not positive leaves that path for the
+    truncation path. All must match the oracle: lists, masks, dense
+    probabilities and tokens."""
     rng = np.random.default_rng(123)
     B, V = 6, 40000
-    z = (0.05 * rng.standard_normal((B, V))).astype(np.float32)
-    z[3:] = (3.0 * rng.standard_normal((3, V))).astype(np.float32)
-    T = np.ones(B, np.float32)
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    z[:2] += 20.0
+    z[2] = (0.05 * rng.standard_normal(V)).astype(np.float32)
+    T = np.array([3.0, 3.0, 1.0, 1.0, 1.0, 1.0], np.float32)
     k = np.zeros(B, np.int32)
-    p = np.array([0.999, 0.99, 0.995, 0.5, 0.9, 0.7], np.float32)
+    p = np.array([0.99, 0.95, 0.999, 0.5, 0.9, 0.7], np.float32)
     bits = np.ones((B, V), bool)
     w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
                            T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
@@ -490,8 +494,10 @@ def test_histogram_pool_overflow_declines(qs):
                            offsets=np.zeros(B, np.uint64))
     rep, out = check_workload(qs, w, seed=8, cand_cap=65536)
     dbg = out["debug"].cpu().numpy()
-    assert (dbg[:3, 1] >= 1).all(), dbg.tolist()   # declined: truncation path rounds
-    assert (dbg[3:, 1] == 0).all(), dbg.tolist()   # settled by the value histogram
+    direct = [0, 1, 3, 4, 5]
+    assert (dbg[direct, 0] == 0).all() and (dbg[direct, 1] == 0).all(), dbg.tolist()
+    assert (dbg[:2, 3] > 16 * 960).all(), dbg.tolist()   # kept sets larger than the pools
+    assert dbg[2, 1] >= 1, dbg.tolist()                   # declined: truncation path rounds
 
 
 @pytest.mark.gpu

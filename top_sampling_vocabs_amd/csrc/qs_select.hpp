@@ -562,6 +562,64 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     }
   };
   const bool long_pool = uni(my_cnt) > 192;
+  // A wave whose tokens at or above the boundary overflow its pool reads its
+  // slice again instead (all steps requested at once, the legal bits from the
+  // bitmask) and walks it: f(e, bits) per step with this lane's 8 tokens as
+  // pool entries and the bits of those at or above the boundary
+  const bool direct = uni(pcnt) > kPool;
+  auto direct_walk = [&](auto&& f) __attribute__((always_inline)) {
+    // steps in groups of 4: the group's requests go out together
+    constexpr int kG = 4;
+    static_for<0, (NL + kG - 1) / kG>([&](auto gc) {
+      constexpr int g0 = decltype(gc)::value * kG;
+      uint4 x[kG];
+      uint32_t lbs[kG];
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        const int st = g0 + i;
+        const int e0 = lane_e + st * kStep;
+        if (st < NL) {
+          x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsrc, voff, st * kStep * 2, 0));
+          uint32_t lb = 0u;
+          if (e0 < sl.we) {
+            lb = bmrow ? (bmrow[e0 >> 5] >> (e0 & 31)) & 0xFFu : 0xFFu;
+            if (e0 + kChunk > sl.we) lb &= (1u << (sl.we - e0)) - 1u;
+          }
+          lbs[i] = lb;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        const int st = g0 + i;
+        if (st < NL) {
+          const uint32_t lb = lbs[i];
+          uint32_t r4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t pm = (((lb >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
+                                (((lb >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+            r4[q] = bfi(pm, r4[q], 0x80008000u);  // illegal -> -0, below the boundary
+          }
+          const uint32_t o0 = (uint32_t)(lane_e + st * kStep - sl.wb);
+          uint32_t e[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            e[jj] = (((r4[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu) << 16) | (o0 + (uint32_t)jj);
+          const uint32_t cb = keep_bits(make_uint4(r4[0], r4[1], r4[2], r4[3]));
+          if (ballot(cb != 0u)) f(e, cb);
+        }
+      }
+    });
+  };
+  auto classify = [&](uint32_t e) __attribute__((always_inline)) {
+    if (e > e_gt) {
+      ++gt;
+      mgt += wtab[tab_base - (e >> 16)];
+    } else {
+      ++ties;
+    }
+  };
   auto walk_a = [&](auto kpc) {
     constexpr int KP = decltype(kpc)::value;
     for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
@@ -569,20 +627,21 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       uint32_t e[4];
       load_entries(kpc, ib, e);
 #pragma unroll
-      for (int k = 0; k < KP; ++k) {
-        if (ib + k < my_cnt) {
-          if (e[k] > e_gt) {
-            ++gt;
-            mgt += wtab[tab_base - (e[k] >> 16)];
-          } else {
-            ++ties;
-          }
-        }
-      }
+      for (int k = 0; k < KP; ++k)
+        if (ib + k < my_cnt) classify(e[k]);
     }
   };
-  if (long_pool) walk_a(std::integral_constant<int, 4>{});
-  else walk_a(std::integral_constant<int, 1>{});
+  if (direct) {
+    direct_walk([&](const uint32_t (&e)[8], uint32_t cb) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if ((cb >> k) & 1u) classify(e[k]);
+    });
+  } else if (long_pool) {
+    walk_a(std::integral_constant<int, 4>{});
+  } else {
+    walk_a(std::integral_constant<int, 1>{});
+  }
   gt = wave_reduce<OpSum>(gt);
   ties = wave_reduce<OpSum>(ties);
   mgt = wave_sum_f64(mgt);
@@ -593,10 +652,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     info.mass[w] = mgt;
   }
   __syncthreads();
-  {
-    const bool over = uni(wave_reduce<OpMax>(act16 && info.cnt[lane] > kPool ? 1u : 0u)) != 0u;
-    if (over) return false;
-  }
 
   // -- tie quota per wave, list offsets, masses, the sampled wave -----------------------
   double u = 0.0;
@@ -684,16 +739,13 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // this lane's last kept entry with q > 0; entries never equal ~0u (their
   // offset field stays below the slice length)
   uint32_t last_e = ~0u;
-  auto walk_d = [&](auto kpc) {
-   constexpr int KP = decltype(kpc)::value;
-   for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
-    const int ib = i0 + KP * lane;
-    uint32_t e[4];
-    load_entries(kpc, ib, e);
+  // KP entries per lane (consecutive ids), vbits marking the valid ones
+  auto emit = [&](auto kpc, const auto& e, uint32_t vbits) __attribute__((always_inline)) {
+    constexpr int KP = decltype(kpc)::value;
     uint32_t kb = 0u, tb = 0u;  // kept (above the boundary) and tie bits of the KP
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
-      const bool valid = ib + k < my_cnt;
+      const bool valid = (vbits >> k) & 1u;
       kb |= (valid && e[k] > e_gt ? 1u : 0u) << k;
       tb |= (valid && e[k] <= e_gt ? 1u : 0u) << k;
     }
@@ -718,7 +770,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     const uint32_t kc = (uint32_t)__popc(kb);
     const uint32_t kincl = KP == 1 ? count_below(ballot(kc != 0u)) + kc : scan_incl_u32(kc);
     uint32_t pos = pos_base + kincl - kc;
-    double qv[4];
+    double qv[KP];
     double lane_sum = 0.0;
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
@@ -762,10 +814,28 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       }
       cbase += readlane_f64(incl, 63);
     }
-  }
   };
-  if (long_pool) walk_d(std::integral_constant<int, 4>{});
-  else walk_d(std::integral_constant<int, 1>{});
+  auto walk_d = [&](auto kpc) {
+    constexpr int KP = decltype(kpc)::value;
+    for (int i0 = 0; i0 < my_cnt; i0 += 64 * KP) {
+      const int ib = i0 + KP * lane;
+      uint32_t e[4];
+      load_entries(kpc, ib, e);
+      uint32_t vb = 0u;
+#pragma unroll
+      for (int k = 0; k < KP; ++k) vb |= (ib + k < my_cnt ? 1u : 0u) << k;
+      emit(kpc, e, vb);
+    }
+  };
+  if (direct) {
+    direct_walk([&](const uint32_t (&e)[8], uint32_t cb) {
+      emit(std::integral_constant<int, 8>{}, e, cb);
+    });
+  } else if (long_pool) {
+    walk_d(std::integral_constant<int, 4>{});
+  } else {
+    walk_d(std::integral_constant<int, 1>{});
+  }
   if (mask_row) {
     for (int i = lane; i < sw1 - sw0; i += 64)
       __builtin_nontemporal_store(my_stage[i], mask_row + sw0 + i);
