@@ -229,7 +229,7 @@ def time_graph(preps, K, flags=None):
 # (its runs C, I and J drop duplicate handling, sort the candidates, or sort
 # the full row: not paths of this library).
 ABLATION_RUNS = [
-    ("A", "normal path: value histogram (bf16 in registers) / truncation hit + quaternary search (fp32)", 0),
+    ("A", "normal path: value histogram (bf16 in registers) / truncation hit + bucket select (fp32)", 0),
     ("B", "single streamed tier instead of the register tiers", 8),
     ("D", "forced fallback: quaternary searches over the full row", 1),
     ("E", "no truncation: quaternary searches over the full row", 2),

@@ -155,6 +155,29 @@ def test_path_invariance(qs):
                 assert (dbg[ok, 1] >= qr).all(), (cfg, dbg[ok, 1], qr)
 
 
+SWITCHES = ("FLAG_FORCE_MISS", "FLAG_NO_TRUNCATION", "FLAG_PIVOT_SEARCH", "FLAG_STREAM",
+            "FLAG_BINARY_PIVOT")
+
+
+@pytest.mark.parametrize("switch", SWITCHES)
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_switches_match_oracle(qs, cfg, switch):
+    """Every ablation switch (page "Qrita", ablation table: runs B, D, E, F, G
+    and the page's own design, Q) against the oracle directly, on every
+    workload at reduced size: masks, lists, probabilities, tokens and
+    statuses, to the same tolerances as the normal path."""
+    w = workloads.make(cfg, **SMALL[cfg])
+    flags = getattr(qs, switch)
+    if switch == "FLAG_BINARY_PIVOT":
+        flags |= qs.FLAG_PIVOT_SEARCH
+    print(f"workload {cfg} switch {switch}", flush=True)
+    rep, out = check_workload(qs, w, seed=31 + cfg, flags=flags)
+    dbg = out["debug"].cpu().numpy()
+    ok = out["status"].cpu().numpy() == 0
+    if switch in ("FLAG_FORCE_MISS", "FLAG_NO_TRUNCATION"):
+        assert (dbg[ok, 0] == 1).all(), np.bincount(dbg[ok, 0])  # searched the full row
+
+
 def lists_equal(a, b):
     """Candidate lists agree on their first cand_count entries (the rest of each
     row is not written)."""
