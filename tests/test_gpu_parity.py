@@ -497,11 +497,10 @@ def test_histogram_pool_overflow_direct(qs):
     """bf16 rows whose kept set is larger than the value-histogram path's
     pools (every token legal, a large temperature and p close to 1, a
     positive boundary value): the waves whose pools overflow emit their
-    outputs from the registers that hold the row, so these rows stay on the
-    histogram path (no search rounds) like the rows with a small kept set. A
-    flat row whose boundary is not positive leaves that path for the
-    truncation path. All must match the oracle: lists, masks, dense
-    probabilities and tokens."""
+    outputs from a second read of their slice, so these rows stay on the
+    histogram path (no search rounds) like the rows with a small kept set,
+    and so does a flat row whose boundary is negative. All must match the
+    oracle: lists, masks, dense probabilities and tokens."""
     rng = np.random.default_rng(123)
     B, V = 6, 40000
     z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
@@ -517,10 +516,8 @@ def test_histogram_pool_overflow_direct(qs):
                            offsets=np.zeros(B, np.uint64))
     rep, out = check_workload(qs, w, seed=8, cand_cap=65536)
     dbg = out["debug"].cpu().numpy()
-    direct = [0, 1, 3, 4, 5]
-    assert (dbg[direct, 0] == 0).all() and (dbg[direct, 1] == 0).all(), dbg.tolist()
-    assert (dbg[:2, 3] > 16 * 960).all(), dbg.tolist()   # kept sets larger than the pools
-    assert dbg[2, 1] >= 1, dbg.tolist()                   # declined: truncation path rounds
+    assert (dbg[:, 0] == 0).all() and (dbg[:, 1] == 0).all(), dbg.tolist()
+    assert (dbg[:3, 3] > 16 * 960).all(), dbg.tolist()   # kept sets larger than the pools
 
 
 @pytest.mark.gpu
@@ -555,3 +552,33 @@ def test_topk_rank_among_zero_logits(qs):
     rows = list(range(0, 320, 16)) + zero_rows.tolist()
     rep, out = check_workload(qs, w, rows=rows, seed=12, cand_cap=V, dense=False)
     assert (out["status"].cpu().numpy()[zero_rows] == 0).all()
+
+
+def test_histogram_far_and_negative_boundaries(qs):
+    """bf16 rows whose top-k or top-p boundary value is negative (a large
+    temperature with p close to 1, or k above half the legal tokens), or lies
+    more than 2,048 values below the maximum (log-uniform magnitudes): the
+    value-histogram path builds the weights of every rank down to the
+    boundary and reads the row again for its outputs, so these rows stay on
+    that path (no search rounds). A row with exact zeros between the signs
+    leaves it for the truncation path. All must match the oracle."""
+    rng = np.random.default_rng(2024)
+    B, V = 8, 40000
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    z[3] = np.exp2(rng.uniform(-12, 8, V)).astype(np.float32)
+    z[4, rng.random(V) < 0.2] = 0.0
+    T = np.array([1.5, 1.0, 1.0, 1000.0, 1.5, 1.44, 1.0, 1.0], np.float32)
+    k = np.array([0, 30000, 25000, 0, 0, 0, 50, 0], np.int32)
+    p = np.array([0.99, 1.0, 0.95, 0.9, 0.99, 0.989, 1.0, 0.9], np.float32)
+    bits = np.ones((B, V), bool)
+    bits[5] = rng.random(V) < 0.3
+    bits[5, 0] = True
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rep, out = check_workload(qs, w, seed=12, cand_cap=V)
+    dbg = out["debug"].cpu().numpy()
+    on_path = [0, 1, 2, 3, 5, 6, 7]
+    assert (dbg[on_path, 0] == 0).all() and (dbg[on_path, 1] == 0).all(), dbg.tolist()
+    assert dbg[4, 1] >= 1 or dbg[4, 0] != 0, dbg.tolist()   # zeros between the signs

@@ -383,7 +383,9 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     nk_k = uni(info.sel_u[1]);
     w_k = uni(info.sel_d[0]);
     w_kap = uni(info.sel_d[1]);
-    if (rho_k >= sel::kExact) return false;  // the k-th value is not positive
+    // a k-th value that is not positive needs the rank order to be the value
+    // order: no tiny values between the signs
+    if (rho_k >= sel::kExact && n_tiny != 0u) return false;
     w_f_err = 0.0;                           // the top-k set is exact
   }
 
@@ -443,10 +445,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     n_keep = uni((uint32_t)cl);
     // rounding left the target above every prefix, or the bound on the tiny
     // values' mass leaves the cut open: the general path
-    if (rho_s == sel::kNone || n_keep == 0u || rho_s < rho_top ||
-        rho_s >= rho_top + (uint32_t)sel::kTab)
-      return false;
-    w_star = wtab[rho_s - rho_top];
+    if (rho_s == sel::kNone || n_keep == 0u || rho_s < rho_top) return false;
+    w_star = 0.0;  // from the weight table below
   } else if (topk_on) {
     rho_s = rho_k;
     n_keep = nk_k;
@@ -454,11 +454,39 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   } else {
     return false;  // everything kept: the general path
   }
-  // the boundary value must be positive and the weight table must reach it
-  if (rho_s >= sel::kExact || rho_s >= rho_top + (uint32_t)sel::kTab) return false;
+  // A boundary that is not positive, or that lies past the weight table (2,048
+  // values below the maximum): the extended mode. The weights of every rank
+  // from the maximum to the boundary go to a table in the pools' LDS, every
+  // wave reads its slice again for its counts and outputs (no pools), and
+  // entries carry 0xFFFF - rank instead of the raw bits (ranks order like
+  // the values, descending, when no tiny value lies between the signs).
+  const bool ext = rho_s >= sel::kExact || rho_s >= rho_top + (uint32_t)sel::kTab;
+  if (ext && n_tiny != 0u) return false;
   const uint32_t raw_star = sel::rho_mag(rho_s);        // bf16 bits of the boundary value
-  const uint32_t pstar = K::of(raw_star);
-  const uint32_t tab_base = sel::kMagLo + sel::kExact - 1u - rho_top;  // wtab[tab_base - raw]
+  uint32_t tab_base = sel::kMagLo + sel::kExact - 1u - rho_top;  // tabw[tab_base - raw]
+  const double* tabw = wtab;
+  if (ext) {
+    double* const xt = reinterpret_cast<double*>(pool_raw);
+    static_assert(sel::kRho * 8 <= kPoolBytes, "the extended weight table fits the pools");
+    if (run_t) {
+      const uint32_t rho0 = 16u * (uint32_t)tid;
+      if (rho0 + 16u > rho_top && rho0 <= rho_s) {
+        double wi = w0;
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t rho = rho0 + (uint32_t)i;
+          if (rho >= rho_top) {
+            if (rho <= rho_s) xt[rho - rho_top] = wi;
+            wi *= rh;
+          }
+        }
+      }
+    }
+    __syncthreads();  // the table
+    tabw = xt;
+    tab_base = 0xFFFFu - rho_top;
+  }
+  if (topp_on) w_star = tabw[ext ? rho_s - rho_top : tab_base - raw_star];
 
   // -- compaction: tokens at or above the boundary, in id order, to the wave's pool ------
   // pool entry: raw bits << 16 | token offset in the slice (id order = entry order)
@@ -491,7 +519,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   };
   // two steps per group: one prefix sum and one set of rounds for both, so
   // the rounds follow the fuller lane of the pair rather than of each step
-  static_for<0, (NL + 1) / 2>([&](auto gc) {
+  if (!ext) static_for<0, (NL + 1) / 2>([&](auto gc) {
     constexpr int s0 = 2 * decltype(gc)::value;
     constexpr bool two = s0 + 1 < NL;
     const uint32_t cb0 = keep_bits(xs[s0]);
@@ -546,7 +574,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // per wave: tokens above the boundary and their mass, ties at it (every
   // entry is at or above the boundary value, which is positive)
   const int my_cnt = (int)min(pcnt, kPool);
-  const uint32_t e_gt = (raw_star << 16) | 0xFFFFu;  // entries above it compare greater
+  // entries above the boundary compare greater
+  const uint32_t e_gt = ext ? ((0xFFFFu - rho_s) << 16) | 0xFFFFu : (raw_star << 16) | 0xFFFFu;
   uint32_t gt = 0u, ties = 0u;
   double mgt = 0.0;
   // KP consecutive entries per lane and round: one for short pools, four for
@@ -566,8 +595,11 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // slice again instead (all steps requested at once, the legal bits from the
   // bitmask) and walks it: f(e, bits) per step with this lane's 8 tokens as
   // pool entries and the bits of those at or above the boundary
-  const bool direct = uni(pcnt) > kPool;
-  auto direct_walk = [&](auto&& f) __attribute__((always_inline)) {
+  const bool direct = ext || uni(pcnt) > kPool;
+  // (write_keep: also store each step's keep byte in the mask staging, which
+  // the compaction did not fill in the extended mode)
+  uint32_t ext_cnt = 0u;
+  auto direct_walk = [&](auto&& f, bool write_keep) __attribute__((always_inline)) {
     // steps in groups of 4: the group's requests go out together
     constexpr int kG = 4;
     static_for<0, (NL + kG - 1) / kG>([&](auto gc) {
@@ -595,18 +627,39 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         if (st < NL) {
           const uint32_t lb = lbs[i];
           uint32_t r4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t pm = (((lb >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
-                                (((lb >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
-            r4[q] = bfi(pm, r4[q], 0x80008000u);  // illegal -> -0, below the boundary
-          }
           const uint32_t o0 = (uint32_t)(lane_e + st * kStep - sl.wb);
           uint32_t e[8];
+          uint32_t cb = 0u;
+          if (ext) {
+            // rank of every exact value (tiny ones are absent, huge ones were
+            // declined); legal tokens ranked at or above the boundary are kept
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            e[jj] = (((r4[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu) << 16) | (o0 + (uint32_t)jj);
-          const uint32_t cb = keep_bits(make_uint4(r4[0], r4[1], r4[2], r4[3]));
+            for (int jj = 0; jj < 8; ++jj) {
+              const uint32_t raw = (r4[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu;
+              const uint32_t mag = raw & 0x7FFFu;
+              const uint32_t rk = (raw >> 15) ? sel::kExact + (mag - sel::kMagLo)
+                                              : sel::kMagLo + sel::kExact - 1u - mag;
+              const bool ok = ((lb >> jj) & 1u) && mag >= sel::kMagLo &&
+                              mag < sel::kMagLo + sel::kExact && rk <= rho_s;
+              cb |= (ok ? 1u : 0u) << jj;
+              e[jj] = ((0xFFFFu - (rk & 0xFFFFu)) << 16) | (o0 + (uint32_t)jj);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t pm = (((lb >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) |
+                                  (((lb >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+              r4[q] = bfi(pm, r4[q], 0x80008000u);  // illegal -> -0, below the boundary
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+              e[jj] = (((r4[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu) << 16) | (o0 + (uint32_t)jj);
+            cb = keep_bits(make_uint4(r4[0], r4[1], r4[2], r4[3]));
+          }
+          if (write_keep) {
+            keep_bytes[st * 64] = (uint8_t)cb;
+            ext_cnt += (uint32_t)__popc(cb);
+          }
           if (ballot(cb != 0u)) f(e, cb);
         }
       }
@@ -615,7 +668,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   auto classify = [&](uint32_t e) __attribute__((always_inline)) {
     if (e > e_gt) {
       ++gt;
-      mgt += wtab[tab_base - (e >> 16)];
+      mgt += tabw[tab_base - (e >> 16)];
     } else {
       ++ties;
     }
@@ -636,7 +689,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if ((cb >> k) & 1u) classify(e[k]);
-    });
+    }, true);
+    if (ext) pcnt = uni(wave_reduce<OpSum>(ext_cnt));
   } else if (long_pool) {
     walk_a(std::integral_constant<int, 4>{});
   } else {
@@ -777,7 +831,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       qv[k] = 0.0;
       if ((kb >> k) & 1u) {
         const int id = (int)(sl.wb + (e[k] & 0xFFFFu));
-        const double q = wtab[tab_base - (e[k] >> 16)] * inv_wp;
+        const double q = tabw[tab_base - (e[k] >> 16)] * inv_wp;
         qv[k] = q;
         lane_sum += q;
         const float qf = (float)q;
@@ -830,7 +884,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   if (direct) {
     direct_walk([&](const uint32_t (&e)[8], uint32_t cb) {
       emit(std::integral_constant<int, 8>{}, e, cb);
-    });
+    }, false);
   } else if (long_pool) {
     walk_d(std::integral_constant<int, 4>{});
   } else {
@@ -848,7 +902,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   if (SAMPLE) {
     double last_q = 0.0;
     if (a.logprobs) {
-      const double last_pos_q = last_e == ~0u ? 0.0 : wtab[tab_base - (last_e >> 16)] * inv_wp;
+      const double last_pos_q = last_e == ~0u ? 0.0 : tabw[tab_base - (last_e >> 16)] * inv_wp;
       last_q = last_token_q(last_pos_id, last_pos_q, last_id);
     }
     if (lane == 0) {
