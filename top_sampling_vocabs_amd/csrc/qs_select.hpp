@@ -222,7 +222,27 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const int32_t raw_max =
       (int32_t)uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u)) - 0x8000;
   par ^= 1;
-  if (n_legal == 0u) return false;  // the general path reports the empty row
+  // an empty row, or a legal +inf or positive NaN (the largest legal bits):
+  // the row error is reported here (the empty check comes first)
+  if (n_legal == 0u || raw_max >= 0x7F80) {
+    if (mask_row && sl.we > sl.wb)
+      for (int i = (sl.wb >> 5) + lane; i < ((sl.we + 31) >> 5); i += 64) mask_row[i] = 0u;
+    if (dense_row)
+      for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
+    if (tid == 0) {
+      a.status[r] = n_legal == 0u ? QS_ROW_EMPTY : QS_ROW_NONFINITE;
+      if (SAMPLE) {
+        a.tokens[r] = -1;
+        if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
+      }
+      if (a.cand_count) a.cand_count[r] = 0;
+      if (a.dbg) {
+        a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
+        a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
+      }
+    }
+    return true;
+  }
   if (SAMPLE && !a.uniforms) u_bits = philox_u24(seed_in, u_bits);
 
   // -- runs of 16 values ----------------------------------------------------------------
