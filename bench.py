@@ -68,6 +68,9 @@ def parse():
                     help="instead of the headline line, print one line timing the path "
                          "switches (the Qrita page's ablation runs) on the headline "
                          "workload and at the page's ablation shape")
+    ap.add_argument("--outliers", type=int, default=0, metavar="N",
+                    help="set N random ids of every row to -1000 and make them legal (a "
+                         "logit bias of -1000 on a few tokens), on top of the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, also run plain device copies of the "
                          "logits (known bytes) so counter runs can scale FETCH/WRITE sizes")
@@ -649,6 +652,9 @@ def main():
     base = workloads.make(cfg)
     sets = [base] + [workloads.make(cfg, seed=workloads.BASE_SEED + cfg + 1000 * i)
                      for i in range(1, args.sets)]
+    if args.outliers:
+        for i, w in enumerate(sets):
+            workloads.add_outliers(w, args.outliers, -1000.0, seed=workloads.BASE_SEED + 77 + i)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     preps = [Prepared(lib, w, args.cand_cap, args.flags, stream) for w in sets[:1]]
     preps += [Prepared(lib, w, args.cand_cap, args.flags, stream, workspace=preps[0].ws)
@@ -743,7 +749,9 @@ def main():
         "vs_baseline": None,
         "dtype": base.dtype,
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[cfg], "batch_rows": B, "vocab": base.V,
+        "config": {"workload": WORKLOAD_NAMES[cfg] + (f", {args.outliers} ids/row at -1000"
+                                                       if args.outliers else ""),
+                   "batch_rows": B, "vocab": base.V,
                    "input_sets": len(sets), "bytes_read_per_step": bytes_read,
                    "cand_cap": args.cand_cap,
                    "launch": launch_mode, "parallelism": "single GPU"},

@@ -582,3 +582,38 @@ def test_histogram_far_and_negative_boundaries(qs):
     on_path = [0, 1, 2, 3, 5, 6, 7]
     assert (dbg[on_path, 0] == 0).all() and (dbg[on_path, 1] == 0).all(), dbg.tolist()
     assert dbg[4, 1] >= 1 or dbg[4, 0] != 0, dbg.tolist()   # zeros between the signs
+
+
+def test_histogram_huge_negative_logits(qs):
+    """bf16 rows holding a few huge negative logits among ordinary ones (a
+    logit bias of -1000, legal -inf tokens, values below -512): their weights
+    are below 2^-60 of the row's mass, so the value-histogram path leaves them
+    out of its sums and keeps these rows (no search rounds), top-k and top-p
+    alike; a large temperature, which gives them weight, sends the row to the
+    truncation path; a legal negative NaN is a row error. All must match the
+    oracle."""
+    rng = np.random.default_rng(99)
+    B, V = 10, 30000
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    for r in range(B):
+        ids = rng.choice(V, size=12, replace=False)
+        z[r, ids[:6]] = -1000.0
+        z[r, ids[6:9]] = -np.inf
+        z[r, ids[9:]] = -600.0
+    T = np.array([1.0, 1.0, 0.7, 1.3, 1.0, 1.0, 1.0, 400.0, 1.0, 1.0], np.float32)
+    k = np.array([50, 0, 200, 0, 20, 0, 1000, 0, 0, 0], np.int32)
+    p = np.array([1.0, 0.9, 0.95, 0.99, 0.8, 0.5, 0.9, 0.9, 0.97, 0.9], np.float32)
+    bits = rng.random((B, V)) < 0.3
+    for r in range(B):
+        bits[r, np.nonzero(z[r] < -500)[0]] = True   # the outliers are legal
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    w.logits[9, int(np.nonzero(bits[9])[0][5])] = 0xFFC1   # a legal negative NaN
+    rep, out = check_workload(qs, w, seed=4, cand_cap=V)
+    dbg = out["debug"].cpu().numpy()
+    st = out["status"].cpu().numpy()
+    assert st[9] == oracle.ROW_NONFINITE
+    on_path = [0, 1, 2, 3, 4, 5, 6, 8]
+    assert (dbg[on_path, 0] == 0).all() and (dbg[on_path, 1] == 0).all(), dbg.tolist()

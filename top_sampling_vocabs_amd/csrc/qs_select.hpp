@@ -222,15 +222,14 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   const int32_t raw_max =
       (int32_t)uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][1] : 0u)) - 0x8000;
   par ^= 1;
-  // an empty row, or a legal +inf or positive NaN (the largest legal bits):
-  // the row error is reported here (the empty check comes first)
-  if (n_legal == 0u || raw_max >= 0x7F80) {
+  // a row error reported here: zero outputs, no token, no draw
+  auto row_error = [&](int code) {
     if (mask_row && sl.we > sl.wb)
       for (int i = (sl.wb >> 5) + lane; i < ((sl.we + 31) >> 5); i += 64) mask_row[i] = 0u;
     if (dense_row)
       for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
     if (tid == 0) {
-      a.status[r] = n_legal == 0u ? QS_ROW_EMPTY : QS_ROW_NONFINITE;
+      a.status[r] = code;
       if (SAMPLE) {
         a.tokens[r] = -1;
         if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
@@ -241,6 +240,11 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
       }
     }
+  };
+  // an empty row, or a legal +inf or positive NaN (the largest legal bits)
+  // (the empty check comes first)
+  if (n_legal == 0u || raw_max >= 0x7F80) {
+    row_error(n_legal == 0u ? QS_ROW_EMPTY : QS_ROW_NONFINITE);
     return true;
   }
   if (SAMPLE && !a.uniforms) u_bits = philox_u24(seed_in, u_bits);
@@ -324,14 +328,13 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
       }
     }
   }
-  uint32_t c_excl, n_ex, n_tiny;
-  bool huge_any;
+  uint32_t c_excl, n_ex, n_tiny, n_huge;
   double m_excl, w_f;
   {
     const uint32_t ci = scan_incl_u32(ct);
     const double mi = scan_incl_f64(mt);
     const uint32_t ts = wave_reduce<OpSum>(tiny);
-    const uint32_t hm = wave_reduce<OpMax>(huge);
+    const uint32_t hm = wave_reduce<OpSum>(huge);
     if (lane == 63) {
       red.v[par][w][0] = ci;
       const uint64_t b = __double_as_longlong(mi);
@@ -353,12 +356,40 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     w_f = uni(readlane_f64(tmi, kWaves - 1));
     n_ex = uni(readlane_u32(tci, kWaves - 1));
     n_tiny = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][3] : 0u));
-    huge_any = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][4] : 0u)) != 0u;
+    n_huge = uni(wave_reduce<OpSum>(act16 ? red.v[par][lane][4] : 0u));
     par ^= 1;
+  }
+  // Legal values of magnitude >= 512 can only be negative here (the maximum is
+  // below 512): -inf, finite values <= -512 and negative NaN. A negative NaN
+  // is a row error; the others weigh at most exp((-512 - m) / T) each, and
+  // when all of them together stay below 2^-60 of the mass they are left out
+  // of every sum (as in the oracle's fp64 sums, where they change nothing
+  // beyond the last place) and never kept. Otherwise the general path.
+  if (n_huge) {
+    uint32_t nan2 = 0u;  // largest raw bits as unsigned: negative NaNs above -inf
+    static_for<0, NL>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        nan2 = bits_of(__builtin_elementwise_max(as_u2(nan2), as_u2(r4[q])));
+    });
+    const uint32_t nmax = max(nan2 & 0xFFFFu, nan2 >> 16);
+    if (lane == 0) red.v[par][w][0] = 0u;
+    const uint64_t bad = ballot(nmax > 0xFF80u);
+    if (lane == 0 && bad) red.v[par][w][0] = 1u;
+    __syncthreads();
+    const bool neg_nan = uni(wave_reduce<OpMax>(act16 ? red.v[par][lane][0] : 0u)) != 0u;
+    par ^= 1;
+    if (neg_nan) {
+      row_error(QS_ROW_NONFINITE);
+      return true;
+    }
+    if (!((double)n_huge * exp64((-512.0 - m) * invT) <= 0x1p-60)) return false;
   }
   // the tiny values lie below every positive exact value: with a positive
   // maximum they only enter the total mass, within a bound
-  if (huge_any || n_ex + n_tiny != n_legal) return false;
+  if (n_ex + n_tiny + n_huge != n_legal) return false;
   const uint32_t n_fin = n_legal;
   // the tiny values' mass: n_tiny w(0), within n_tiny (w(2^-24) - w(-2^-24))
   double w_f_err = 0.0;

@@ -207,3 +207,22 @@ def bytes_read(w):
     if w.bitmask is not None:
         total += w.bitmask.size * 4
     return total
+
+
+def add_outliers(w, n, value, seed):
+    """Set n distinct random ids of every row to `value` (in the workload's
+    dtype) and make them legal: the effect of a per-token logit bias that
+    pushes a few tokens far down. Modifies w in place."""
+    rng = np.random.default_rng(seed)
+    B, V = w.logits.shape
+    if w.dtype == "bf16":
+        bits = np.frombuffer(np.float32(value).tobytes(), np.uint32)[0] >> 16
+        v = np.uint16(bits)
+    else:
+        v = np.float32(value)
+    for r in range(B):
+        ids = rng.choice(V, size=n, replace=False)
+        w.logits[r, ids] = v
+        if w.bitmask is not None:
+            for t in ids:
+                w.bitmask[r, t >> 5] |= np.uint32(1) << np.uint32(t & 31)
