@@ -148,7 +148,7 @@ class Prepared:
 # kernels live in files of their own and do not change it)
 FILTER_SOURCES = ("qs_device.hpp", "qs_filter.hpp", "qs_filter_bf16.hip", "qs_filter_f32.hip",
                   "qs_launch.hpp", "qs_select.hpp", "qs_stream.hpp", "qs_merge.hpp",
-                  "qs_bins.hpp", "qs_chunk.hpp", "qs_chunk.hip")
+                  "qs_bins.hpp", "qs_chunk.hpp", "qs_chunk.hip", "qs_proc.hpp")
 
 
 def source_digest():

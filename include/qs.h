@@ -261,6 +261,67 @@ QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* tar
                    const double* u_resample, int32_t* tokens, int32_t* accepted,
                    int32_t* row_status, void* stream);
 
+/* Logit processors applied inside qs_sample_processed / qs_filter_mask_processed
+ * (page "Sampling 系统设计：从 logits 到可控生成", repetition-penalty and
+ * LogitsProcessor sections: history-dependent processors edit the logits
+ * before the selection). Per row r the logits the selection sees are those
+ * qs_apply_penalties and then qs_apply_logit_bias would leave (same formulas,
+ * float32 operations and dtype rounding), but the caller's logits are only
+ * read: the edited values exist only inside the kernel.
+ *
+ * Penalties (all four pointers NULL: none): history [B][history_cap] int32
+ *   token ids, history_count [B] int32, repetition_penalty and
+ *   presence_penalty [B] float32, frequency_penalty [B] float32 or NULL (0).
+ * Bias (all three pointers NULL: none): bias_ids [B][bias_cap] int32,
+ *   bias_values [B][bias_cap] float32, bias_count [B] int32.
+ * A row whose processor arguments qs_apply_penalties or qs_apply_logit_bias
+ * would flag, or whose history and bias lists hold more than 4096 distinct
+ * in-range ids together, gets QS_ROW_BAD_PARAM and no outputs (no token, no
+ * draw). */
+typedef struct QsProcessors {
+  const int32_t* history;
+  int64_t history_cap;
+  const int32_t* history_count;
+  const float* repetition_penalty;
+  const float* presence_penalty;
+  const float* frequency_penalty;
+  const int32_t* bias_ids;
+  const float* bias_values;
+  int64_t bias_cap;
+  const int32_t* bias_count;
+} QsProcessors;
+
+/* Bytes of caller workspace a processed call needs: B rows of
+ * align256(V * element size) (a row that the kernel cannot settle from its
+ * registers is rewritten there with its processors applied, and selected
+ * from that copy); V at most 155648. 0 for invalid arguments. */
+QS_API size_t qs_processors_workspace_bytes(int64_t B, int64_t V, int dtype);
+
+/* qs_sample / qs_filter_mask with logit processors `proc` (non-NULL) applied
+ * to every row first, in the same launch. Arguments, outputs and statuses are
+ * those of qs_sample / qs_filter_mask, with `workspace` sized by
+ * qs_processors_workspace_bytes (256-byte aligned; QS_ERR_WORKSPACE before
+ * any HIP call otherwise) and V <= 155648 (QS_ERR_INVALID_ARG otherwise). */
+QS_API int qs_sample_processed(const void* logits, int dtype, int64_t B, int64_t V,
+              int64_t row_stride, const float* temperature,
+              const int32_t* top_k, const float* top_p,
+              const uint32_t* bitmask, int64_t bitmask_stride,
+              const uint64_t* seed, uint64_t* offset, const double* uniforms,
+              int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+              float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+              uint32_t flags, const QsProcessors* proc, void* workspace,
+              size_t workspace_bytes, void* stream);
+QS_API int qs_filter_mask_processed(const void* logits, int dtype, int64_t B, int64_t V,
+                   int64_t row_stride, const float* temperature,
+                   const int32_t* top_k, const float* top_p,
+                   const uint32_t* bitmask, int64_t bitmask_stride,
+                   uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
+                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
+                   int32_t* row_status, int32_t* debug_stats, uint32_t flags,
+                   const QsProcessors* proc, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Repetition and presence penalties over each row's history, applied in place
  * to the logits before qs_filter_mask / qs_sample (page "Sampling 系统设计：从
  * logits 到可控生成", repetition-penalty section: a history-dependent logits

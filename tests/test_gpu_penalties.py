@@ -144,3 +144,99 @@ def test_logit_bias_bitwise(qs, dtype, cap):
     ref = want.view(np.uint16) if dtype == "bf16" else want.view(np.uint32)
     diff = np.argwhere(got != ref)
     assert len(diff) == 0, diff[:10]
+
+
+def _edited_workload(w, hist, hcnt, rep, pres, freq, bids, bvals, bcnt):
+    """The oracle's composition: penalties, then the bias, on the host rows;
+    a row either processor flags is BAD_PARAM for the fused call."""
+    import dataclasses
+    st_p, z1 = oracle.apply_penalties_batch(w.logits, w.dtype, hist, hcnt, rep, pres, freq)
+    st_b, z2 = oracle.apply_logit_bias_batch(z1, w.dtype, bids, bvals, bcnt)
+    bad = (st_p != oracle.ROW_OK) | (st_b != oracle.ROW_OK)
+    return dataclasses.replace(w, logits=z2), bad
+
+
+@pytest.mark.parametrize("case", ["bf16_resident", "bf16_switch", "f32", "bf16_greedy"])
+def test_processed_matches_oracle(qs, case):
+    """qs_sample_processed / qs_filter_mask_processed: penalties and bias
+    applied inside the call (the caller's logits untouched) give the outputs
+    of the oracle's filter and draw on the oracle's edited rows (penalties,
+    then bias), bit for bit for masks and lists; rows with invalid processor
+    arguments (either processor's, or too many edited ids) are BAD_PARAM.
+    bf16 rows held in registers patch the edited tokens in place; fp32 rows,
+    switched runs and greedy rows are selected from an edited copy in the
+    workspace."""
+    import torch
+    rng = np.random.default_rng({"bf16_resident": 1, "bf16_switch": 2, "f32": 3,
+                                 "bf16_greedy": 4}[case])
+    dtype = "f32" if case == "f32" else "bf16"
+    B, V = 24, (20000 if dtype == "f32" else 40000)
+    w = workloads.make(3 if dtype == "bf16" else 2, B=B, V=V, seed=int(rng.integers(1 << 30)))
+    if case == "bf16_greedy":
+        w.T[::2] = 0.0
+    hist, hcnt = _history(rng, B, V, 700)
+    rep = rng.choice([1.0, 1.3, 0.7, 2.0], B).astype(np.float32)
+    pres = rng.choice([0.0, 0.4, -0.2], B).astype(np.float32)
+    freq = rng.choice([0.0, 0.1, 0.5], B).astype(np.float32)
+    bcap = 300
+    bids = np.stack([rng.choice(V, bcap, replace=False) for _ in range(B)]).astype(np.int32)
+    bids[:, ::17] = -5                              # out of range: ignored
+    bvals = rng.normal(0, 2, (B, bcap)).astype(np.float32)
+    bvals[:, ::5] = 40.0                            # pushed to the top
+    bcnt = rng.integers(0, bcap + 1, B).astype(np.int32)
+    # invalid rows: a bad repetition penalty, a repeated bias id, a non-finite bias
+    rep[3] = 0.0
+    bids[4, 1] = bids[4, 0] if bids[4, 0] >= 0 else 7
+    bids[4, 0] = bids[4, 1]
+    bcnt[4] = max(bcnt[4], 2)
+    bvals[5, 0] = np.inf
+    bcnt[5] = max(bcnt[5], 1)
+    ew, bad = _edited_workload(w, hist, hcnt, rep, pres, freq, bids, bvals, bcnt)
+    d = to_device(w)
+    before = d["logits"].clone()
+    P = {k: torch.from_numpy(v).cuda() for k, v in (
+        ("history", hist), ("history_count", hcnt), ("repetition", rep), ("presence", pres),
+        ("frequency", freq), ("bias_ids", bids), ("bias_values", bvals), ("bias_count", bcnt))}
+    uni = np.random.default_rng(8).random(B)
+    flags = qs.FLAG_STREAM if case == "bf16_switch" else 0
+    out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                    uniforms=torch.from_numpy(uni).cuda(), keep_mask=True, cand_cap=V,
+                    dense=True, debug=True, logprobs=True, flags=flags, processors=P)
+    fm = qs.filter_mask(d["logits"], d["T"], d["k"], d["p"], d["bitmask"], cand_cap=V,
+                        flags=flags, processors=P)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d["logits"])        # the caller's logits are only read
+    st = out["status"].cpu().numpy()
+    assert (st[bad] == oracle.ROW_BAD_PARAM).all(), (np.nonzero(bad)[0], st[bad])
+    assert bad[[3, 4, 5]].all()
+    good = [r for r in range(B) if not bad[r]]
+    res = oracle.filter_batch(ew.logits, ew.dtype, ew.T, ew.k, ew.p, ew.bitmask, rows=good)
+    rep_ = Report()
+    compare_filter(ew, res, out, good, rep_)
+    compare_tokens(res, out["tokens"], good, rep_, uniforms=uni)
+    rep_.check()
+    assert np.array_equal(fm["keep_mask"].cpu().numpy(), out["keep_mask"].cpu().numpy())
+    if case == "bf16_resident":
+        dbg = out["debug"].cpu().numpy()
+        assert (dbg[good, 0] == 0).all() and (dbg[good, 1] == 0).all(), dbg[good].tolist()
+
+
+def test_processed_too_many_ids(qs):
+    """More than 4096 distinct edited tokens in a row: BAD_PARAM; the other
+    rows are unaffected."""
+    import torch
+    B, V = 4, 30000
+    w = workloads.make(3, B=B, V=V)
+    hist = np.tile(np.arange(5000, dtype=np.int32), (B, 1))
+    hcnt = np.array([5000, 100, 0, 4096], np.int32)
+    rep = np.full(B, 1.5, np.float32)
+    pres = np.zeros(B, np.float32)
+    d = to_device(w)
+    P = {k: torch.from_numpy(v).cuda() for k, v in (
+        ("history", hist), ("history_count", hcnt), ("repetition", rep), ("presence", pres))}
+    out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
+                    uniforms=torch.full((B,), 0.5, dtype=torch.float64, device="cuda"),
+                    keep_mask=True, processors=P)
+    torch.cuda.synchronize()
+    st = out["status"].cpu().numpy()
+    assert st[0] == oracle.ROW_BAD_PARAM and (st[1:] != oracle.ROW_BAD_PARAM).all(), st

@@ -8,6 +8,7 @@ stream. The library is loaded on first use; calls raise if it is missing.
 
 from ._lib import (  # noqa: F401
     filter_mask, sample, sample_noalloc, argmax, spec_verify, apply_penalties, apply_logit_bias, top_logprobs,
+    processors_workspace_for,
     load, workspace_bytes, workspace_for,
     LIB_PATH,
     ROW_OK, ROW_EMPTY, ROW_ALL_NEG_INF, ROW_NONFINITE, ROW_BAD_PARAM,

@@ -38,6 +38,7 @@ FLAG_BINARY_PIVOT = 16
 SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("qs_workspace_bytes", "qs_filter_mask", "qs_sample", "qs_sample_noalloc", "qs_argmax",
+           "qs_processors_workspace_bytes", "qs_sample_processed", "qs_filter_mask_processed",
            "qs_spec_verify",
            "qs_apply_penalties", "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
 
@@ -48,6 +49,15 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int
 _u32 = ctypes.c_uint32
 _sz = ctypes.c_size_t
+
+
+class QsProcessors(ctypes.Structure):
+    """The C struct QsProcessors: device pointers of the logit processors."""
+    _fields_ = [("history", ctypes.c_void_p), ("history_cap", ctypes.c_int64),
+                ("history_count", ctypes.c_void_p), ("repetition_penalty", ctypes.c_void_p),
+                ("presence_penalty", ctypes.c_void_p), ("frequency_penalty", ctypes.c_void_p),
+                ("bias_ids", ctypes.c_void_p), ("bias_values", ctypes.c_void_p),
+                ("bias_cap", ctypes.c_int64), ("bias_count", ctypes.c_void_p)]
 
 
 def load(path=LIB_PATH):
@@ -80,6 +90,12 @@ def load(path=LIB_PATH):
         _p, _sz, _p]
     lib.qs_sample_noalloc.restype = _i32
     lib.qs_sample_noalloc.argtypes = lib.qs_sample.argtypes[:-3] + [_p]
+    lib.qs_processors_workspace_bytes.restype = _sz
+    lib.qs_processors_workspace_bytes.argtypes = [_i64, _i64, _i32]   # B, V, dtype
+    lib.qs_sample_processed.restype = _i32
+    lib.qs_sample_processed.argtypes = lib.qs_sample.argtypes[:-3] + [_p, _p, _sz, _p]
+    lib.qs_filter_mask_processed.restype = _i32
+    lib.qs_filter_mask_processed.argtypes = lib.qs_filter_mask.argtypes[:-3] + [_p, _p, _sz, _p]
     lib.qs_argmax.restype = _i32
     lib.qs_argmax.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _p, _p]
     lib.qs_spec_verify.restype = _i32
@@ -178,7 +194,7 @@ def _workspace_args(workspace, logits, cand_cap):
 
 
 def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
-                dense=False, debug=False, flags=0, workspace=None):
+                dense=False, debug=False, flags=0, workspace=None, processors=None):
     """Kept-candidate mask and renormalised probabilities for every row.
 
     logits [B, V] float32 / bfloat16 (CUDA); temperature, top_p float32 [B];
@@ -208,21 +224,75 @@ def filter_mask(logits, temperature, top_k, top_p, bitmask=None, *, cand_cap=0,
         out["dense"] = torch.empty((B, V), dtype=torch.float32, device=dev)
     if debug:
         out["debug"] = torch.empty((B, 4), dtype=torch.int32, device=dev)
+    args = (_ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
+            _ptr(temperature), _ptr(top_k), _ptr(top_p),
+            _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
+            _ptr(out["keep_mask"]), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
+            _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
+            _ptr(out["status"]), _ptr(out.get("debug")), int(flags))
+    if processors is not None:
+        pr, ws = _processors_args(processors, logits, workspace)
+        rc = lib.qs_filter_mask_processed(*args, ctypes.byref(pr), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(dev))
+        _status(rc, "qs_filter_mask_processed")
+        return out
     ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
-    rc = lib.qs_filter_mask(
-        _ptr(logits), _dtype_code(logits), B, V, logits.stride(0),
-        _ptr(temperature), _ptr(top_k), _ptr(top_p),
-        _ptr(bitmask), 0 if bitmask is None else bitmask.stride(0),
-        _ptr(out["keep_mask"]), _ptr(out.get("cand_ids")), _ptr(out.get("cand_probs")),
-        _ptr(out.get("cand_count")), int(cand_cap), _ptr(out.get("dense")),
-        _ptr(out["status"]), _ptr(out.get("debug")), int(flags), ws_p, ws_n, _stream(dev))
+    rc = lib.qs_filter_mask(*args, ws_p, ws_n, _stream(dev))
     _status(rc, "qs_filter_mask")
     return out
 
 
+def _processors_args(proc, logits, workspace):
+    """QsProcessors from a dict of device tensors: history [B, cap] int32,
+    history_count [B] int32, repetition / presence [B] float32, frequency [B]
+    float32 (optional); bias_ids [B, cap] int32, bias_values [B, cap] float32,
+    bias_count [B] int32. Either group may be absent. Also returns a workspace
+    of processors_workspace_bytes (the given one, or a new one)."""
+    import torch
+    lib = load()
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    dev = logits.device
+    pr = QsProcessors()
+    keep = []
+    if proc.get("history") is not None:
+        h = proc["history"]
+        if h.dim() != 2 or h.shape[0] != B or h.dtype != torch.int32 or not h.is_contiguous():
+            raise ValueError("history: need a contiguous [B, cap] int32 tensor")
+        _check_rowvec(proc["history_count"], B, torch.int32, "history_count")
+        _check_rowvec(proc["repetition"], B, torch.float32, "repetition")
+        _check_rowvec(proc["presence"], B, torch.float32, "presence")
+        if proc.get("frequency") is not None:
+            _check_rowvec(proc["frequency"], B, torch.float32, "frequency")
+        pr.history, pr.history_cap = _ptr(h), int(h.shape[1])
+        pr.history_count = _ptr(proc["history_count"])
+        pr.repetition_penalty = _ptr(proc["repetition"])
+        pr.presence_penalty = _ptr(proc["presence"])
+        pr.frequency_penalty = _ptr(proc.get("frequency"))
+    if proc.get("bias_ids") is not None:
+        bi, bv = proc["bias_ids"], proc["bias_values"]
+        if bi.dim() != 2 or bi.shape[0] != B or bi.dtype != torch.int32 or bv.shape != bi.shape \
+                or bv.dtype != torch.float32 or not bi.is_contiguous() or not bv.is_contiguous():
+            raise ValueError("bias_ids / bias_values: need contiguous [B, cap] int32 / float32")
+        _check_rowvec(proc["bias_count"], B, torch.int32, "bias_count")
+        pr.bias_ids, pr.bias_values, pr.bias_cap = _ptr(bi), _ptr(bv), int(bi.shape[1])
+        pr.bias_count = _ptr(proc["bias_count"])
+    need = lib.qs_processors_workspace_bytes(B, V, _dtype_code(logits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return pr, workspace
+
+
+def processors_workspace_for(logits):
+    """A device workspace for processed calls on these logits."""
+    import torch
+    n = load().qs_processors_workspace_bytes(int(logits.shape[0]), int(logits.shape[1]),
+                                             _dtype_code(logits))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=logits.device)
+
+
 def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset=None,
            uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False,
-           logprobs=False, flags=0, workspace=None):
+           logprobs=False, flags=0, workspace=None, processors=None):
     """Filter and draw one token per row.
 
     seed, offset: int64 [B] CUDA tensors holding the uint64 RNG state; offset is
@@ -231,9 +301,12 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
     return the log-probability of each drawn token under the distribution it
     was drawn from (float32 [B]). Returns a dict with tokens [B], status [B]
     and the optional outputs of filter_mask. workspace as for filter_mask.
+    processors: a dict of logit-processor tensors (see _processors_args),
+    applied inside the call (qs_sample_processed); the logits are only read.
     """
     return _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms,
-                   keep_mask, cand_cap, dense, debug, logprobs, flags, workspace, False)
+                   keep_mask, cand_cap, dense, debug, logprobs, flags, workspace, False,
+                   processors)
 
 
 def sample_noalloc(logits, temperature, top_k, top_p, bitmask=None, *, seed=None,
@@ -247,7 +320,7 @@ def sample_noalloc(logits, temperature, top_k, top_p, bitmask=None, *, seed=None
 
 
 def _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms, keep_mask,
-            cand_cap, dense, debug, logprobs, flags, workspace, noalloc):
+            cand_cap, dense, debug, logprobs, flags, workspace, noalloc, processors=None):
     import torch
     lib = load()
     B, V = _check_logits(logits, bitmask)
@@ -287,6 +360,12 @@ def _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms, 
     if noalloc:
         rc = lib.qs_sample_noalloc(*args, _stream(dev))
         _status(rc, "qs_sample_noalloc")
+        return out
+    if processors is not None:
+        pr, ws = _processors_args(processors, logits, workspace)
+        rc = lib.qs_sample_processed(*args, ctypes.byref(pr), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(dev))
+        _status(rc, "qs_sample_processed")
         return out
     ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
     rc = lib.qs_sample(*args, ws_p, ws_n, _stream(dev))

@@ -14,6 +14,7 @@
 #include "qs_aux.hpp"
 #include "qs_chunk.hpp"
 #include "qs_launch.hpp"
+#include "qs_proc.hpp"
 
 namespace {
 
@@ -33,6 +34,13 @@ bool chunked_rows(int64_t V, int dtype) {
 size_t ws_bytes(int64_t B, int64_t V, int dtype) {
   if (B == 0 || !chunked_rows(V, dtype)) return 0;
   return qs::chunk::workspace_bytes(B, V);
+}
+// a processed call: one 256-byte aligned workspace row per row
+size_t proc_row_bytes(int64_t V, int dtype) {
+  return ((size_t)V * (dtype == QS_F32 ? 4 : 2) + 255) & ~(size_t)255;
+}
+size_t proc_ws_bytes(int64_t B, int64_t V, int dtype) {
+  return (size_t)B * proc_row_bytes(V, dtype);
 }
 
 // Shared checks of the logits / bitmask description.
@@ -59,7 +67,7 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
                   float* cand_probs,
                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
                   int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream, const QsProcessors* proc = nullptr) {
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
   if (rc != QS_OK) return rc;
   if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION | QS_FLAG_PIVOT_SEARCH |
@@ -81,7 +89,25 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
       !aligned(debug_stats, 4) || !aligned(tokens, 4) || !aligned(logprobs, 4) ||
       !aligned(seed, 8) || !aligned(offset, 8) || !aligned(uniforms, 8))
     return QS_ERR_INVALID_ARG;
-  const size_t need = ws_bytes(B, V, dtype);
+  if (proc) {
+    // every pointer of a group or none; V within the in-kernel table
+    const bool hist_any = proc->history || proc->history_count || proc->repetition_penalty ||
+                          proc->presence_penalty || proc->frequency_penalty;
+    const bool hist_all = proc->history && proc->history_count && proc->repetition_penalty &&
+                          proc->presence_penalty;
+    const bool bias_any = proc->bias_ids || proc->bias_values || proc->bias_count;
+    const bool bias_all = proc->bias_ids && proc->bias_values && proc->bias_count;
+    if (V > qs::proc::kMaxV || (hist_any && !hist_all) || (bias_any && !bias_all))
+      return QS_ERR_INVALID_ARG;
+    if (hist_all && (proc->history_cap < 0 || proc->history_cap > kMaxV * 64)) return QS_ERR_INVALID_ARG;
+    if (bias_all && (proc->bias_cap < 0 || proc->bias_cap > kMaxV * 64)) return QS_ERR_INVALID_ARG;
+    if (!aligned(proc->history, 4) || !aligned(proc->history_count, 4) ||
+        !aligned(proc->repetition_penalty, 4) || !aligned(proc->presence_penalty, 4) ||
+        !aligned(proc->frequency_penalty, 4) || !aligned(proc->bias_ids, 4) ||
+        !aligned(proc->bias_values, 4) || !aligned(proc->bias_count, 4))
+      return QS_ERR_INVALID_ARG;
+  }
+  const size_t need = proc ? proc_ws_bytes(B, V, dtype) : ws_bytes(B, V, dtype);
   if (need > 0) {
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return QS_ERR_WORKSPACE;
   }
@@ -114,8 +140,28 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.ws_mass = nullptr;
   a.ws_cands = nullptr;
   a.S = 0;
+  a.p_on = 0;
+  a.p_hist = nullptr; a.p_hist_cap = 0; a.p_hist_count = nullptr;
+  a.p_rep = nullptr; a.p_pres = nullptr; a.p_freq = nullptr;
+  a.p_bias_ids = nullptr; a.p_bias_vals = nullptr; a.p_bias_cap = 0; a.p_bias_count = nullptr;
+  a.p_copy = nullptr; a.p_copy_bytes = 0;
+  if (proc) {
+    a.p_on = 1;
+    if (proc->history) {
+      a.p_hist = proc->history; a.p_hist_cap = proc->history_cap;
+      a.p_hist_count = proc->history_count;
+      a.p_rep = proc->repetition_penalty; a.p_pres = proc->presence_penalty;
+      a.p_freq = proc->frequency_penalty;
+    }
+    if (proc->bias_ids) {
+      a.p_bias_ids = proc->bias_ids; a.p_bias_vals = proc->bias_values;
+      a.p_bias_cap = proc->bias_cap; a.p_bias_count = proc->bias_count;
+    }
+    a.p_copy = static_cast<uint8_t*>(workspace);
+    a.p_copy_bytes = (int64_t)proc_row_bytes(V, dtype);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (need > 0 && flags == 0u) {
+  if (!proc && need > 0 && flags == 0u) {
     // long bf16 rows: the chunk kernel streams every row first, the filter
     // kernel then settles each row from the chunks' candidates (path switches
     // skip it)
@@ -170,6 +216,43 @@ void* scratch_address() {
 }  // namespace
 
 extern "C" {
+
+size_t qs_processors_workspace_bytes(int64_t B, int64_t V, int dtype) {
+  if (B < 0 || B > kMaxB || V < 1 || V > qs::proc::kMaxV || (dtype != QS_F32 && dtype != QS_BF16))
+    return 0;
+  return proc_ws_bytes(B, V, dtype);
+}
+
+int qs_sample_processed(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                        const float* temperature, const int32_t* top_k, const float* top_p,
+                        const uint32_t* bitmask, int64_t bitmask_stride, const uint64_t* seed,
+                        uint64_t* offset, const double* uniforms, int32_t* tokens,
+                        float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+                        float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+                        float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+                        uint32_t flags, const QsProcessors* proc, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!proc) return QS_ERR_INVALID_ARG;
+  return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
+                       keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs,
+                       row_status, debug_stats, flags, workspace, workspace_bytes, stream, proc);
+}
+
+int qs_filter_mask_processed(const void* logits, int dtype, int64_t B, int64_t V,
+                             int64_t row_stride, const float* temperature, const int32_t* top_k,
+                             const float* top_p, const uint32_t* bitmask, int64_t bitmask_stride,
+                             uint32_t* keep_mask, int32_t* cand_ids, float* cand_probs,
+                             int32_t* cand_count, int64_t cand_cap, float* dense_probs,
+                             int32_t* row_status, int32_t* debug_stats, uint32_t flags,
+                             const QsProcessors* proc, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!proc) return QS_ERR_INVALID_ARG;
+  return filter_common(false, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs,
+                       row_status, debug_stats, flags, workspace, workspace_bytes, stream, proc);
+}
 
 size_t qs_workspace_bytes(int64_t B, int64_t V, int dtype, int64_t cand_cap) {
   (void)cand_cap;

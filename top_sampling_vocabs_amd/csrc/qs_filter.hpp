@@ -45,6 +45,7 @@
 #include "qs_launch.hpp"
 #include "qs_stream.hpp"
 #include "qs_bins.hpp"
+#include "qs_proc.hpp"
 #include "../../include/qs.h"
 
 namespace qs {
@@ -127,6 +128,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
   __shared__ RowInfo info;
+  __shared__ uint32_t s_proc[20];  // logit processors: block-scan totals and a flag
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
   uint16_t* const pool_id = reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap);
@@ -165,7 +167,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       float* const dense_row = a.dense ? a.dense + (size_t)r * a.V : nullptr;
       if (select_row<SAMPLE, NL>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
                                  pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
-                                 info))
+                                 info, s_proc))
         return;
       __syncthreads();  // the general path reuses the LDS
     }
@@ -188,6 +190,78 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
 
   uint32_t* mask_row = a.keep_mask ? a.keep_mask + (size_t)r * W : nullptr;
   float* dense_row = a.dense ? a.dense + (size_t)r * V : nullptr;
+
+  // -- logit processors: the row is selected from an edited copy in the
+  //    workspace (its table in the pools' LDS, the biases in the stage) ---------
+  if (a.p_on) {
+    const proc::RowParams prm = proc::row_params(a, r);
+    const proc::Table pt = proc::table_at(pool_raw, &stage[0][0]);
+    static_assert(proc::kBytes <= kPoolBytes, "processor table");
+    const bool ok = prm.ok && proc::build(a, r, tid, prm, pt, s_proc + 16, s_proc);
+    if (!ok) {
+      if (mask_row)
+        for (int i = tid; i < W; i += kThreads) mask_row[i] = 0u;
+      if (dense_row)
+        for (int i = tid; i < V; i += kThreads) dense_row[i] = 0.0f;
+      if (tid == 0) {
+        a.status[r] = QS_ROW_BAD_PARAM;
+        if (SAMPLE) {
+          a.tokens[r] = -1;
+          if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
+        }
+        if (a.cand_count) a.cand_count[r] = 0;
+        if (a.dbg) {
+          a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
+          a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
+        }
+      }
+      return;
+    }
+    // copy in 16-byte pieces; the edited tokens of a piece are rewritten first
+    constexpr int kPT = 16 / (DT == 0 ? 4 : 2);  // tokens per piece
+    uint8_t* const dst = a.p_copy + (size_t)r * a.p_copy_bytes;
+    const int npieces = V / kPT;
+    for (int c = tid; c < npieces; c += kThreads) {
+      uint4 x = *reinterpret_cast<const uint4*>(sl.row + (size_t)c * 16);
+      const int e0 = c * kPT;
+      const uint32_t pb = (pt.bits[e0 >> 5] >> (e0 & 31)) & ((1u << kPT) - 1u);
+      if (pb) {
+        uint32_t r4[4] = {x.x, x.y, x.z, x.w};
+        for (int j = 0; j < kPT; ++j) {
+          if (!((pb >> j) & 1u)) continue;
+          const uint32_t rk = proc::rank_of(pt, (uint32_t)(e0 + j));
+          const int q = DT == 0 ? j : j >> 1;
+          const uint32_t sh = DT == 0 ? 0u : 16u * (uint32_t)(j & 1);
+          const uint32_t msk = DT == 0 ? 0xFFFFFFFFu : 0xFFFFu;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            if (qq == q) {
+              const uint32_t raw = (r4[qq] >> sh) & msk;
+              const uint32_t nv = proc::edit<DT>(raw, pt.count[rk], pt.bias[rk], prm.rep,
+                                                 prm.pres, prm.freq) & msk;
+              r4[qq] = (r4[qq] & ~(msk << sh)) | (nv << sh);
+            }
+          }
+        }
+        x = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)c * 16) = x;
+    }
+    // the tokens past the last whole piece, one by one
+    for (int e = npieces * kPT + tid; e < V; e += kThreads) {
+      uint32_t raw = DT == 0 ? reinterpret_cast<const uint32_t*>(sl.row)[e]
+                             : (uint32_t)reinterpret_cast<const uint16_t*>(sl.row)[e];
+      if ((pt.bits[e >> 5] >> (e & 31)) & 1u) {
+        const uint32_t rk = proc::rank_of(pt, (uint32_t)e);
+        raw = proc::edit<DT>(raw, pt.count[rk], pt.bias[rk], prm.rep, prm.pres, prm.freq);
+      }
+      if (DT == 0) reinterpret_cast<uint32_t*>(dst)[e] = raw;
+      else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)raw;
+    }
+    __threadfence();
+    __syncthreads();  // the copy is complete; the LDS is the general path's again
+    sl.row = dst;
+  }
   // this slice's packed-mask words fit the LDS stage (always for resident rows)
   const bool stage_ok = (sl.we - sl.wb + 31) / 32 <= kStageWords;
 

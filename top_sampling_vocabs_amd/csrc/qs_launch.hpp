@@ -42,6 +42,21 @@ struct FilterArgs {
   const chunk::ChunkMass* ws_mass;
   const uint32_t* ws_cands;
   int S;                  // chunks per row
+  // logit processors applied in the kernel (p_on = 0: none); p_copy holds one
+  // workspace row of p_copy_bytes per row for rows selected from an edited copy
+  int p_on;
+  const int32_t* p_hist;
+  int64_t p_hist_cap;
+  const int32_t* p_hist_count;
+  const float* p_rep;
+  const float* p_pres;
+  const float* p_freq;
+  const int32_t* p_bias_ids;
+  const float* p_bias_vals;
+  int64_t p_bias_cap;
+  const int32_t* p_bias_count;
+  uint8_t* p_copy;
+  int64_t p_copy_bytes;
 };
 
 struct ArgmaxArgs {

@@ -25,6 +25,8 @@
 // packed 16-bit helpers.
 #pragma once
 
+#include "qs_proc.hpp"
+
 // Per-row scalars shared through LDS by the general and the histogram paths.
 struct RowInfo {
   uint32_t cnt[kWaves];
@@ -46,7 +48,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                            uint32_t* mask_row, float* dense_row,
                                            uint8_t* pool_raw, uint32_t (*stage)[kStageWords],
                                            uint4* lut, double* wtab, RedScratch& red,
-                                           RowInfo& info) {
+                                           RowInfo& info, uint32_t* s_proc) {
   using K = Keys<1>;
   constexpr uint32_t kCap = (uint32_t)PoolLayout<1>::kPerWave;
   // entries per wave; 64 dump slots and two steps of the slice (64 lanes x 32 B) follow
@@ -199,6 +201,87 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     }
     xs[st] = make_uint4(dm[0], dm[1], dm[2], dm[3]);
   });
+
+  // -- logit processors: edited tokens patched in the registers, the histogram
+  //    corrected (their table after the histogram and the pair-mask table in the
+  //    pools' LDS, the biases in the stage) ----------------------------------------
+  if (a.p_on) {
+    const proc::RowParams prm = proc::row_params(a, r);
+    const proc::Table pt = proc::table_at(pool_raw + (sel::kBins + 64) * 4 + 4096, &stage[0][0]);
+    static_assert((sel::kBins + 64) * 4 + 4096 + proc::kBytes <= kPoolBytes, "processor table");
+    static_assert(kWaves * kStageWords >= proc::kMaxIds, "processor biases");
+    const bool ok = prm.ok && proc::build(a, r, tid, prm, pt, s_proc + 16, s_proc);
+    if (!ok) {
+      if (mask_row && sl.we > sl.wb)
+        for (int i = (sl.wb >> 5) + lane; i < ((sl.we + 31) >> 5); i += 64) mask_row[i] = 0u;
+      if (dense_row)
+        for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
+      if (tid == 0) {
+        a.status[r] = QS_ROW_BAD_PARAM;
+        if (SAMPLE) {
+          a.tokens[r] = -1;
+          if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
+        }
+        if (a.cand_count) a.cand_count[r] = 0;
+        if (a.dbg) {
+          a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
+          a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
+        }
+      }
+      return true;
+    }
+    bool patched = false;
+    // the bin of a legal token's raw bits, as the pass computes it
+    auto bin_of = [](uint32_t raw) -> uint32_t {
+      const uint32_t mag = raw & 0x7FFFu;
+      uint32_t b = mag > sel::kMagLo - 16u ? mag - (sel::kMagLo - 16u) : 0u;
+      b = min(b, sel::kTop);
+      return b + (raw >> 15) * sel::kSide;
+    };
+    static_for<0, NL>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const int e0 = lane_e + st * kStep;
+      const uint32_t pb = e0 < sl.we ? (pt.bits[e0 >> 5] >> (e0 & 31)) & 0xFFu : 0u;
+      const uint32_t wd = legal_word(st);
+      if (ballot(pb != 0u)) {
+        uint32_t m = pb & legal_bits(st, wd);
+        uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+        while (m) {
+          const uint32_t j = (uint32_t)__builtin_ctz(m);
+          m &= m - 1u;
+          const uint32_t rk = proc::rank_of(pt, (uint32_t)e0 + j);
+          const uint32_t sh = 16u * (j & 1u);
+          uint32_t raw = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if ((uint32_t)q == (j >> 1)) raw = (r4[q] >> sh) & 0xFFFFu;
+          const uint32_t nv = proc::edit<1>(raw, pt.count[rk], pt.bias[rk], prm.rep, prm.pres,
+                                            prm.freq) & 0xFFFFu;
+          if (nv != raw) {
+            __hip_atomic_fetch_sub(hist + bin_of(raw), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(hist + bin_of(nv), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if ((uint32_t)q == (j >> 1)) r4[q] = (r4[q] & ~(0xFFFFu << sh)) | (nv << sh);
+            patched = true;
+          }
+        }
+        xs[st] = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    });
+    if (patched) {  // this lane's largest legal value again
+      vmax2 = 0x80008000u;
+      static_for<0, NL>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          vmax2 = bits_of(__builtin_elementwise_max(as_s2(vmax2), as_s2(r4[q])));
+      });
+    }
+  }
 
   // -- parameters (only the scans below need them) -------------------------------------
   const float Tf = a.T[r];
