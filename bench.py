@@ -482,21 +482,86 @@ def penalties_bench(args, lib, stream):
     torch.cuda.synchronize()
     ms, graph, cs = time_graph(bias, args.steps)
     out["logit_bias"] = ms / args.steps
-    del graph, qs
+    del graph
+
+    class SeparateAll:
+        """penalties, then the bias kernel, then sample: three launches"""
+
+        def __init__(self, pn, bc):
+            self.pn, self.bc = pn, bc
+
+        def call(self, stream=None, flags=None):
+            self.pn.with_sample = False
+            self.pn.call(stream)
+            self.bc.call(stream)
+            self.pn.prep.call(stream)
+
+    class FusedCall:
+        """qs_sample_processed: the processors applied inside the sampling
+        launch. The caller's rows are only read, so the real parameters
+        (repetition 1.2, presence 0.3) are used on every step."""
+
+        def __init__(self, pn, bc):
+            pr, w = pn.prep, pn.prep.w
+            dt = 1 if w.dtype == "bf16" else 0
+            self.rep = torch.full((w.B,), 1.2, dtype=torch.float32, device="cuda")
+            self.pres = torch.full((w.B,), 0.3, dtype=torch.float32, device="cuda")
+            P = lambda t: t.data_ptr()  # noqa: E731
+            self.proc = qsl.QsProcessors(
+                P(pn.hist), PenaltyPrepared.H, P(pn.cnt), P(self.rep), P(self.pres), None,
+                P(bc.ids) if bc else None, P(bc.vals) if bc else None,
+                PenaltyPrepared.H if bc else 0, P(bc.cnt) if bc else None)
+            nb = lib.qs_processors_workspace_bytes(w.B, w.V, dt)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            self.args = pr.args[:-4] + (pr.args[-4], ctypes.byref(self.proc),
+                                        ctypes.c_void_p(self.ws.data_ptr()), nb, None)
+            self.pr = pr
+
+        def call(self, stream=None, flags=None):
+            rc = lib.qs_sample_processed(*(self.args[:-1] + (stream,)))
+            if rc != 0:
+                raise RuntimeError(f"qs_sample_processed returned {rc}")
+
+    from top_sampling_vocabs_amd import _lib as qsl
+    modes = [("penalties+bias+sample", [SeparateAll(pn, bc) for pn, bc in zip(pens, bias)]),
+             ("fused penalties+sample", [FusedCall(pn, None) for pn in pens]),
+             ("fused penalties+bias+sample", [FusedCall(pn, bc) for pn, bc in zip(pens, bias)])]
+    for mode, calls in modes:
+        for i in range(args.warmup):
+            calls[i % len(calls)].call(stream)
+        torch.cuda.synchronize()
+        ms, graph, cs = time_graph(calls, args.steps)
+        out[mode] = ms / args.steps
+        del graph
+        if mode.startswith("fused"):
+            # every row processed and sampled (none over the id limit; a kept
+            # set larger than the candidate lists' capacity still samples)
+            for c in calls:
+                st = c.pr.status.cpu().numpy()
+                bad = np.nonzero((st != qsl.ROW_OK) & (st != qsl.ROW_CAND_OVERFLOW))[0]
+                if bad.size:
+                    raise RuntimeError(f"{mode}: rows {bad.tolist()} not sampled, "
+                                       f"statuses {st[bad].tolist()}")
+    del qs
     B = preps[0].w.B
     H = PenaltyPrepared.H
     nbytes = B * (4 * H + 12 + 2 * 2 * H)  # ids, params, read + write of each penalised logit
     per = out["penalties"]
     line = {
         "metric": "rows/sec of penalties + sample, B=256 V=151936",
-        "value": round(B / (out["penalties+sample"] * 1e-3), 1), "unit": "rows/s",
+        "value": round(B / (out["fused penalties+sample"] * 1e-3), 1), "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(out["penalties+sample"], 5), "higher_is_better": True,
+        "ms_per_step": round(out["fused penalties+sample"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "B=256 V=151936 bf16 batch, 2048-token history per row, "
-                               "repetition 1.2, presence 0.3",
+                               "repetition 1.2, presence 0.3, value = one fused launch",
+                   "fused_penalties_sample_ms": round(out["fused penalties+sample"], 5),
+                   "separate_penalties_then_sample_ms": round(out["penalties+sample"], 5),
                    "penalties_ms": round(per, 5),
-                   "logit_bias_ms_2048_ids": round(out["logit_bias"], 5)},
+                   "logit_bias_ms_2048_ids": round(out["logit_bias"], 5),
+                   "separate_penalties_bias_sample_ms": round(out["penalties+bias+sample"], 5),
+                   "fused_penalties_bias_sample_ms":
+                       round(out["fused penalties+bias+sample"], 5)},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
                      "peak": 8000.0, "unit": "GB/s",
                      "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,

@@ -275,9 +275,10 @@ QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* tar
  * Bias (all three pointers NULL: none): bias_ids [B][bias_cap] int32,
  *   bias_values [B][bias_cap] float32, bias_count [B] int32.
  * A row whose processor arguments qs_apply_penalties or qs_apply_logit_bias
- * would flag, or whose history and bias lists hold more than 4096 distinct
- * in-range ids together, gets QS_ROW_BAD_PARAM and no outputs (no token, no
- * draw). */
+ * would flag (a frequency penalty with more than 4096 history entries among
+ * them), or whose bias list holds more than 4096 entries, gets
+ * QS_ROW_BAD_PARAM and no outputs (no token, no draw). Histories without a
+ * frequency penalty may be of any length. */
 typedef struct QsProcessors {
   const int32_t* history;
   int64_t history_cap;

@@ -156,7 +156,8 @@ def _edited_workload(w, hist, hcnt, rep, pres, freq, bids, bvals, bcnt):
     return dataclasses.replace(w, logits=z2), bad
 
 
-@pytest.mark.parametrize("case", ["bf16_resident", "bf16_switch", "f32", "bf16_greedy"])
+@pytest.mark.parametrize("case", ["bf16_resident", "bf16_switch", "f32", "bf16_greedy",
+                                  "bf16_direct", "bf16_penalties_only", "bf16_direct_penalties"])
 def test_processed_matches_oracle(qs, case):
     """qs_sample_processed / qs_filter_mask_processed: penalties and bias
     applied inside the call (the caller's logits untouched) give the outputs
@@ -165,15 +166,29 @@ def test_processed_matches_oracle(qs, case):
     arguments (either processor's, or too many edited ids) are BAD_PARAM.
     bf16 rows held in registers patch the edited tokens in place; fp32 rows,
     switched runs and greedy rows are selected from an edited copy in the
-    workspace."""
+    workspace. bf16_direct: every token legal and kept sets larger than the
+    histogram path's per-wave pools (and flat rows with a negative boundary),
+    so waves read their slices again: from the edited copy, not the caller's
+    row."""
     import torch
     rng = np.random.default_rng({"bf16_resident": 1, "bf16_switch": 2, "f32": 3,
-                                 "bf16_greedy": 4}[case])
+                                 "bf16_greedy": 4, "bf16_direct": 5, "bf16_penalties_only": 6,
+                                 "bf16_direct_penalties": 7}[case])
+    # (the *_penalties cases pass repetition and presence penalties alone: no
+    # frequency penalty, no bias list)
+    pen_only = case in ("bf16_penalties_only", "bf16_direct_penalties")
     dtype = "f32" if case == "f32" else "bf16"
     B, V = 24, (20000 if dtype == "f32" else 40000)
     w = workloads.make(3 if dtype == "bf16" else 2, B=B, V=V, seed=int(rng.integers(1 << 30)))
     if case == "bf16_greedy":
         w.T[::2] = 0.0
+    if case in ("bf16_direct", "bf16_direct_penalties"):
+        w.bitmask = None
+        w.k[:] = 0
+        w.T[:] = np.where(np.arange(B) % 2 == 0, 3.0, 1.0).astype(np.float32)
+        w.p[:] = rng.choice([0.95, 0.99, 0.999], B).astype(np.float32)
+        flat = (0.05 * rng.standard_normal((4, V))).astype(np.float32)
+        w.logits[B - 4:] = workloads.f32_to_bf16_bits(flat)
     hist, hcnt = _history(rng, B, V, 700)
     rep = rng.choice([1.0, 1.3, 0.7, 2.0], B).astype(np.float32)
     pres = rng.choice([0.0, 0.4, -0.2], B).astype(np.float32)
@@ -182,21 +197,34 @@ def test_processed_matches_oracle(qs, case):
     bids = np.stack([rng.choice(V, bcap, replace=False) for _ in range(B)]).astype(np.int32)
     bids[:, ::17] = -5                              # out of range: ignored
     bvals = rng.normal(0, 2, (B, bcap)).astype(np.float32)
-    bvals[:, ::5] = 40.0                            # pushed to the top
+    if case != "bf16_direct":
+        bvals[:, ::5] = 40.0                        # pushed to the top
     bcnt = rng.integers(0, bcap + 1, B).astype(np.int32)
-    # invalid rows: a bad repetition penalty, a repeated bias id, a non-finite bias
+    if pen_only:
+        freq = np.zeros(B, np.float32)
+        bcnt = np.zeros(B, np.int32)
+    # invalid rows: a bad repetition penalty, a repeated bias id, a non-finite
+    # bias (a bad presence penalty and a history count past the capacity for
+    # the penalties alone)
     rep[3] = 0.0
-    bids[4, 1] = bids[4, 0] if bids[4, 0] >= 0 else 7
-    bids[4, 0] = bids[4, 1]
-    bcnt[4] = max(bcnt[4], 2)
-    bvals[5, 0] = np.inf
-    bcnt[5] = max(bcnt[5], 1)
+    if pen_only:
+        pres[4] = np.nan
+        hcnt[5] = 701
+    else:
+        bids[4, 1] = bids[4, 0] if bids[4, 0] >= 0 else 7
+        bids[4, 0] = bids[4, 1]
+        bcnt[4] = max(bcnt[4], 2)
+        bvals[5, 0] = np.inf
+        bcnt[5] = max(bcnt[5], 1)
     ew, bad = _edited_workload(w, hist, hcnt, rep, pres, freq, bids, bvals, bcnt)
     d = to_device(w)
     before = d["logits"].clone()
-    P = {k: torch.from_numpy(v).cuda() for k, v in (
-        ("history", hist), ("history_count", hcnt), ("repetition", rep), ("presence", pres),
-        ("frequency", freq), ("bias_ids", bids), ("bias_values", bvals), ("bias_count", bcnt))}
+    groups = (("history", hist), ("history_count", hcnt), ("repetition", rep),
+              ("presence", pres))
+    if not pen_only:
+        groups += (("frequency", freq), ("bias_ids", bids), ("bias_values", bvals),
+                   ("bias_count", bcnt))
+    P = {k: torch.from_numpy(v).cuda() for k, v in groups}
     uni = np.random.default_rng(8).random(B)
     flags = qs.FLAG_STREAM if case == "bf16_switch" else 0
     out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
@@ -216,27 +244,48 @@ def test_processed_matches_oracle(qs, case):
     compare_tokens(res, out["tokens"], good, rep_, uniforms=uni)
     rep_.check()
     assert np.array_equal(fm["keep_mask"].cpu().numpy(), out["keep_mask"].cpu().numpy())
+    dbg = out["debug"].cpu().numpy()
     if case == "bf16_resident":
-        dbg = out["debug"].cpu().numpy()
         assert (dbg[good, 0] == 0).all() and (dbg[good, 1] == 0).all(), dbg[good].tolist()
+    if case in ("bf16_direct", "bf16_direct_penalties"):  # kept sets past the pools
+        hist_path = (dbg[good, 0] == 0) & (dbg[good, 1] == 0)
+        assert (hist_path & (dbg[good, 3] > 16 * 960)).sum() >= 4, dbg[good].tolist()
 
 
-def test_processed_too_many_ids(qs):
-    """More than 4096 distinct edited tokens in a row: BAD_PARAM; the other
-    rows are unaffected."""
+def test_processed_limits(qs):
+    """The fused call's limits: a row with more than 4096 bias entries, or
+    with more than 4096 history entries and a frequency penalty, is
+    BAD_PARAM; a longer history without a frequency penalty is applied like
+    any other (5,000 entries here) and matches the oracle."""
     import torch
+    rng = np.random.default_rng(77)
     B, V = 4, 30000
     w = workloads.make(3, B=B, V=V)
-    hist = np.tile(np.arange(5000, dtype=np.int32), (B, 1))
-    hcnt = np.array([5000, 100, 0, 4096], np.int32)
+    hist = np.stack([rng.permutation(V)[:5000] for _ in range(B)]).astype(np.int32)
+    hcnt = np.array([5000, 5000, 100, 0], np.int32)
     rep = np.full(B, 1.5, np.float32)
-    pres = np.zeros(B, np.float32)
+    pres = np.full(B, 0.2, np.float32)
+    freq = np.array([0.0, 0.1, 0.1, 0.0], np.float32)
+    bids = np.stack([rng.permutation(V)[:5000] for _ in range(B)]).astype(np.int32)
+    bvals = rng.normal(0, 1, bids.shape).astype(np.float32)
+    bcnt = np.array([10, 0, 4096, 4097], np.int32)
+    ew, bad = _edited_workload(w, hist, hcnt, rep, pres, freq, bids, bvals, bcnt)
+    bad = bad | (bcnt > 4096)
+    assert bad.tolist() == [False, True, False, True]
     d = to_device(w)
     P = {k: torch.from_numpy(v).cuda() for k, v in (
-        ("history", hist), ("history_count", hcnt), ("repetition", rep), ("presence", pres))}
+        ("history", hist), ("history_count", hcnt), ("repetition", rep), ("presence", pres),
+        ("frequency", freq), ("bias_ids", bids), ("bias_values", bvals), ("bias_count", bcnt))}
+    uni = np.random.default_rng(9).random(B)
     out = qs.sample(d["logits"], d["T"], d["k"], d["p"], d["bitmask"],
-                    uniforms=torch.full((B,), 0.5, dtype=torch.float64, device="cuda"),
-                    keep_mask=True, processors=P)
+                    uniforms=torch.from_numpy(uni).cuda(), keep_mask=True, cand_cap=V,
+                    dense=True, logprobs=True, processors=P)
     torch.cuda.synchronize()
     st = out["status"].cpu().numpy()
-    assert st[0] == oracle.ROW_BAD_PARAM and (st[1:] != oracle.ROW_BAD_PARAM).all(), st
+    assert (st[bad] == oracle.ROW_BAD_PARAM).all() and (st[~bad] != oracle.ROW_BAD_PARAM).all(), st
+    good = [0, 2]
+    res = oracle.filter_batch(ew.logits, ew.dtype, ew.T, ew.k, ew.p, ew.bitmask, rows=good)
+    rep_ = Report()
+    compare_filter(ew, res, out, good, rep_)
+    compare_tokens(res, out["tokens"], good, rep_, uniforms=uni)
+    rep_.check()

@@ -108,7 +108,9 @@ __device__ __forceinline__ double weight(uint32_t key, double m, double invT) {
 // ---------------------------------------------------------------------------
 // NL > 0: the row is held in registers, NL steps of 512 tokens per wave slice.
 // NL == 0: the row streams through a prefetch ring.
-template <int DT, bool SAMPLE, int NL>
+// P: logit processors applied in the kernel: 0 none (the instances hold none
+// of their code), 1 repetition and presence penalties only, 2 any.
+template <int DT, bool SAMPLE, int NL, int P>
 __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   using K = Keys<DT>;
   using PL = PoolLayout<DT>;
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ __align__(16) uint32_t bgh[DT == 1 ? kBgBins + 64 : 4];
   __shared__ RedScratch red;
   __shared__ RowInfo info;
-  __shared__ uint32_t s_proc[20];  // logit processors: block-scan totals and a flag
+  __shared__ uint32_t s_proc[P ? 20 : 1];  // logit processors: block-scan totals and a flag
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
   uint16_t* const pool_id = reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap);
@@ -137,7 +139,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const int w = uni((int)threadIdx.x >> 6);  // wave index, kept in a scalar register
 
   // -- bf16 rows scanned by the chunk kernel: settled from its candidates --------
-  if constexpr (DT == 1) {
+  if constexpr (DT == 1 && !P) {
     if (a.ws_segs != nullptr) {
       const int tid = threadIdx.x;
       if (merge_row<SAMPLE>(a, r, tid, w, tid & 63, pool_raw, &stage[0][0], hist, binw, red,
@@ -165,7 +167,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       const uint32_t* const bmrow = a.bitmask ? a.bitmask + (size_t)r * a.bm_stride : nullptr;
       uint32_t* const mask_row = a.keep_mask ? a.keep_mask + (size_t)r * W : nullptr;
       float* const dense_row = a.dense ? a.dense + (size_t)r * a.V : nullptr;
-      if (select_row<SAMPLE, NL>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
+      if (select_row<SAMPLE, NL, P>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
                                  pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
                                  info, s_proc))
         return;
@@ -192,13 +194,18 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   float* dense_row = a.dense ? a.dense + (size_t)r * V : nullptr;
 
   // -- logit processors: the row is selected from an edited copy in the
-  //    workspace (its table in the pools' LDS, the biases in the stage) ---------
-  if (a.p_on) {
-    const proc::RowParams prm = proc::row_params(a, r);
-    const proc::Table pt = proc::table_at(pool_raw, &stage[0][0]);
-    static_assert(proc::kBytes <= kPoolBytes, "processor table");
-    const bool ok = prm.ok && proc::build(a, r, tid, prm, pt, s_proc + 16, s_proc);
-    if (!ok) {
+  //    workspace (its table in the pools' LDS, the side part in the stage) ------
+  if constexpr (P) {
+    const proc::RowParams prm = proc::row_params<P>(a, r);
+    const proc::Table pt = proc::table_at(pool_raw, reinterpret_cast<uint8_t*>(&stage[0][0]));
+    static_assert(proc::kMainBytes <= kPoolBytes, "processor table");
+    static_assert(proc::kSideBytes <= kWaves * kStageWords * 4, "processor side table");
+    const proc::HistIds hids = proc::prefetch_ids(a, r, tid);
+    proc::build_clear(a, pt, tid, s_proc + 16);
+    __syncthreads();
+    proc::build_mark(a, r, prm, pt, tid, s_proc + 16, hids);
+    __syncthreads();
+    if (!prm.ok || s_proc[16] != 0u) {
       if (mask_row)
         for (int i = tid; i < W; i += kThreads) mask_row[i] = 0u;
       if (dense_row)
@@ -217,19 +224,26 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       }
       return;
     }
+    if (prm.need_cnt || prm.has_b) proc::build_ranks(a, r, prm, pt, tid, s_proc);
     // copy in 16-byte pieces; the edited tokens of a piece are rewritten first
     constexpr int kPT = 16 / (DT == 0 ? 4 : 2);  // tokens per piece
+    constexpr uint32_t kPM = (1u << kPT) - 1u;
     uint8_t* const dst = a.p_copy + (size_t)r * a.p_copy_bytes;
+    auto bits_at = [&](int e0, uint32_t m) -> uint32_t {  // history | bias << 8
+      const uint32_t sh = (uint32_t)e0 & 31u;
+      const uint32_t hw = prm.has_h ? (pt.hbits[e0 >> 5] >> sh) & m : 0u;
+      const uint32_t bw = prm.has_b ? (pt.bbits[e0 >> 5] >> sh) & m : 0u;
+      return hw | (bw << 8);
+    };
     const int npieces = V / kPT;
     for (int c = tid; c < npieces; c += kThreads) {
       uint4 x = *reinterpret_cast<const uint4*>(sl.row + (size_t)c * 16);
       const int e0 = c * kPT;
-      const uint32_t pb = (pt.bits[e0 >> 5] >> (e0 & 31)) & ((1u << kPT) - 1u);
-      if (pb) {
+      const uint32_t pw = bits_at(e0, kPM);
+      if (pw) {
         uint32_t r4[4] = {x.x, x.y, x.z, x.w};
         for (int j = 0; j < kPT; ++j) {
-          if (!((pb >> j) & 1u)) continue;
-          const uint32_t rk = proc::rank_of(pt, (uint32_t)(e0 + j));
+          if (!(((pw | (pw >> 8)) >> j) & 1u)) continue;
           const int q = DT == 0 ? j : j >> 1;
           const uint32_t sh = DT == 0 ? 0u : 16u * (uint32_t)(j & 1);
           const uint32_t msk = DT == 0 ? 0xFFFFFFFFu : 0xFFFFu;
@@ -237,8 +251,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           for (int qq = 0; qq < 4; ++qq) {
             if (qq == q) {
               const uint32_t raw = (r4[qq] >> sh) & msk;
-              const uint32_t nv = proc::edit<DT>(raw, pt.count[rk], pt.bias[rk], prm.rep,
-                                                 prm.pres, prm.freq) & msk;
+              const uint32_t nv = proc::edit_token<DT>(pt, prm, (uint32_t)(e0 + j), raw,
+                                                       (pw >> j) & 1u, (pw >> (8 + j)) & 1u) &
+                                  msk;
               r4[qq] = (r4[qq] & ~(msk << sh)) | (nv << sh);
             }
           }
@@ -251,10 +266,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
     for (int e = npieces * kPT + tid; e < V; e += kThreads) {
       uint32_t raw = DT == 0 ? reinterpret_cast<const uint32_t*>(sl.row)[e]
                              : (uint32_t)reinterpret_cast<const uint16_t*>(sl.row)[e];
-      if ((pt.bits[e >> 5] >> (e & 31)) & 1u) {
-        const uint32_t rk = proc::rank_of(pt, (uint32_t)e);
-        raw = proc::edit<DT>(raw, pt.count[rk], pt.bias[rk], prm.rep, prm.pres, prm.freq);
-      }
+      const uint32_t pw = bits_at(e, 1u);
+      if (pw) raw = proc::edit_token<DT>(pt, prm, (uint32_t)e, raw, pw & 1u, (pw >> 8) & 1u);
       if (DT == 0) reinterpret_cast<uint32_t*>(dst)[e] = raw;
       else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)raw;
     }
@@ -2188,20 +2201,22 @@ inline int resident_steps(int V) {
   return (per_wave + kStep - 1) / kStep;
 }
 
-template <int DT, bool S>
+template <int DT, bool S, int P>
 hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
   dim3 grid((unsigned)B), block(kThreads);
   const int n = resident_steps(a.V);
   const bool stream = (a.flags & QS_FLAG_STREAM) != 0u;
   if (!stream && n <= kResidentTier[DT][0]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0]>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0], P>), grid, block, 0, st,
+                       a);
   } else if (!stream && n <= kResidentTier[DT][1]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1]>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1], P>), grid, block, 0, st,
+                       a);
   } else {
     a.seg = seg_for(a.V);
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0, P>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -10,11 +10,13 @@
 // values (registers, or a workspace row).
 //
 // Per row, a table in LDS answers "is token t edited, and how" in O(1):
-//   - a bitmap of the row's tokens with one bit per edited token;
-//   - per bitmap word, the count of set bits in the words before it (so the
-//     rank of a set bit is that count plus the set bits below it in its word);
-//   - per rank: the token's count in the history (0: not in it) and its bias
-//     (NaN: none; a bias must be finite).
+//   - a bitmap of the history's tokens and one of the bias list's tokens;
+//   - only where needed, per 128-token block of a bitmap, the count of set
+//     bits in the blocks before it (the rank of a set bit is that count plus
+//     the set bits below it in its block), and per rank the history count
+//     (with a frequency penalty) or the bias.
+// A row with only repetition and presence penalties needs the history bitmap
+// alone: its table is two barriers and one atomic OR per history entry.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,34 +31,50 @@ namespace proc {
 
 constexpr int kMaxV = 155648;          // tokens a table covers
 constexpr int kWords = kMaxV / 32;      // bitmap words
-constexpr int kMaxIds = 4096;           // distinct edited tokens per row
-constexpr int kFreqMaxHistory = 4096;   // history length allowed with a frequency penalty
+constexpr int kBlocks = kWords / 4;     // 128-token blocks
+constexpr int kMaxIds = 4096;           // bias entries per row; history entries with a
+                                        // frequency penalty
 constexpr uint32_t kNoBias = 0x7FC00000u;
 
-// Table bytes: bitmap, 16-bit word prefixes, 32-bit counts (the biases live
-// in a separate region of kMaxIds floats).
-constexpr int kBytes = kWords * 4 + kWords * 2 + kMaxIds * 4;
+// The two LDS regions of a table: the main one (history and bias bitmaps,
+// history block prefixes, history counts) and the side one (biases, bias
+// block prefixes). Both 16-byte aligned.
+constexpr int kMainBytes = kWords * 4 * 2 + kBlocks * 2 + kMaxIds * 4;
+constexpr int kSideBytes = kMaxIds * 4 + kBlocks * 2;
 
 struct Table {
-  uint32_t* bits;      // [kWords]
-  uint16_t* before;    // [kWords]: set bits in the words before
-  uint32_t* count;     // [kMaxIds]
-  uint32_t* bias;      // [kMaxIds] float bits, kNoBias when none
+  uint32_t* hbits;   // [kWords] history tokens
+  uint32_t* bbits;   // [kWords] bias tokens
+  uint16_t* hpre;    // [kBlocks] set history bits in the blocks before
+  uint32_t* count;   // [kMaxIds] history count per history rank
+  uint32_t* bias;    // [kMaxIds] float bits per bias rank
+  uint16_t* bpre;    // [kBlocks] set bias bits in the blocks before
 };
 
-__device__ __forceinline__ Table table_at(uint8_t* base, uint32_t* bias_region) {
+__device__ __forceinline__ Table table_at(uint8_t* main, uint8_t* side) {
   Table t;
-  t.bits = reinterpret_cast<uint32_t*>(base);
-  t.before = reinterpret_cast<uint16_t*>(base + kWords * 4);
-  t.count = reinterpret_cast<uint32_t*>(base + kWords * 6);
-  t.bias = bias_region;
+  t.hbits = reinterpret_cast<uint32_t*>(main);
+  t.bbits = reinterpret_cast<uint32_t*>(main + kWords * 4);
+  t.hpre = reinterpret_cast<uint16_t*>(main + kWords * 8);
+  t.count = reinterpret_cast<uint32_t*>(main + kWords * 8 + kBlocks * 2);
+  t.bias = reinterpret_cast<uint32_t*>(side);
+  t.bpre = reinterpret_cast<uint16_t*>(side + kMaxIds * 4);
   return t;
 }
 
-// rank of token id among the edited tokens (the bit must be set)
-__device__ __forceinline__ uint32_t rank_of(const Table& t, uint32_t id) {
-  const uint32_t wd = t.bits[id >> 5];
-  return (uint32_t)t.before[id >> 5] + (uint32_t)__popc(wd & ((1u << (id & 31u)) - 1u));
+// rank of token id among the set bits of a bitmap (the bit must be set)
+__device__ __forceinline__ uint32_t rank_in(const uint32_t* bits, const uint16_t* pre,
+                                            uint32_t id) {
+  const uint32_t blk = id >> 7;
+  const uint4 q = *reinterpret_cast<const uint4*>(bits + blk * 4u);
+  const uint32_t wi = (id >> 5) & 3u;
+  const uint32_t below = (1u << (id & 31u)) - 1u;
+  uint32_t c = (uint32_t)pre[blk];
+  c += (uint32_t)__popc(wi > 0u ? q.x : q.x & below);
+  c += wi >= 1u ? (uint32_t)__popc(wi > 1u ? q.y : q.y & below) : 0u;
+  c += wi >= 2u ? (uint32_t)__popc(wi > 2u ? q.z : q.z & below) : 0u;
+  c += wi >= 3u ? (uint32_t)__popc(q.w & below) : 0u;
+  return c;
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float v) {
@@ -87,13 +105,19 @@ __device__ __forceinline__ uint32_t edit(uint32_t raw, uint32_t n, uint32_t bb, 
   return out;
 }
 
-// Per-row processor parameters, read by every thread.
+// Per-row processor parameters, read by every thread (uniform).
 struct RowParams {
   int hcnt, bcnt;
   float rep, pres, freq;
-  bool ok;
+  bool ok;         // the arguments pass the processors' checks (biases aside)
+  bool has_h;      // history entries to apply
+  bool has_b;      // bias entries to apply
+  bool need_cnt;   // a frequency penalty: history counts per token
 };
 
+// (P == 1: the call has no frequency penalties and no bias list, which the
+// compiler then knows)
+template <int P>
 __device__ __forceinline__ RowParams row_params(const FilterArgs& a, int r) {
   RowParams p;
   p.hcnt = a.p_hist ? a.p_hist_count[r] : 0;
@@ -103,94 +127,156 @@ __device__ __forceinline__ RowParams row_params(const FilterArgs& a, int r) {
   p.freq = (a.p_hist && a.p_freq) ? a.p_freq[r] : 0.0f;
   p.ok = isfinite(p.rep) && p.rep > 0.0f && isfinite(p.pres) && isfinite(p.freq) &&
          p.hcnt >= 0 && (int64_t)p.hcnt <= a.p_hist_cap &&
-         (p.freq == 0.0f || p.hcnt <= kFreqMaxHistory) && p.bcnt >= 0 &&
-         (int64_t)p.bcnt <= a.p_bias_cap;
+         (p.freq == 0.0f || p.hcnt <= kMaxIds) && p.bcnt >= 0 &&
+         (int64_t)p.bcnt <= a.p_bias_cap && p.bcnt <= kMaxIds;
+  p.has_h = p.ok && p.hcnt > 0;
+  p.has_b = p.ok && p.bcnt > 0;
+  p.need_cnt = p.has_h && p.freq != 0.0f;
+  if constexpr (P == 1) {
+    p.freq = 0.0f;
+    p.bcnt = 0;
+    p.has_b = false;
+    p.need_cnt = false;
+  }
   return p;
 }
 
-// Build the table of row r with all 1024 threads (every thread must call it;
-// it holds barriers). `flag` is one LDS word of scratch. Returns false, the
-// same in every thread, when the row's processor arguments are invalid: a
-// non-finite bias, a token listed twice in the bias list, or more than
-// kMaxIds distinct edited tokens.
-__device__ __forceinline__ bool build(const FilterArgs& a, int r, int tid, const RowParams& p,
-                                      const Table& t, uint32_t* flag, uint32_t* wsum) {
-  const int V = a.V;
-  const int W = (V + 31) >> 5;
-  const int32_t* const h = a.p_hist ? a.p_hist + (size_t)r * a.p_hist_cap : nullptr;
-  const int32_t* const bi = a.p_bias_ids ? a.p_bias_ids + (size_t)r * a.p_bias_cap : nullptr;
-  const float* const bv = a.p_bias_ids ? a.p_bias_vals + (size_t)r * a.p_bias_cap : nullptr;
-  for (int i = tid; i < W; i += 1024) t.bits[i] = 0u;
-  for (int i = tid; i < kMaxIds; i += 1024) {
-    t.count[i] = 0u;
-    t.bias[i] = kNoBias;
+// Table build in three parts, each ended by a barrier of the caller's
+// (all threads call each part; `flag` is one LDS word that part 1 clears and
+// part 2 sets for a bad row).
+//   1. clear: both bitmaps;
+//   2. mark: the counts cleared, one atomic OR per history / bias entry (a
+//      bias token listed twice, or a non-finite bias, flags the row);
+//   3. ranks (only with a frequency penalty or a bias list): block prefixes
+//      of both bitmaps in one block scan, a barrier, then the counts and
+//      biases by rank. Ends with its own barrier.
+// (part 1 needs no row parameter, so it does not wait for them)
+__device__ __forceinline__ void build_clear(const FilterArgs& a, const Table& t, int tid,
+                                            uint32_t* flag) {
+  const int Wc = (((a.V + 31) >> 5) + 3) & ~3;  // whole 4-word blocks
+  for (int i = tid; i < Wc; i += 1024) {
+    t.hbits[i] = 0u;
+    t.bbits[i] = 0u;
   }
   if (tid == 0) *flag = 0u;
-  __syncthreads();
-  for (int i = tid; i < p.hcnt; i += 1024) {
-    const int x = h[i];
-    if (x >= 0 && x < V)
-      __hip_atomic_fetch_or(t.bits + (x >> 5), 1u << (x & 31), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  bool bad = false;
-  for (int i = tid; i < p.bcnt; i += 1024) {
-    const int x = bi[i];
-    bad = bad || !isfinite(bv[i]);
-    if (x >= 0 && x < V)
-      __hip_atomic_fetch_or(t.bits + (x >> 5), 1u << (x & 31), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  if (bad) *flag = 1u;
-  __syncthreads();
-  // word prefixes: each thread sums a run of up to 5 words, a block scan of
-  // the runs, then each thread writes its words' prefixes
-  constexpr int kPer = (kWords + 1023) / 1024;
-  const int w0 = tid * kPer;
-  uint32_t mine = 0u;
+}
+
+// The first two history entries of a thread (entries tid and tid + 1024 of
+// the row, -1 past the history's capacity), requested before the table is
+// cleared so that their latency hides behind it.
+struct HistIds {
+  int32_t v[2];
+};
+
+__device__ __forceinline__ HistIds prefetch_ids(const FilterArgs& a, int r, int tid) {
+  HistIds q;
+  const int32_t* const h = a.p_hist ? a.p_hist + (size_t)r * a.p_hist_cap : nullptr;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (w0 + j < W) mine += (uint32_t)__popc(t.bits[w0 + j]);
+  for (int j = 0; j < 2; ++j) {
+    const int64_t i = tid + 1024 * j;
+    q.v[j] = (h && i < a.p_hist_cap) ? h[i] : -1;
+  }
+  return q;
+}
+
+__device__ __forceinline__ void build_mark(const FilterArgs& a, int r, const RowParams& p,
+                                           const Table& t, int tid, uint32_t* flag,
+                                           const HistIds& pre) {
+  const int V = a.V;
+  if (p.need_cnt)
+    for (int i = tid; i < kMaxIds; i += 1024) t.count[i] = 0u;
+  if (p.has_h) {
+    const int32_t* const h = a.p_hist + (size_t)r * a.p_hist_cap;
+    for (int i = tid; i < p.hcnt; i += 1024) {
+      const int x = i < 2048 ? pre.v[i >> 10] : h[i];
+      if (x >= 0 && x < V)
+        __hip_atomic_fetch_or(t.hbits + (x >> 5), 1u << (x & 31), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  if (p.has_b) {
+    const int32_t* const bi = a.p_bias_ids + (size_t)r * a.p_bias_cap;
+    const float* const bv = a.p_bias_vals + (size_t)r * a.p_bias_cap;
+    bool bad = false;
+    for (int i = tid; i < p.bcnt; i += 1024) {
+      const int x = bi[i];
+      bad = bad || !isfinite(bv[i]);
+      if (x >= 0 && x < V) {
+        const uint32_t bit = 1u << (x & 31);
+        const uint32_t old = __hip_atomic_fetch_or(t.bbits + (x >> 5), bit, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        bad = bad || (old & bit) != 0u;  // listed twice
+      }
+    }
+    if (bad) *flag = 1u;
+  }
+}
+
+__device__ __forceinline__ void build_ranks(const FilterArgs& a, int r, const RowParams& p,
+                                            const Table& t, int tid, uint32_t* wsum) {
+  // thread i covers blocks 2i and 2i + 1; both bitmaps' counts in 16-bit
+  // fields (each total is at most kMaxIds)
+  const int nb = (((a.V + 31) >> 5) + 3) >> 2;
+  const int b0 = 2 * tid;
+  uint32_t s0 = 0u, s1 = 0u;
+  auto cnt4 = [&](const uint32_t* bits, int b) -> uint32_t {
+    const uint4 q = *reinterpret_cast<const uint4*>(bits + 4 * b);
+    return (uint32_t)(__popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w));
+  };
+  if (b0 < nb) {
+    if (p.need_cnt) s0 += cnt4(t.hbits, b0);
+    if (p.has_b) s0 += cnt4(t.bbits, b0) << 16;
+  }
+  if (b0 + 1 < nb) {
+    if (p.need_cnt) s1 += cnt4(t.hbits, b0 + 1);
+    if (p.has_b) s1 += cnt4(t.bbits, b0 + 1) << 16;
+  }
+  const uint32_t mine = s0 + s1;
   const int lane = tid & 63, wv = tid >> 6;
   const uint32_t incl = scan_incl_u32(mine);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  uint32_t base = 0u, total = 0u;
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t s = wsum[k];
-    base += k < wv ? s : 0u;
-    total += s;
+  uint32_t base = 0u;
+  for (int k = 0; k < 16; ++k) base += k < wv ? wsum[k] : 0u;
+  const uint32_t e0 = base + incl - mine, e1 = e0 + s0;
+  if (b0 < nb) {
+    if (p.need_cnt) t.hpre[b0] = (uint16_t)(e0 & 0xFFFFu);
+    if (p.has_b) t.bpre[b0] = (uint16_t)(e0 >> 16);
   }
-  uint32_t run = base + incl - mine;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (w0 + j < W) {
-      t.before[w0 + j] = (uint16_t)min(run, 0xFFFFu);
-      run += (uint32_t)__popc(t.bits[w0 + j]);
+  if (b0 + 1 < nb) {
+    if (p.need_cnt) t.hpre[b0 + 1] = (uint16_t)(e1 & 0xFFFFu);
+    if (p.has_b) t.bpre[b0 + 1] = (uint16_t)(e1 >> 16);
+  }
+  __syncthreads();
+  const int V = a.V;
+  if (p.need_cnt) {
+    const int32_t* const h = a.p_hist + (size_t)r * a.p_hist_cap;
+    for (int i = tid; i < p.hcnt; i += 1024) {
+      const int x = h[i];
+      if (x >= 0 && x < V)
+        __hip_atomic_fetch_add(t.count + rank_in(t.hbits, t.hpre, (uint32_t)x), 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  if (p.has_b) {
+    const int32_t* const bi = a.p_bias_ids + (size_t)r * a.p_bias_cap;
+    const float* const bv = a.p_bias_vals + (size_t)r * a.p_bias_cap;
+    for (int i = tid; i < p.bcnt; i += 1024) {
+      const int x = bi[i];
+      if (x >= 0 && x < V) t.bias[rank_in(t.bbits, t.bpre, (uint32_t)x)] = __float_as_uint(bv[i]);
     }
   }
   __syncthreads();
-  if (total > (uint32_t)kMaxIds) return false;
-  for (int i = tid; i < p.hcnt; i += 1024) {
-    const int x = h[i];
-    if (x >= 0 && x < V)
-      __hip_atomic_fetch_add(t.count + rank_of(t, (uint32_t)x), 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  bad = false;
-  for (int i = tid; i < p.bcnt; i += 1024) {
-    const int x = bi[i];
-    if (x >= 0 && x < V) {
-      uint32_t expect = kNoBias;
-      const bool won = __hip_atomic_compare_exchange_strong(
-          t.bias + rank_of(t, (uint32_t)x), &expect, __float_as_uint(bv[i]), __ATOMIC_RELAXED,
-          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      bad = bad || !won;  // listed twice
-    }
-  }
-  if (bad) *flag = 1u;
-  __syncthreads();
-  return *flag == 0u;
+}
+
+// The edited raw bits of token id (raw bits `raw`) whose history bit is hb
+// and bias bit bb (at least one set).
+template <int DT>
+__device__ __forceinline__ uint32_t edit_token(const Table& t, const RowParams& p, uint32_t id,
+                                               uint32_t raw, bool hb, bool bb) {
+  const uint32_t n = hb ? (p.need_cnt ? t.count[rank_in(t.hbits, t.hpre, id)] : 1u) : 0u;
+  const uint32_t bv = bb ? t.bias[rank_in(t.bbits, t.bpre, id)] : kNoBias;
+  return edit<DT>(raw, n, bv, p.rep, p.pres, p.freq);
 }
 
 }  // namespace proc

@@ -42,7 +42,7 @@ struct RowInfo {
 };
 
 
-template <bool SAMPLE, int NL>
+template <bool SAMPLE, int NL, int P>
 __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl, int r, int w,
                                            int lane, int tid, int W, const uint32_t* bmrow,
                                            uint32_t* mask_row, float* dense_row,
@@ -101,6 +101,8 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
                                              rsrc, voff, st * kStep * 2, 0));
   };
   static_for<0, kEarly>(issue);
+  proc::HistIds hids{};
+  if constexpr (P) hids = proc::prefetch_ids(a, r, tid);
 
   // -- tables: legal pair masks, the cleared histogram, this slice's mask words ------
   uint32_t* const hist = reinterpret_cast<uint32_t*>(pool_raw);  // kBins + 64 dump bins
@@ -128,8 +130,47 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     // the row declines
     info.sel_u[0] = sel::kNone;
   }
+  // logit processors: the row's table (after the histogram and the pair-mask
+  // table in the pools' LDS, its side part in the stage), built while the
+  // first steps are in flight; the pass edits the tokens it flags
+  proc::RowParams prm{};
+  proc::Table pt{};
+  if constexpr (P) {
+    prm = proc::row_params<P>(a, r);
+    pt = proc::table_at(pool_raw + (sel::kBins + 64) * 4 + 4096,
+                        reinterpret_cast<uint8_t*>(&stage[0][0]));
+    static_assert((sel::kBins + 64) * 4 + 4096 + proc::kMainBytes <= kPoolBytes,
+                  "processor table");
+    static_assert(proc::kSideBytes <= kWaves * kStageWords * 4, "processor side table");
+    proc::build_clear(a, pt, tid, s_proc + 16);
+  }
   __syncthreads();  // cleared histogram
   static_for<kEarly, kLook>(issue);
+  if constexpr (P) {
+    proc::build_mark(a, r, prm, pt, tid, s_proc + 16, hids);
+    __syncthreads();  // marked
+    if (!prm.ok || s_proc[16] != 0u) {
+      if (mask_row && sl.we > sl.wb)
+        for (int i = (sl.wb >> 5) + lane; i < ((sl.we + 31) >> 5); i += 64) mask_row[i] = 0u;
+      if (dense_row)
+        for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
+      if (tid == 0) {
+        a.status[r] = QS_ROW_BAD_PARAM;
+        if (SAMPLE) {
+          a.tokens[r] = -1;
+          if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
+        }
+        if (a.cand_count) a.cand_count[r] = 0;
+        if (a.dbg) {
+          a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
+          a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
+        }
+      }
+      return true;
+    }
+    if (prm.need_cnt || prm.has_b) proc::build_ranks(a, r, prm, pt, tid, s_proc);
+  }
+  const bool p_any = P && (prm.has_h || prm.has_b);
 
   // -- the pass: count every legal token in its value bin ------------------------------
   // legal bits of step st: byte (lane & 3) of slice word 16 st + lane / 4, held
@@ -159,6 +200,21 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   if constexpr (NL > 1) wdv[1] = legal_word(1);
   mbv[0] = legal_bits(0, wdv[0]);
   nbv[0] = lut[mbv[0]];
+  // logit processors: this lane's history bits (low byte) and bias bits (next
+  // byte) of a step, read one step ahead like the legal bits (bits past the
+  // slice are masked by the legal bits)
+  uint32_t pwv[NL];
+  auto proc_bits = [&](int st) -> uint32_t {
+    const int e0 = lane_e + st * kStep;  // below 16 slices of NL steps: inside the bitmaps
+    const uint32_t sh = (uint32_t)e0 & 31u;
+    const uint32_t hw = prm.has_h ? (pt.hbits[e0 >> 5] >> sh) & 0xFFu : 0u;
+    const uint32_t bw = prm.has_b ? (pt.bbits[e0 >> 5] >> sh) & 0xFFu : 0u;
+    return hw | (bw << 8);
+  };
+  if constexpr (P) {
+    static_assert(16 * NL * kStep <= proc::kMaxV, "slices inside the processor bitmaps");
+    pwv[0] = p_any ? proc_bits(0) : 0u;
+  }
   uint32_t n_legal = 0u;
   // the largest legal raw bits read as signed 16-bit: positive values order
   // like their bits, negative ones lie below every positive one
@@ -170,11 +226,36 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     if constexpr (st + 1 < NL) {
       mbv[st + 1] = legal_bits(st + 1, wdv[st + 1]);
       nbv[st + 1] = lut[mbv[st + 1]];
+      if constexpr (P) pwv[st + 1] = p_any ? proc_bits(st + 1) : 0u;
     }
     n_legal += (uint32_t)__popc(mbv[st]);
     issue(std::integral_constant<int, st + kLook>{});
     const uint4 nb4 = nbv[st];
     const uint32_t nb[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
+    if constexpr (P) {
+      // the legal tokens the processors edit, rewritten before they are counted
+      const uint32_t pw = pwv[st];
+      uint32_t m = (pw | (pw >> 8)) & mbv[st];
+      if (ballot(m != 0u)) {
+        const uint32_t e0 = (uint32_t)(lane_e + st * kStep);
+        uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
+        while (m) {
+          const uint32_t j = (uint32_t)__builtin_ctz(m);
+          m &= m - 1u;
+          const uint32_t sh = 16u * (j & 1u);
+          uint32_t raw = 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if ((uint32_t)q == (j >> 1)) raw = (r4[q] >> sh) & 0xFFFFu;
+          const uint32_t nv = proc::edit_token<1>(pt, prm, e0 + j, raw, (pw >> j) & 1u,
+                                                  (pw >> (8u + j)) & 1u) & 0xFFFFu;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if ((uint32_t)q == (j >> 1)) r4[q] = (r4[q] & ~(0xFFFFu << sh)) | (nv << sh);
+        }
+        xs[st] = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    }
     const uint32_t d4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
     uint32_t dm[4];
 #pragma unroll
@@ -201,87 +282,6 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
     }
     xs[st] = make_uint4(dm[0], dm[1], dm[2], dm[3]);
   });
-
-  // -- logit processors: edited tokens patched in the registers, the histogram
-  //    corrected (their table after the histogram and the pair-mask table in the
-  //    pools' LDS, the biases in the stage) ----------------------------------------
-  if (a.p_on) {
-    const proc::RowParams prm = proc::row_params(a, r);
-    const proc::Table pt = proc::table_at(pool_raw + (sel::kBins + 64) * 4 + 4096, &stage[0][0]);
-    static_assert((sel::kBins + 64) * 4 + 4096 + proc::kBytes <= kPoolBytes, "processor table");
-    static_assert(kWaves * kStageWords >= proc::kMaxIds, "processor biases");
-    const bool ok = prm.ok && proc::build(a, r, tid, prm, pt, s_proc + 16, s_proc);
-    if (!ok) {
-      if (mask_row && sl.we > sl.wb)
-        for (int i = (sl.wb >> 5) + lane; i < ((sl.we + 31) >> 5); i += 64) mask_row[i] = 0u;
-      if (dense_row)
-        for (int i = sl.wb + lane; i < sl.we; i += 64) dense_row[i] = 0.0f;
-      if (tid == 0) {
-        a.status[r] = QS_ROW_BAD_PARAM;
-        if (SAMPLE) {
-          a.tokens[r] = -1;
-          if (a.logprobs) a.logprobs[r] = __builtin_nanf("");
-        }
-        if (a.cand_count) a.cand_count[r] = 0;
-        if (a.dbg) {
-          a.dbg[4 * r + 0] = 0; a.dbg[4 * r + 1] = 0;
-          a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
-        }
-      }
-      return true;
-    }
-    bool patched = false;
-    // the bin of a legal token's raw bits, as the pass computes it
-    auto bin_of = [](uint32_t raw) -> uint32_t {
-      const uint32_t mag = raw & 0x7FFFu;
-      uint32_t b = mag > sel::kMagLo - 16u ? mag - (sel::kMagLo - 16u) : 0u;
-      b = min(b, sel::kTop);
-      return b + (raw >> 15) * sel::kSide;
-    };
-    static_for<0, NL>([&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      const int e0 = lane_e + st * kStep;
-      const uint32_t pb = e0 < sl.we ? (pt.bits[e0 >> 5] >> (e0 & 31)) & 0xFFu : 0u;
-      const uint32_t wd = legal_word(st);
-      if (ballot(pb != 0u)) {
-        uint32_t m = pb & legal_bits(st, wd);
-        uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
-        while (m) {
-          const uint32_t j = (uint32_t)__builtin_ctz(m);
-          m &= m - 1u;
-          const uint32_t rk = proc::rank_of(pt, (uint32_t)e0 + j);
-          const uint32_t sh = 16u * (j & 1u);
-          uint32_t raw = 0u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if ((uint32_t)q == (j >> 1)) raw = (r4[q] >> sh) & 0xFFFFu;
-          const uint32_t nv = proc::edit<1>(raw, pt.count[rk], pt.bias[rk], prm.rep, prm.pres,
-                                            prm.freq) & 0xFFFFu;
-          if (nv != raw) {
-            __hip_atomic_fetch_sub(hist + bin_of(raw), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_add(hist + bin_of(nv), 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if ((uint32_t)q == (j >> 1)) r4[q] = (r4[q] & ~(0xFFFFu << sh)) | (nv << sh);
-            patched = true;
-          }
-        }
-        xs[st] = make_uint4(r4[0], r4[1], r4[2], r4[3]);
-      }
-    });
-    if (patched) {  // this lane's largest legal value again
-      vmax2 = 0x80008000u;
-      static_for<0, NL>([&](auto stc) {
-        constexpr int st = decltype(stc)::value;
-        const uint32_t r4[4] = {xs[st].x, xs[st].y, xs[st].z, xs[st].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          vmax2 = bits_of(__builtin_elementwise_max(as_s2(vmax2), as_s2(r4[q])));
-      });
-    }
-  }
 
   // -- parameters (only the scans below need them) -------------------------------------
   const float Tf = a.T[r];
@@ -730,6 +730,22 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
   // bitmask) and walks it: f(e, bits) per step with this lane's 8 tokens as
   // pool entries and the bits of those at or above the boundary
   const bool direct = ext || uni(pcnt) > kPool;
+  // With logit processors the caller's row holds the unedited values: such a
+  // wave first stores its edited registers (its own slice only; slices start
+  // at multiples of a step) to the row's workspace copy and reads that instead
+  const uint8_t* dsrc = sl.row;
+  if (P && direct) {
+    uint8_t* const cp = a.p_copy + (size_t)r * a.p_copy_bytes;
+    static_for<0, NL>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const int c = lane_e + st * kStep;
+      if (c < sl.we) *reinterpret_cast<uint4*>(cp + 2 * (size_t)c) = xs[st];
+    });
+    dsrc = cp;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc_d = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(dsrc), (short)0, (int)(((uint32_t)sl.V * 2u + 15u) & ~15u),
+      0x00020000);
   // (write_keep: also store each step's keep byte in the mask staging, which
   // the compaction did not fill in the extended mode)
   uint32_t ext_cnt = 0u;
@@ -746,7 +762,7 @@ __device__ __forceinline__ bool select_row(const FilterArgs& a, const Slice& sl,
         const int e0 = lane_e + st * kStep;
         if (st < NL) {
           x[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsrc, voff, st * kStep * 2, 0));
+                                               rsrc_d, voff, st * kStep * 2, 0));
           uint32_t lb = 0u;
           if (e0 < sl.we) {
             lb = bmrow ? (bmrow[e0 >> 5] >> (e0 & 31)) & 0xFFu : 0xFFu;
