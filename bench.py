@@ -229,8 +229,8 @@ def time_graph(preps, K, flags=None):
 
 
 # Path switches of the library and the Qrita page's ablation runs they mirror
-# (its runs C, I and J drop duplicate handling, sort the candidates, or sort
-# the full row: not paths of this library).
+# (its runs C and J drop duplicate handling or sort the full row: not paths of
+# this library).
 ABLATION_RUNS = [
     ("A", "normal path: value histogram (bf16 in registers) / truncation hit + bucket select (fp32)", 0),
     ("B", "single streamed tier instead of the register tiers", 8),
@@ -239,6 +239,8 @@ ABLATION_RUNS = [
     ("F", "truncation hit, binary pivot (one pivot per round)", 16 | 4),
     ("G", "forced fallback, binary pivot", 16 | 1),
     ("Q", "truncation hit, quaternary search on bf16 pools (the page's design)", 4),
+    ("I", "truncation hit, the candidate subset sorted in LDS (up to 8,192 candidates; "
+          "larger subsets are searched)", 32),
 ]
 
 

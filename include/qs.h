@@ -91,6 +91,10 @@ typedef enum { QS_F32 = 0, QS_BF16 = 1 } qs_dtype;
                                       registers                                 */
 #define QS_FLAG_BINARY_PIVOT  16u  /* one pivot per search round (the interval's
                                       midpoint) instead of three (ablation)     */
+#define QS_FLAG_SORT_SUBSET   32u  /* on a truncation hit, sort the candidate
+                                      subset (up to 8192 candidates) and read the
+                                      boundaries off the sorted order instead of
+                                      searching (the ablation's run I)          */
 
 /* Device scratch a qs_filter_mask / qs_sample call on B rows of V tokens of
  * `dtype` needs, in bytes (0: none). The caller owns it and passes it as

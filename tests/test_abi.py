@@ -69,7 +69,7 @@ def filt(lib, **kw):
     dict(T=None), dict(k=None), dict(p=None), dict(status=None), dict(keep=None),
     dict(cids=A16, ccount=None, cap=8), dict(cids=A16, ccount=A16, cap=0),
     dict(bitmask=A16, bms=1), dict(bitmask=ctypes.c_void_p(0x100002), bms=2),
-    dict(flags=32), dict(T=ctypes.c_void_p(0x100001)),
+    dict(flags=64), dict(T=ctypes.c_void_p(0x100001)),
     dict(dtype=1, stride=68),
 ])
 def test_filter_rejects_bad_arguments(lib, kw):

@@ -156,14 +156,14 @@ def test_path_invariance(qs):
 
 
 SWITCHES = ("FLAG_FORCE_MISS", "FLAG_NO_TRUNCATION", "FLAG_PIVOT_SEARCH", "FLAG_STREAM",
-            "FLAG_BINARY_PIVOT")
+            "FLAG_BINARY_PIVOT", "FLAG_SORT_SUBSET")
 
 
 @pytest.mark.parametrize("switch", SWITCHES)
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_switches_match_oracle(qs, cfg, switch):
-    """Every ablation switch (page "Qrita", ablation table: runs B, D, E, F, G
-    and the page's own design, Q) against the oracle directly, on every
+    """Every ablation switch (page "Qrita", ablation table: runs B, D, E, F, G,
+    I and the page's own design, Q) against the oracle directly, on every
     workload at reduced size: masks, lists, probabilities, tokens and
     statuses, to the same tolerances as the normal path."""
     w = workloads.make(cfg, **SMALL[cfg])

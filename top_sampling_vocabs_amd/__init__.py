@@ -13,6 +13,6 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     ROW_OK, ROW_EMPTY, ROW_ALL_NEG_INF, ROW_NONFINITE, ROW_BAD_PARAM,
     ROW_CAND_OVERFLOW, ROW_INTERNAL, FLAG_FORCE_MISS, FLAG_NO_TRUNCATION,
-    FLAG_PIVOT_SEARCH, FLAG_STREAM, FLAG_BINARY_PIVOT)
+    FLAG_PIVOT_SEARCH, FLAG_STREAM, FLAG_BINARY_PIVOT, FLAG_SORT_SUBSET)
 
 __version__ = "0.1.0"

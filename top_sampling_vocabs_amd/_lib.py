@@ -33,6 +33,7 @@ FLAG_NO_TRUNCATION = 2
 FLAG_PIVOT_SEARCH = 4
 FLAG_STREAM = 8
 FLAG_BINARY_PIVOT = 16
+FLAG_SORT_SUBSET = 32
 
 # size of the fixed per-GPU scratch behind qs_sample_noalloc (QS_SCRATCH_BYTES)
 SCRATCH_BYTES = 64 << 20

@@ -71,7 +71,7 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
   if (rc != QS_OK) return rc;
   if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION | QS_FLAG_PIVOT_SEARCH |
-                QS_FLAG_STREAM | QS_FLAG_BINARY_PIVOT))
+                QS_FLAG_STREAM | QS_FLAG_BINARY_PIVOT | QS_FLAG_SORT_SUBSET))
     return QS_ERR_INVALID_ARG;
   if (B == 0) return QS_OK;
   if (!temperature || !top_k || !top_p || !row_status) return QS_ERR_INVALID_ARG;

@@ -110,7 +110,8 @@ __device__ __forceinline__ double weight(uint32_t key, double m, double invT) {
 // NL == 0: the row streams through a prefetch ring.
 // P: logit processors applied in the kernel: 0 none (the instances hold none
 // of their code), 1 repetition and presence penalties only, 2 any.
-template <int DT, bool SAMPLE, int NL, int P>
+// SRT: the instance holds the sorted-subset ablation switch.
+template <int DT, bool SAMPLE, int NL, int P, bool SRT>
 __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   using K = Keys<DT>;
   using PL = PoolLayout<DT>;
@@ -131,6 +132,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   __shared__ RedScratch red;
   __shared__ RowInfo info;
   __shared__ uint32_t s_proc[P ? 20 : 1];  // logit processors: block-scan totals and a flag
+  __shared__ uint32_t s_sort[1];  // the sorted-subset switch: a counter, a claim
 
   PKey* const pool_key = reinterpret_cast<PKey*>(pool_raw);
   uint16_t* const pool_id = reinterpret_cast<uint16_t*>(pool_raw + sizeof(PKey) * kWaves * kCap);
@@ -983,7 +985,8 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   // test N_tau >= k > N_tau - N_zm evaluated at every key) and the top-p
   // boundary (suffix fp64 masses reaching p * W) with DPP prefix sums; the
   // other waves wait at the barrier that publishes the result.
-  if (hist_t && !(a.flags & QS_FLAG_PIVOT_SEARCH) && use_pool) {
+  if (hist_t && !(a.flags & (QS_FLAG_PIVOT_SEARCH | (SRT ? QS_FLAG_SORT_SUBSET : 0u))) &&
+      use_pool) {
     const bool tk = kk > 0 && (uint32_t)kk < ccount;
     double bg_mass = bgm;
     double bg_bound = bgb;
@@ -1577,6 +1580,140 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           src_lo = lk;
         }
       }
+    }
+  }
+
+  // Ablation switch (page "Qrita", ablation table, run I): on a truncation
+  // hit the candidate subset is sorted in LDS (keys descending, a bitonic
+  // network over the next power of two, at most kSortMax candidates) and the
+  // top-k and top-p boundaries are read off the sorted order instead of
+  // searched. Larger subsets, and top-p cuts the subset does not reach, take
+  // the searches below. The buffer is LDS the searches do not use then: the
+  // radix bins (fp32) or the background histogram (bf16, read before).
+  // (bf16 keys are 16-bit: 2 bytes an entry)
+  constexpr uint32_t kSortMax = 8192u;
+  using SKey = typename PL::KeyT;
+  SKey* const sbuf = reinterpret_cast<SKey*>(DT == 0 ? rb_f32 : bgh);
+  static_assert(sizeof(rb_f32) >= kSortMax * sizeof(SKey) || DT == 1, "fp32 sort buffer");
+  static_assert(sizeof(bgh) >= kSortMax * sizeof(SKey) || DT == 0, "bf16 sort buffer");
+  if (SRT && (a.flags & QS_FLAG_SORT_SUBSET) && use_pool && !settled && !greedy) {
+    if (tid == 0) s_sort[0] = 0u;
+    __syncthreads();
+    walk_pool<DT>(pk, pid, my_cnt, (uint32_t)sl.wb, lane,
+                  [&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm)
+                      __attribute__((always_inline)) {
+      if (vm) {
+        uint32_t at = __hip_atomic_fetch_add(s_sort, (uint32_t)__popc(vm), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((vm >> j) & 1u) {
+            if (at < kSortMax) sbuf[at] = (SKey)key[j];
+            ++at;
+          }
+        }
+      }
+    });
+    __syncthreads();
+    const uint32_t n = uni(s_sort[0]);
+    if (n <= kSortMax) {
+      uint32_t N = 2u;
+      while (N < n) N <<= 1;
+      for (uint32_t i = n + (uint32_t)tid; i < N; i += kThreads) sbuf[i] = (SKey)0;  // below every key
+      __syncthreads();
+      for (uint32_t size = 2u; size <= N; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1) {
+          for (uint32_t t = (uint32_t)tid; t < N / 2u; t += kThreads) {
+            const uint32_t i = 2u * t - (t & (stride - 1u));
+            const uint32_t j = i + stride;
+            const SKey x = sbuf[i], y = sbuf[j];
+            const bool down = (i & size) == 0u;  // this run of `size` ends descending
+            if (down ? x < y : x > y) {
+              sbuf[i] = y;
+              sbuf[j] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      // entries of the sorted subset's first lim that lie above key x
+      auto sorted_above = [&](uint32_t x, uint32_t lim) -> uint32_t {
+        double c = 0.0;
+        for (uint32_t i = (uint32_t)tid; i < lim; i += kThreads)
+          c += (uint32_t)sbuf[i] > x ? 1.0 : 0.0;
+        return (uint32_t)block_sum_f64(c);
+      };
+      // top-k: the k-th entry and the entries above it
+      uint32_t skap = 0u, snk = 0u;
+      if (topk_eff) {
+        skap = uni((uint32_t)sbuf[kk - 1]);
+        snk = (uint32_t)kk - sorted_above(skap, (uint32_t)kk);
+      }
+      if (topp_on) {
+        // top-p over the sorted top-k set (every entry without top-k): running
+        // fp64 sums, thread t taking a run of consecutive entries; the cut is
+        // the first entry whose running sum reaches p W (the smallest index
+        // any thread claims). A cut the subset does not reach, or one that the
+        // fp32 background's error bound leaves open, goes to the searches.
+        const double w_ref = topk_eff ? mass_above(skap) + (double)snk * wkey(skap)
+                                      : (w_f >= 0.0 ? w_f : mass_above(0u));
+        const double err = topk_eff ? 0.0 : w_f_err;
+        const double target = p * w_ref;
+        const uint32_t L = topk_eff ? (uint32_t)kk : n;
+        const uint32_t c = (L + kThreads - 1u) / kThreads;
+        const uint32_t i0 = min((uint32_t)tid * c, L), i1 = min(i0 + c, L);
+        double sw = 0.0;
+        for (uint32_t i = i0; i < i1; ++i) sw += wkey((uint32_t)sbuf[i]);
+        const double incl = scan_incl_f64(sw);
+        if (lane == 63) info.mass[w] = incl;
+        if (tid == 0) s_sort[0] = 0xFFFFFFFFu;
+        __syncthreads();
+        double cum = incl - sw;
+        for (int ww = 0; ww < kWaves; ++ww) cum += ww < w ? info.mass[ww] : 0.0;
+        double prev = 0.0, at = 0.0;
+        uint32_t jx = 0xFFFFFFFFu;
+        if (cum < target) {
+          for (uint32_t i = i0; i < i1; ++i) {
+            const double wi = wkey((uint32_t)sbuf[i]);
+            if (cum + wi >= target) {
+              jx = i;
+              prev = cum;
+              at = cum + wi;
+              break;
+            }
+            cum += wi;
+          }
+        }
+        if (jx != 0xFFFFFFFFu)
+          __hip_atomic_fetch_min(s_sort, jx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
+        const uint32_t jw = uni(s_sort[0]);
+        if (jx != 0xFFFFFFFFu && jx == jw) {
+          info.sel_d[0] = prev;
+          info.sel_d[1] = at;
+        }
+        __syncthreads();
+        if (jw != 0xFFFFFFFFu) {
+          const double pv = uni(info.sel_d[0]), w_p = uni(info.sel_d[1]);
+          const bool open = err > 0.0 && !(pv < p * (w_ref - err) && p * (w_ref + err) <= w_p);
+          if (!open) {
+            pstar = uni((uint32_t)sbuf[jw]);
+            n_keep = jw + 1u - sorted_above(pstar, jw + 1u);
+            w_star = wkey(pstar);
+            kap = skap;
+            n_keep_k = snk;
+            settled = true;
+          }
+        }
+      } else if (topk_eff) {
+        kap = skap;
+        n_keep_k = snk;
+        pstar = skap;
+        n_keep = snk;
+        w_star = wkey(skap);
+        settled = true;
+      }
+      ++rounds;
     }
   }
 
@@ -2201,22 +2338,22 @@ inline int resident_steps(int V) {
   return (per_wave + kStep - 1) / kStep;
 }
 
-template <int DT, bool S, int P>
+template <int DT, bool S, int P, bool SRT>
 hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
   dim3 grid((unsigned)B), block(kThreads);
   const int n = resident_steps(a.V);
   const bool stream = (a.flags & QS_FLAG_STREAM) != 0u;
   if (!stream && n <= kResidentTier[DT][0]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0], P>), grid, block, 0, st,
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0], P, SRT>), grid, block, 0, st,
                        a);
   } else if (!stream && n <= kResidentTier[DT][1]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1], P>), grid, block, 0, st,
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1], P, SRT>), grid, block, 0, st,
                        a);
   } else {
     a.seg = seg_for(a.V);
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0, P>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0, P, SRT>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -4,10 +4,12 @@
 namespace qs {
 
 hipError_t launch_filter_bf16_proc(const FilterArgs& a, bool sample, int B, hipStream_t st);
+hipError_t launch_filter_bf16_sort(const FilterArgs& a, bool sample, int B, hipStream_t st);
 
 hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream_t st) {
   if (a.p_on) return launch_filter_bf16_proc(a, sample, B, st);
-  return sample ? launch_dt<1, true, 0>(a, B, st) : launch_dt<1, false, 0>(a, B, st);
+  if (a.flags & QS_FLAG_SORT_SUBSET) return launch_filter_bf16_sort(a, sample, B, st);
+  return sample ? launch_dt<1, true, 0, false>(a, B, st) : launch_dt<1, false, 0, false>(a, B, st);
 }
 
 bool filter_row_resident(int dtype, int V) {

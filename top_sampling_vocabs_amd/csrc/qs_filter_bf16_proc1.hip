@@ -6,7 +6,7 @@
 namespace qs {
 
 hipError_t launch_filter_bf16_proc1(const FilterArgs& a, bool sample, int B, hipStream_t st) {
-  return sample ? launch_dt<1, true, 1>(a, B, st) : launch_dt<1, false, 1>(a, B, st);
+  return sample ? launch_dt<1, true, 1, false>(a, B, st) : launch_dt<1, false, 1, false>(a, B, st);
 }
 
 }  // namespace qs

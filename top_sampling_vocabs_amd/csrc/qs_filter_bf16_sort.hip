@@ -1,0 +1,12 @@
+// bf16 instances of the filter/sample kernel holding the sorted-subset
+// ablation switch (their own translation unit: the other instances hold none
+// of its code).
+#include "qs_filter.hpp"
+
+namespace qs {
+
+hipError_t launch_filter_bf16_sort(const FilterArgs& a, bool sample, int B, hipStream_t st) {
+  return sample ? launch_dt<1, true, 0, true>(a, B, st) : launch_dt<1, false, 0, true>(a, B, st);
+}
+
+}  // namespace qs

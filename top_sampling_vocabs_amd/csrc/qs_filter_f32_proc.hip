@@ -6,7 +6,7 @@
 namespace qs {
 
 hipError_t launch_filter_f32_proc(const FilterArgs& a, bool sample, int B, hipStream_t st) {
-  return sample ? launch_dt<0, true, 2>(a, B, st) : launch_dt<0, false, 2>(a, B, st);
+  return sample ? launch_dt<0, true, 2, true>(a, B, st) : launch_dt<0, false, 2, true>(a, B, st);
 }
 
 }  // namespace qs
