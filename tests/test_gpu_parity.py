@@ -617,3 +617,41 @@ def test_histogram_huge_negative_logits(qs):
     assert st[9] == oracle.ROW_NONFINITE
     on_path = [0, 1, 2, 3, 4, 5, 6, 8]
     assert (dbg[on_path, 0] == 0).all() and (dbg[on_path, 1] == 0).all(), dbg.tolist()
+
+
+@pytest.mark.gpu
+def test_histogram_error_rows(qs):
+    """bf16 error rows: no legal token (EMPTY) and a legal +inf (NONFINITE),
+    which the value-histogram path reports itself, and rows whose every legal
+    value is -inf (ALL_NEG_INF, also with NaN at illegal positions), which
+    the truncation path reports. Rows mixing -inf with finite negative values
+    or -0 are not errors. Statuses, zeroed outputs and tokens must match the
+    oracle."""
+    rng = np.random.default_rng(2024)
+    B, V = 8, 30000
+    z = (3.0 * rng.standard_normal((B, V))).astype(np.float32)
+    bits = rng.random((B, V)) < 0.3
+    bits[0] = False                                   # EMPTY
+    z[1, np.nonzero(bits[1])[0][3]] = np.inf          # NONFINITE
+    z[2] = -np.inf                                    # ALL_NEG_INF
+    z[3, bits[3]] = -np.inf                           # ALL_NEG_INF (legal ones only)
+    z[3, np.nonzero(~bits[3])[0][:5]] = np.nan
+    z[4] = -np.inf
+    z[4, np.nonzero(bits[4])[0][7]] = -3.0            # one finite legal value: not an error
+    z[5] = -np.inf
+    z[5, np.nonzero(bits[5])[0][2]] = -0.0            # -0 among -inf: not an error
+    z[6] = -np.abs(z[6]) - 1.0                        # all negative: not an error
+    T = np.ones(B, np.float32)
+    k = np.full(B, 40, np.int32)
+    p = np.full(B, 0.9, np.float32)
+    w = workloads.Workload(cfg=3, dtype="bf16", logits=workloads.f32_to_bf16_bits(z),
+                           T=T, k=k, p=p, bitmask=workloads.pack_bits(bits),
+                           seeds=np.arange(B, dtype=np.uint64),
+                           offsets=np.zeros(B, np.uint64))
+    rep, out = check_workload(qs, w, seed=6, cand_cap=V)
+    st = out["status"].cpu().numpy()
+    assert st[:4].tolist() == [oracle.ROW_EMPTY, oracle.ROW_NONFINITE, oracle.ROW_ALL_NEG_INF,
+                               oracle.ROW_ALL_NEG_INF], st.tolist()
+    assert (st[4:] == oracle.ROW_OK).all(), st.tolist()
+    dbg = out["debug"].cpu().numpy()
+    assert (dbg[:2] == 0).all(), dbg.tolist()        # reported by the histogram path
