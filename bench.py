@@ -46,7 +46,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--sets", type=int, default=4,
                     help="distinct input sets rotated through (default 4 > 256 MB MALL)")
-    ap.add_argument("--cand-cap", type=int, default=8192)
+    ap.add_argument("--cand-cap", type=int, default=0,
+                    help="candidate-list capacity per row; 0 (the default): V, so every "
+                         "kept token is written (the line counts rows whose kept set "
+                         "overflowed a smaller capacity)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle baseline takes row chunks of the input sets, in "
                          "order and cyclically, until this much wall time has passed")
@@ -86,6 +89,8 @@ class Prepared:
         import top_sampling_vocabs_amd as qs
         dev = "cuda"
         self.w = w
+        cand_cap = cand_cap if cand_cap > 0 else w.V  # 0: room for every kept token
+        self.cand_cap = cand_cap
         if w.dtype == "bf16":
             self.logits = torch.from_numpy(w.logits.view(np.int16)).to(dev).view(torch.bfloat16)
         else:
@@ -792,6 +797,9 @@ def main():
     # sanity: every row OK or an expected degenerate status
     st = preps[0].status.cpu().numpy()
     assert ((st == 0) | (st == 1) | (st == 2) | (st == 3) | (st == 5)).all(), np.unique(st)
+    # rows of every input set whose kept set was longer than the lists (their
+    # lists hold the first cand_cap entries only)
+    overflow_rows = int(sum(int((p_.status == 5).sum()) for p_ in preps))
 
     copy = copy_calibration(preps) if args.copy_calibration else None
 
@@ -820,7 +828,8 @@ def main():
                                                        if args.outliers else ""),
                    "batch_rows": B, "vocab": base.V,
                    "input_sets": len(sets), "bytes_read_per_step": bytes_read,
-                   "cand_cap": args.cand_cap,
+                   "cand_cap": preps[0].cand_cap,
+                   "cand_overflow_rows": overflow_rows,
                    "launch": launch_mode, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
