@@ -387,6 +387,57 @@ def toplp_bench(args, lib, stream):
     stats = [pr.bytes_moved() for pr in preps]
     nbytes = sum(s[0] for s in stats) / len(stats)
     B = preps[0].args[0]
+    del graph
+
+    # the sampling step alone, then with the separate call on its lists, then
+    # with the top tokens written by the sampling launch itself
+    # (qs_sample_top_logprobs); candidate lists of capacity V
+    sets = [workloads.make(args.workload, seed=workloads.BASE_SEED + args.workload + 1000 * i)
+            for i in range(args.sets)]
+    samp = [Prepared(lib, w, 0, 0, stream) for w in sets]
+    n = args.toplp
+
+    class Then:
+        def __init__(self, sp):
+            import torch
+            self.sp = sp
+            P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+            self.ids = torch.empty(sp.w.B, n, dtype=torch.int32, device="cuda")
+            self.lp = torch.empty(sp.w.B, n, dtype=torch.float32, device="cuda")
+            self.st = torch.empty(sp.w.B, dtype=torch.int32, device="cuda")
+            self.targs = (sp.w.B, P(sp.cids), P(sp.cprobs), P(sp.ccount), sp.cand_cap, n,
+                          P(self.ids), P(self.lp), P(self.st))
+            a_ = sp.args
+            self.fargs = a_[:-3] + (n, P(self.ids), P(self.lp)) + a_[-3:]
+
+        def call(self, stream=None, flags=None):
+            self.sp.call(stream)
+            rc = lib.qs_top_logprobs(*(self.targs + (stream,)))
+            if rc != 0:
+                raise RuntimeError(f"qs_top_logprobs returned {rc}")
+
+    class Fused(Then):
+        def call(self, stream=None, flags=None):
+            rc = lib.qs_sample_top_logprobs(*(self.fargs[:-1] + (stream,)))
+            if rc != 0:
+                raise RuntimeError(f"qs_sample_top_logprobs returned {rc}")
+
+    times = {}
+    for name, calls in (("sample", samp), ("sample_then_top_logprobs", [Then(sp) for sp in samp]),
+                        ("sample_with_top_logprobs", [Fused(sp) for sp in samp])):
+        for i in range(args.warmup):
+            calls[i % len(calls)].call()
+        torch.cuda.synchronize()
+        ms_, g_, cs_ = time_graph(calls, args.steps)
+        del g_
+        times[name] = round(ms_ / args.steps, 5)
+        if name == "sample_with_top_logprobs":  # the same slots as the separate call
+            ref = Then(calls[0].sp)
+            ref.call()
+            calls[0].call()
+            torch.cuda.synchronize()
+            assert torch.equal(calls[0].ids, ref.ids)
+            assert torch.equal(calls[0].lp.view(torch.int32), ref.lp.view(torch.int32))
     line = {
         "metric": f"top-{args.toplp} logprobs rows/sec over candidate lists, B=256 V=151936",
         "value": round(B / (per * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
@@ -395,7 +446,10 @@ def toplp_bench(args, lib, stream):
         "data": "synthetic",
         "config": {"workload": "candidate lists (cap 16384) of the B=256 V=151936 bf16 batch",
                    "n": args.toplp,
-                   "mean_list_length": round(float(np.mean([s[1] for s in stats])), 1)},
+                   "mean_list_length": round(float(np.mean([s[1] for s in stats])), 1),
+                   "sample_ms": times["sample"],
+                   "sample_then_top_logprobs_ms": times["sample_then_top_logprobs"],
+                   "sample_with_top_logprobs_in_launch_ms": times["sample_with_top_logprobs"]},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (per * 1e-3) / 1e9, 1),
                      "peak": 8000.0, "unit": "GB/s",
                      "frac": round(nbytes / (per * 1e-3) / 8e12, 5), "traffic": None,

@@ -265,6 +265,34 @@ QS_API int qs_spec_verify(int64_t B, const int32_t* target_ids, const float* tar
                    const double* u_resample, int32_t* tokens, int32_t* accepted,
                    int32_t* row_status, void* stream);
 
+/* qs_sample that also writes each row's n most probable tokens and their
+ * log-probabilities, as qs_top_logprobs would read them off the candidate
+ * lists this call writes (page "Sampling 系统设计：从 logits 到可控生成",
+ * logprobs section: top tokens with their log-probabilities besides the
+ * chosen one's), in the same launch: each row's workgroup reads its own list
+ * back once it is written. Arguments and outputs are qs_sample's, plus
+ *   top_n        1 <= top_n <= 64 (QS_ERR_INVALID_ARG otherwise)
+ *   top_ids      [B][top_n] int32 out: the ids, probability descending
+ *                (float32 values compared exactly), ties by ascending id; -1
+ *                past the list's length
+ *   top_logprobs [B][top_n] float32 out: ln q (ln 2 (e + log2 m) from frexp and
+ *                the hardware log2, within about 1e-7); -inf past the list's
+ *                length and for q = 0
+ * cand_ids and cand_probs are required (the source of the top tokens); a row
+ * whose status is not QS_ROW_OK (a row error, or QS_ROW_CAND_OVERFLOW: the
+ * list was truncated to cand_cap, so its top tokens are not known) gets every
+ * slot empty. */
+QS_API int qs_sample_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V,
+              int64_t row_stride, const float* temperature,
+              const int32_t* top_k, const float* top_p,
+              const uint32_t* bitmask, int64_t bitmask_stride,
+              const uint64_t* seed, uint64_t* offset, const double* uniforms,
+              int32_t* tokens, float* logprobs, uint32_t* keep_mask, int32_t* cand_ids,
+              float* cand_probs, int32_t* cand_count, int64_t cand_cap,
+              float* dense_probs, int32_t* row_status, int32_t* debug_stats,
+              uint32_t flags, int64_t top_n, int32_t* top_ids, float* top_logprobs,
+              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Logit processors applied inside qs_sample_processed / qs_filter_mask_processed
  * (page "Sampling 系统设计：从 logits 到可控生成", repetition-penalty and
  * LogitsProcessor sections: history-dependent processors edit the logits

@@ -40,6 +40,7 @@ SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("qs_workspace_bytes", "qs_filter_mask", "qs_sample", "qs_sample_noalloc", "qs_argmax",
            "qs_processors_workspace_bytes", "qs_sample_processed", "qs_filter_mask_processed",
+           "qs_sample_top_logprobs",
            "qs_spec_verify",
            "qs_apply_penalties", "qs_apply_logit_bias", "qs_top_logprobs", "qs_version")
 
@@ -95,6 +96,9 @@ def load(path=LIB_PATH):
     lib.qs_processors_workspace_bytes.argtypes = [_i64, _i64, _i32]   # B, V, dtype
     lib.qs_sample_processed.restype = _i32
     lib.qs_sample_processed.argtypes = lib.qs_sample.argtypes[:-3] + [_p, _p, _sz, _p]
+    lib.qs_sample_top_logprobs.restype = _i32
+    lib.qs_sample_top_logprobs.argtypes = lib.qs_sample.argtypes[:-3] + [_i64, _p, _p, _p, _sz,
+                                                                         _p]
     lib.qs_filter_mask_processed.restype = _i32
     lib.qs_filter_mask_processed.argtypes = lib.qs_filter_mask.argtypes[:-3] + [_p, _p, _sz, _p]
     lib.qs_argmax.restype = _i32
@@ -293,7 +297,7 @@ def processors_workspace_for(logits):
 
 def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset=None,
            uniforms=None, keep_mask=False, cand_cap=0, dense=False, debug=False,
-           logprobs=False, flags=0, workspace=None, processors=None):
+           logprobs=False, flags=0, workspace=None, processors=None, top_n=0):
     """Filter and draw one token per row.
 
     seed, offset: int64 [B] CUDA tensors holding the uint64 RNG state; offset is
@@ -304,10 +308,13 @@ def sample(logits, temperature, top_k, top_p, bitmask=None, *, seed=None, offset
     and the optional outputs of filter_mask. workspace as for filter_mask.
     processors: a dict of logit-processor tensors (see _processors_args),
     applied inside the call (qs_sample_processed); the logits are only read.
+    top_n: also return each row's top_n most probable tokens (top_ids [B, n]
+    int32) and their log-probabilities (top_logprobs [B, n] float32), written
+    by the same launch (qs_sample_top_logprobs; needs cand_cap).
     """
     return _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms,
                    keep_mask, cand_cap, dense, debug, logprobs, flags, workspace, False,
-                   processors)
+                   processors, top_n)
 
 
 def sample_noalloc(logits, temperature, top_k, top_p, bitmask=None, *, seed=None,
@@ -321,7 +328,8 @@ def sample_noalloc(logits, temperature, top_k, top_p, bitmask=None, *, seed=None
 
 
 def _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms, keep_mask,
-            cand_cap, dense, debug, logprobs, flags, workspace, noalloc, processors=None):
+            cand_cap, dense, debug, logprobs, flags, workspace, noalloc, processors=None,
+            top_n=0):
     import torch
     lib = load()
     B, V = _check_logits(logits, bitmask)
@@ -369,6 +377,13 @@ def _sample(logits, temperature, top_k, top_p, bitmask, seed, offset, uniforms, 
         _status(rc, "qs_sample_processed")
         return out
     ws_p, ws_n, _ws = _workspace_args(workspace, logits, cand_cap)
+    if top_n:
+        out["top_ids"] = torch.empty((B, top_n), dtype=torch.int32, device=dev)
+        out["top_logprobs"] = torch.empty((B, top_n), dtype=torch.float32, device=dev)
+        rc = lib.qs_sample_top_logprobs(*args, int(top_n), _ptr(out["top_ids"]),
+                                        _ptr(out["top_logprobs"]), ws_p, ws_n, _stream(dev))
+        _status(rc, "qs_sample_top_logprobs")
+        return out
     rc = lib.qs_sample(*args, ws_p, ws_n, _stream(dev))
     _status(rc, "qs_sample")
     return out

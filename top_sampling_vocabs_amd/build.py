@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqs.so")
 SOURCES = ["qs_filter_bf16.hip", "qs_filter_f32.hip", "qs_filter_bf16_proc.hip",
            "qs_filter_f32_proc.hip", "qs_filter_bf16_proc1.hip",
-           "qs_filter_bf16_sort.hip", "qs_filter_f32_sort.hip", "qs_chunk.hip", "qs_api.hip",
+           "qs_filter_bf16_sort.hip", "qs_filter_f32_sort.hip", "qs_filter_bf16_topn.hip",
+           "qs_filter_f32_topn.hip", "qs_chunk.hip", "qs_api.hip",
            "qs_spec.hip", "qs_penalty.hip", "qs_toplp.hip"]
 ARCH = os.environ.get("QS_OFFLOAD_ARCH", "gfx950")
 

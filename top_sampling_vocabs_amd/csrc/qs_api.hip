@@ -15,6 +15,7 @@
 #include "qs_chunk.hpp"
 #include "qs_launch.hpp"
 #include "qs_proc.hpp"
+#include "qs_topn.hpp"
 
 namespace {
 
@@ -67,7 +68,8 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
                   float* cand_probs,
                   int32_t* cand_count, int64_t cand_cap, float* dense_probs,
                   int32_t* row_status, int32_t* debug_stats, uint32_t flags, void* workspace,
-                  size_t workspace_bytes, void* stream, const QsProcessors* proc = nullptr) {
+                  size_t workspace_bytes, void* stream, const QsProcessors* proc = nullptr,
+                  int64_t top_n = 0, int32_t* top_ids = nullptr, float* top_logprobs = nullptr) {
   int rc = check_input(logits, dtype, B, V, row_stride, bitmask, bitmask_stride);
   if (rc != QS_OK) return rc;
   if (flags & ~(QS_FLAG_FORCE_MISS | QS_FLAG_NO_TRUNCATION | QS_FLAG_PIVOT_SEARCH |
@@ -105,6 +107,12 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
         !aligned(proc->repetition_penalty, 4) || !aligned(proc->presence_penalty, 4) ||
         !aligned(proc->frequency_penalty, 4) || !aligned(proc->bias_ids, 4) ||
         !aligned(proc->bias_values, 4) || !aligned(proc->bias_count, 4))
+      return QS_ERR_INVALID_ARG;
+  }
+  if (top_n != 0) {
+    // the top tokens are read off the candidate lists the call writes
+    if (top_n < 1 || top_n > qs::kTopNMax || !top_ids || !top_logprobs || !cand_ids ||
+        !cand_probs || proc || !aligned(top_ids, 4) || !aligned(top_logprobs, 4))
       return QS_ERR_INVALID_ARG;
   }
   const size_t need = proc ? proc_ws_bytes(B, V, dtype) : ws_bytes(B, V, dtype);
@@ -145,6 +153,9 @@ int filter_common(bool sample, const void* logits, int dtype, int64_t B, int64_t
   a.p_rep = nullptr; a.p_pres = nullptr; a.p_freq = nullptr;
   a.p_bias_ids = nullptr; a.p_bias_vals = nullptr; a.p_bias_cap = 0; a.p_bias_count = nullptr;
   a.p_copy = nullptr; a.p_copy_bytes = 0;
+  a.top_n = (int)top_n;
+  a.top_ids = top_ids;
+  a.top_lp = top_logprobs;
   if (proc) {
     a.p_on = 1;
     if (proc->history) {
@@ -284,6 +295,24 @@ int qs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_s
                        bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
                        keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs, row_status,
                        debug_stats, flags, workspace, workspace_bytes, stream);
+}
+
+int qs_sample_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V,
+                           int64_t row_stride, const float* temperature, const int32_t* top_k,
+                           const float* top_p, const uint32_t* bitmask, int64_t bitmask_stride,
+                           const uint64_t* seed, uint64_t* offset, const double* uniforms,
+                           int32_t* tokens, float* logprobs, uint32_t* keep_mask,
+                           int32_t* cand_ids, float* cand_probs, int32_t* cand_count,
+                           int64_t cand_cap, float* dense_probs, int32_t* row_status,
+                           int32_t* debug_stats, uint32_t flags, int64_t top_n, int32_t* top_ids,
+                           float* top_logprobs, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (top_n == 0) return QS_ERR_INVALID_ARG;
+  return filter_common(true, logits, dtype, B, V, row_stride, temperature, top_k, top_p,
+                       bitmask, bitmask_stride, seed, offset, uniforms, tokens, logprobs,
+                       keep_mask, cand_ids, cand_probs, cand_count, cand_cap, dense_probs,
+                       row_status, debug_stats, flags, workspace, workspace_bytes, stream,
+                       nullptr, top_n, top_ids, top_logprobs);
 }
 
 int qs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,

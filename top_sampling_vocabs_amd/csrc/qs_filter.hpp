@@ -46,6 +46,7 @@
 #include "qs_stream.hpp"
 #include "qs_bins.hpp"
 #include "qs_proc.hpp"
+#include "qs_topn.hpp"
 #include "../../include/qs.h"
 
 namespace qs {
@@ -111,8 +112,10 @@ __device__ __forceinline__ double weight(uint32_t key, double m, double invT) {
 // P: logit processors applied in the kernel: 0 none (the instances hold none
 // of their code), 1 repetition and presence penalties only, 2 any.
 // SRT: the instance holds the sorted-subset ablation switch.
+// One row (workgroup blockIdx.x); returns the workgroup's pool LDS, free again
+// once every thread has returned.
 template <int DT, bool SAMPLE, int NL, int P, bool SRT>
-__global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
+__device__ __forceinline__ uint8_t* filter_row(FilterArgs a) {
   using K = Keys<DT>;
   using PL = PoolLayout<DT>;
   using PKey = typename PL::KeyT;
@@ -146,7 +149,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       const int tid = threadIdx.x;
       if (merge_row<SAMPLE>(a, r, tid, w, tid & 63, pool_raw, &stage[0][0], hist, binw, red,
                             info))
-        return;
+        return pool_raw;
       __syncthreads();  // the other paths reuse the LDS
     }
   }
@@ -172,7 +175,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       if (select_row<SAMPLE, NL, P>(a, sl, r, w, lane, tid, W, bmrow, mask_row, dense_row,
                                  pool_raw, stage, lut, reinterpret_cast<double*>(bgh), red,
                                  info, s_proc))
-        return;
+        return pool_raw;
       __syncthreads();  // the general path reuses the LDS
     }
   }
@@ -224,7 +227,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
           a.dbg[4 * r + 2] = 0; a.dbg[4 * r + 3] = 0;
         }
       }
-      return;
+      return pool_raw;
     }
     if (prm.need_cnt || prm.has_b) proc::build_ranks(a, r, prm, pt, tid, s_proc);
     // copy in 16-byte pieces; the edited tokens of a piece are rewritten first
@@ -273,7 +276,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       if (DT == 0) reinterpret_cast<uint32_t*>(dst)[e] = raw;
       else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)raw;
     }
-    __threadfence();
+    // the copy's stores have completed before this workgroup reads it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // the copy is complete; the LDS is the general path's again
     sl.row = dst;
   }
@@ -365,7 +370,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   const float pf = a.p[r];
   if (!(isfinite(Tf) && Tf >= 0.0f) || kk < 0 || !(pf > 0.0f && pf <= 1.0f)) {
     finish_error(QS_ROW_BAD_PARAM);
-    return;
+    return pool_raw;
   }
   const bool greedy = (Tf == 0.0f);
   const double invT = greedy ? 0.0 : 1.0 / (double)Tf;
@@ -933,9 +938,9 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   nonfinite = nonfinite || maxk >= K::kPosInf;
 
   // -- row status --------------------------------------------------------------
-  if (!any_legal) { finish_error(QS_ROW_EMPTY); return; }
-  if (nonfinite) { finish_error(QS_ROW_NONFINITE); return; }
-  if (maxk <= K::kNegInf) { finish_error(QS_ROW_ALL_NEG_INF); return; }
+  if (!any_legal) { finish_error(QS_ROW_EMPTY); return pool_raw; }
+  if (nonfinite) { finish_error(QS_ROW_NONFINITE); return pool_raw; }
+  if (maxk <= K::kNegInf) { finish_error(QS_ROW_ALL_NEG_INF); return pool_raw; }
 
   const double m = (double)K::value(maxk);
 
@@ -2022,7 +2027,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
   }
   if (failed) {
     finish_error(QS_ROW_INTERNAL);
-    return;
+    return pool_raw;
   }
   if (pstar == K::kNegInf) n_keep = 0u;
 
@@ -2268,6 +2273,7 @@ __global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
       a.dbg[4 * r + 3] = (int32_t)n_p;
     }
   }
+  return pool_raw;
 }
 
 // ---------------------------------------------------------------------------
@@ -2338,22 +2344,29 @@ inline int resident_steps(int V) {
   return (per_wave + kStep - 1) / kStep;
 }
 
-template <int DT, bool S, int P, bool SRT>
+// T: the instance also writes each row's top-n tokens (after the row).
+template <int DT, bool SAMPLE, int NL, int P, bool SRT, bool T>
+__global__ void __launch_bounds__(kThreads) filter_rows_kernel(FilterArgs a) {
+  uint8_t* const lds = filter_row<DT, SAMPLE, NL, P, SRT>(a);
+  if constexpr (T) top_n_tail(a, lds);
+}
+
+template <int DT, bool S, int P, bool SRT, bool T = false>
 hipError_t launch_dt(FilterArgs a, int B, hipStream_t st) {
   dim3 grid((unsigned)B), block(kThreads);
   const int n = resident_steps(a.V);
   const bool stream = (a.flags & QS_FLAG_STREAM) != 0u;
   if (!stream && n <= kResidentTier[DT][0]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0], P, SRT>), grid, block, 0, st,
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][0], P, SRT, T>), grid, block, 0, st,
                        a);
   } else if (!stream && n <= kResidentTier[DT][1]) {
     a.seg = n * kStep;
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1], P, SRT>), grid, block, 0, st,
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, kResidentTier[DT][1], P, SRT, T>), grid, block, 0, st,
                        a);
   } else {
     a.seg = seg_for(a.V);
-    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0, P, SRT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((filter_rows_kernel<DT, S, 0, P, SRT, T>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

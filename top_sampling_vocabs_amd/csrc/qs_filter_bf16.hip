@@ -5,9 +5,11 @@ namespace qs {
 
 hipError_t launch_filter_bf16_proc(const FilterArgs& a, bool sample, int B, hipStream_t st);
 hipError_t launch_filter_bf16_sort(const FilterArgs& a, bool sample, int B, hipStream_t st);
+hipError_t launch_filter_bf16_topn(const FilterArgs& a, bool sample, int B, hipStream_t st);
 
 hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream_t st) {
   if (a.p_on) return launch_filter_bf16_proc(a, sample, B, st);
+  if (a.top_n > 0) return launch_filter_bf16_topn(a, sample, B, st);
   if (a.flags & QS_FLAG_SORT_SUBSET) return launch_filter_bf16_sort(a, sample, B, st);
   return sample ? launch_dt<1, true, 0, false>(a, B, st) : launch_dt<1, false, 0, false>(a, B, st);
 }

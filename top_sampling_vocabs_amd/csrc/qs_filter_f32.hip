@@ -13,11 +13,13 @@ int seg_for(int V) {
 hipError_t launch_filter_bf16(const FilterArgs& a, bool sample, int B, hipStream_t st);
 hipError_t launch_filter_f32_proc(const FilterArgs& a, bool sample, int B, hipStream_t st);
 hipError_t launch_filter_f32_sort(const FilterArgs& a, bool sample, int B, hipStream_t st);
+hipError_t launch_filter_f32_topn(const FilterArgs& a, bool sample, int B, hipStream_t st);
 hipError_t launch_argmax_bf16(const ArgmaxArgs& a, int B, hipStream_t st);
 
 hipError_t launch_filter(const FilterArgs& a, int dtype, bool sample, int B, hipStream_t st) {
   if (dtype == QS_F32) {
     if (a.p_on) return launch_filter_f32_proc(a, sample, B, st);
+    if (a.top_n > 0) return launch_filter_f32_topn(a, sample, B, st);
     if (a.flags & QS_FLAG_SORT_SUBSET) return launch_filter_f32_sort(a, sample, B, st);
     return sample ? launch_dt<0, true, 0, false>(a, B, st) : launch_dt<0, false, 0, false>(a, B, st);
   }

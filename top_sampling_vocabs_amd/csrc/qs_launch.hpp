@@ -57,6 +57,11 @@ struct FilterArgs {
   const int32_t* p_bias_count;
   uint8_t* p_copy;
   int64_t p_copy_bytes;
+  // the n most probable tokens of each row written after the row (top_n = 0:
+  // none): ids and log-probabilities, [B][top_n]
+  int top_n;
+  int32_t* top_ids;
+  float* top_lp;
 };
 
 struct ArgmaxArgs {
