@@ -391,10 +391,11 @@ def toplp_bench(args, lib, stream):
 
     # the sampling step alone, then with the separate call on its lists, then
     # with the top tokens written by the sampling launch itself
-    # (qs_sample_top_logprobs); candidate lists of capacity V
+    # (qs_sample_top_logprobs); lists of capacity 16384 (every kept token of
+    # this batch fits, and the separate call takes its register path)
     sets = [workloads.make(args.workload, seed=workloads.BASE_SEED + args.workload + 1000 * i)
             for i in range(args.sets)]
-    samp = [Prepared(lib, w, 0, 0, stream) for w in sets]
+    samp = [Prepared(lib, w, cap, 0, stream) for w in sets]
     n = args.toplp
 
     class Then:
