@@ -1842,6 +1842,63 @@ __device__ __forceinline__ uint8_t* filter_row(FilterArgs a) {
     }
   }
 
+  // -- top-p over a small top-k set (fp32, flags 0, the pool as source, k <= 64):
+  //    the set's keys are gathered, one wave sorts them and cuts at the first
+  //    running fp64 mass that reaches p W_K, instead of a bucket select over
+  //    the pool ----------------------------------------------------------------
+  if constexpr (DT == 0) {
+    if (radix && use_pool && topk_eff && topp_on && !settled && !failed && !greedy &&
+        kk <= 64) {
+      uint32_t* const sk = rb_f32;  // 64 keys, a counter, the result
+      if (tid == 0) sk[64] = 0u;
+      __syncthreads();
+      walk([&](const uint32_t (&key)[8], const uint32_t (&)[8], uint32_t vm)
+               __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (((vm >> j) & 1u) && key[j] > kap) {
+            const uint32_t at = __hip_atomic_fetch_add(sk + 64, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (at < 64u) sk[at] = key[j];
+          }
+        }
+      });
+      __syncthreads();
+      if (w == 0) {
+        // the set: the keys above kap and n_keep_k copies of kap (kk in all)
+        const uint32_t ca = sk[64];
+        uint32_t key = (uint32_t)lane < ca ? sk[lane]
+                       : ((uint32_t)lane < ca + n_keep_k ? kap : 0u);
+#pragma unroll
+        for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)key, stride, 64);
+            const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
+            key = take_max ? max(o, key) : min(o, key);
+          }
+        }
+        const bool on = lane < kk;
+        const double wt = on ? wkey(key) : 0.0;
+        const double incl = scan_incl_f64(wt);
+        const double target = p * readlane_f64(incl, 63);
+        const uint64_t hit = ballot(on && incl >= target);  // the last set entry reaches it
+        const int j = __ffsll((unsigned long long)hit) - 1;
+        const uint32_t ps = (uint32_t)__shfl((int)key, j, 64);
+        const int first = __ffsll((unsigned long long)ballot(key == ps)) - 1;
+        if (lane == 0) {
+          sk[65] = ps;
+          sk[66] = (uint32_t)(j + 1 - first);  // its ties needed
+        }
+      }
+      __syncthreads();
+      pstar = uni(sk[65]);
+      n_keep = uni(sk[66]);
+      w_star = wkey(pstar);
+      settled = true;
+    }
+  }
+
   // -- final boundary (pstar, n_keep): keep key > pstar, and the first n_keep
   //    ids of key == pstar --------------------------------------------------
   if (greedy) {
