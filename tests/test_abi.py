@@ -254,3 +254,52 @@ def test_sample_noalloc_rejects_before_any_hip_call(lib):
         fit += 1
     assert fit >= 256
     assert na(B=fit + 1, V=V, stride=V) == _lib.QS_ERR_WORKSPACE
+
+
+def smp_top(lib, top_n=5, top_ids=A16, top_lp=A16, **kw):
+    """qs_sample_top_logprobs with qs_sample's arguments (candidate lists on)."""
+    args = dict(logits=A16, dtype=1, B=4, V=64, stride=64, T=A16, k=A16, p=A16,
+                bitmask=None, bms=0, seed=A8, offset=A8, uni=None, tokens=A16, lp=None,
+                keep=None, cids=A16, cprobs=A16, ccount=A16, cap=64, dense=None,
+                status=A16, dbg=None, flags=0, ws=WS, wsn=WSN, stream=None)
+    args.update(kw)
+    return lib.qs_sample_top_logprobs(
+        args["logits"], args["dtype"], args["B"], args["V"], args["stride"], args["T"],
+        args["k"], args["p"], args["bitmask"], args["bms"], args["seed"], args["offset"],
+        args["uni"], args["tokens"], args["lp"], args["keep"], args["cids"], args["cprobs"],
+        args["ccount"], args["cap"], args["dense"], args["status"], args["dbg"], args["flags"],
+        top_n, top_ids, top_lp, args["ws"], args["wsn"], args["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_n=0), dict(top_n=65), dict(top_n=-3), dict(top_ids=None), dict(top_lp=None),
+    dict(top_ids=ctypes.c_void_p(0x100002)), dict(cids=None), dict(cprobs=None),
+    dict(tokens=None), dict(V=0),
+])
+def test_sample_top_logprobs_rejects_bad_arguments(lib, kw):
+    """The top tokens are read off the call's candidate lists: both lists are
+    required, and 1 <= top_n <= 64; checked before any launch."""
+    assert smp_top(lib, **kw) == _lib.QS_ERR_INVALID_ARG
+
+
+def test_processed_rejects_bad_arguments(lib):
+    """qs_sample_processed needs its processor struct; a group given in part,
+    or rows longer than the in-kernel table covers, are refused before any
+    launch; so is a workspace smaller than a row copy per row."""
+    def call(proc, V=64, wsn=WSN, ws=WS):
+        return lib.qs_sample_processed(
+            A16, 1, 4, V, V, A16, A16, A16, None, 0, A8, A8, None, A16, None, None, None, None,
+            None, 0, None, A16, None, 0, proc, ws, wsn, None)
+    assert call(None) == _lib.QS_ERR_INVALID_ARG
+    full = _lib.QsProcessors(0x300000, 8, 0x300100, 0x300200, 0x300300, None,
+                             None, None, 0, None)
+    part = _lib.QsProcessors(0x300000, 8, None, 0x300200, 0x300300, None, None, None, 0, None)
+    bias_part = _lib.QsProcessors(None, 0, None, None, None, None, 0x300000, None, 8, 0x300100)
+    assert call(ctypes.byref(part)) == _lib.QS_ERR_INVALID_ARG
+    assert call(ctypes.byref(bias_part)) == _lib.QS_ERR_INVALID_ARG
+    assert call(ctypes.byref(full), V=155649) == _lib.QS_ERR_INVALID_ARG
+    assert call(ctypes.byref(full), wsn=16) == _lib.QS_ERR_WORKSPACE
+    assert call(ctypes.byref(full), ws=None) == _lib.QS_ERR_WORKSPACE
+    need = lib.qs_processors_workspace_bytes(4, 64, 1)
+    assert need == 4 * 256
+    assert lib.qs_processors_workspace_bytes(4, 155649, 1) == 0
