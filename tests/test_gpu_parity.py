@@ -414,6 +414,21 @@ def test_parity_long_bf16_rows(qs, B, V):
     assert (dbg[:, 0] == 2).mean() > 0.3, np.bincount(dbg[:, 0])   # the chunked path ran
 
 
+@pytest.mark.parametrize("cfg", [3, 2])
+def test_parity_rows_past_16bit_slices(qs, cfg):
+    """Rows of more than 2^20 tokens (the longest the tests take): each wave's
+    slice then holds more than 65536 tokens, so the candidate pools (16-bit
+    offsets) are not used and every search runs over the whole row; bf16 rows
+    of this length also skip the chunked pass. Masks, lists, dense
+    probabilities and tokens must match the oracle (bf16: top-k, top-p and both;
+    fp32: top-k with top-p and a greedy row)."""
+    # (a row length whose rows start on 16-byte boundaries; not a multiple of
+    # a wave step)
+    w = workloads.make(cfg, B=4, V=(1 << 20) + 4136)
+    print(f"rows past 16-bit slices cfg={cfg} B={w.B} V={w.V} {w.dtype}", flush=True)
+    check_workload(qs, w, seed=11, cand_cap=w.V, dense=True)
+
+
 def test_topp_background_extremes(qs):
     """Rows with top-k off whose background (legal tokens below the truncation
     threshold) lies outside the exact bf16 value bins: values of magnitude
