@@ -18,6 +18,9 @@
  *   work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *   default stream). Row outputs are valid once the caller has synchronised
  *   with that stream. Concurrent calls on different streams are safe.
+ * - Sizes: 0 <= B <= 4194303 rows (2^22 - 1: one workgroup per row in a
+ *   single launch grid) and 1 <= V <= 2^30 tokens; other sizes are
+ *   QS_ERR_INVALID_ARG (entry points with a smaller V limit state it).
  * - Logits are row-major, `row_stride` elements apart (row_stride >= V).
  *   `logits` must be 16-byte aligned and row_stride * element size must be a
  *   multiple of 16 bytes.

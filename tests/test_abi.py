@@ -64,7 +64,7 @@ def filt(lib, **kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(logits=None), dict(dtype=2), dict(dtype=-1), dict(B=-1), dict(V=0),
+    dict(logits=None), dict(dtype=2), dict(dtype=-1), dict(B=-1), dict(B=1 << 22), dict(V=0),
     dict(stride=63), dict(stride=65), dict(logits=ctypes.c_void_p(0x100004)),
     dict(T=None), dict(k=None), dict(p=None), dict(status=None), dict(keep=None),
     dict(cids=A16, ccount=None, cap=8), dict(cids=A16, ccount=A16, cap=0),
@@ -168,7 +168,7 @@ def test_spec_verify_rejects_bad_arguments(lib):
         return lib.qs_spec_verify(a["B"], a["tids"], a["tp"], a["tc"], a["tcap"], a["dids"],
                                   a["dp"], a["dc"], a["dcap"], a["x"], a["u1"], a["u2"],
                                   a["tok"], a["acc"], a["status"], a["stream"])
-    for kw in (dict(B=-1), dict(tcap=0), dict(dcap=0), dict(tids=None), dict(dp=None),
+    for kw in (dict(B=-1), dict(B=1 << 22), dict(tcap=0), dict(dcap=0), dict(tids=None), dict(dp=None),
                dict(x=None), dict(u1=None), dict(u2=ctypes.c_void_p(0x200004)),
                dict(acc=ctypes.c_void_p(0x200002)), dict(status=None)):
         assert sv(**kw) == _lib.QS_ERR_INVALID_ARG, kw
@@ -183,7 +183,7 @@ def test_apply_penalties_rejects_bad_arguments(lib):
         return lib.qs_apply_penalties(a["logits"], a["dtype"], a["B"], a["V"], a["stride"],
                                       a["hist"], a["cap"], a["cnt"], a["rep"], a["pres"],
                                       a["freq"], a["status"], a["stream"])
-    for kw in (dict(dtype=2), dict(B=-1), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
+    for kw in (dict(dtype=2), dict(B=-1), dict(B=1 << 22), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
                dict(stride=63), dict(logits=ctypes.c_void_p(0x100001)),
                dict(dtype=0, logits=ctypes.c_void_p(0x100002)), dict(cap=0), dict(hist=None),
                dict(cnt=None), dict(rep=None), dict(pres=ctypes.c_void_p(0x100002)),
@@ -200,7 +200,7 @@ def test_apply_logit_bias_rejects_bad_arguments(lib):
         return lib.qs_apply_logit_bias(a["logits"], a["dtype"], a["B"], a["V"], a["stride"],
                                        a["ids"], a["vals"], a["cap"], a["cnt"], a["status"],
                                        a["stream"])
-    for kw in (dict(dtype=5), dict(B=-1), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
+    for kw in (dict(dtype=5), dict(B=-1), dict(B=1 << 22), dict(V=0), dict(V=(1 << 20) + 1, stride=(1 << 20) + 1),
                dict(stride=10), dict(logits=ctypes.c_void_p(0x100002)), dict(cap=0),
                dict(ids=None), dict(vals=ctypes.c_void_p(0x100001)), dict(cnt=None),
                dict(status=None)):
@@ -215,7 +215,7 @@ def test_top_logprobs_rejects_bad_arguments(lib):
         a.update(kw)
         return lib.qs_top_logprobs(a["B"], a["ids"], a["probs"], a["cnt"], a["cap"], a["n"],
                                    a["tid"], a["tlp"], a["status"], a["stream"])
-    for kw in (dict(B=-1), dict(cap=0), dict(n=0), dict(n=4097), dict(ids=None),
+    for kw in (dict(B=-1), dict(B=1 << 22), dict(cap=0), dict(n=0), dict(n=4097), dict(ids=None),
                dict(probs=ctypes.c_void_p(0x100002)), dict(cnt=None), dict(tid=None),
                dict(tlp=None), dict(status=None)):
         assert tp(**kw) == _lib.QS_ERR_INVALID_ARG, kw

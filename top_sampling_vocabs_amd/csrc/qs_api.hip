@@ -20,7 +20,9 @@
 namespace {
 
 constexpr int64_t kMaxV = (int64_t)1 << 30;
-constexpr int64_t kMaxB = ((int64_t)1 << 31) - 1;
+// one workgroup of up to 1024 threads per row: B * 1024 threads must fit one
+// launch grid (fewer than 2^32)
+constexpr int64_t kMaxB = ((int64_t)1 << 22) - 1;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
