@@ -429,6 +429,19 @@ def test_parity_rows_past_16bit_slices(qs, cfg):
     check_workload(qs, w, seed=11, cand_cap=w.V, dense=True)
 
 
+@pytest.mark.parametrize("cfg", [5, 2])
+def test_parity_many_rows(qs, cfg):
+    """A batch of 66,000 short rows: a launch grid past 65,535 workgroups (one
+    per row) and per-row offsets past 2^22 elements. Rows sampled across the
+    batch, the first and last among them, must match the oracle (bf16: the
+    mixed batch with error rows; fp32: top-k / top-p rows and greedy rows)."""
+    w = workloads.make(cfg, B=66000, V=72)
+    print(f"many rows cfg={cfg} B={w.B} V={w.V} {w.dtype}", flush=True)
+    rng = np.random.default_rng(cfg)
+    pick = sorted(set(rng.choice(w.B, size=240, replace=False).tolist()) | {0, 1, w.B - 2, w.B - 1})
+    check_workload(qs, w, rows=pick, seed=13, dense=True)
+
+
 def test_topp_background_extremes(qs):
     """Rows with top-k off whose background (legal tokens below the truncation
     threshold) lies outside the exact bf16 value bins: values of magnitude
